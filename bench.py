@@ -1,0 +1,168 @@
+"""Benchmark of the fused diagonal-GMM EM step on one MI355X.
+
+A step is one EM iteration (log-densities, log-sum-exp, responsibilities,
+sufficient statistics, deterministic reduction, M-step) over the whole data
+set, which is resident in HBM before timing starts.  The default workload is
+N=100M rows, D=128, K=1024 fp32 (51.2 GB of X), 30 iterations; data and the
+mixture law are seeded synthetic (see soft_clustering_amd/datagen.py).
+
+Prints one JSON line with the throughput (useful GFLOP/s: N*K*(8D+2) per
+iteration), ms per iteration, the roofline of the dominant kernel measured
+with HIP events around each of its launches, and the float64 oracle timed on
+a bounded row sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, AMD published figure
+HBM_PEAK_GBS = 8000.0
+
+WORKLOAD_TEXT = {
+    "large": "large EM: N=100,000,000, D=128, K=1024, fp32, diagonal covariance, 30 EM iterations",
+    "mid": "mid EM: N=1,000,000, D=128, K=1024, fp32, diagonal covariance, 30 EM iterations",
+    "tiny": "tiny EM: N=10,000, D=8, K=16, fp32, diagonal covariance, 10 EM iterations",
+    "embed": "embedding-like EM: N=10,000,000, D=768, K=4096, fp32, diagonal covariance, 20 EM iterations",
+}
+
+
+def useful_flops(N, K, D):
+    """[x^2, x] logit contraction (4D per pair) + r^T[1, x, x^2] statistics (2(2D+1))."""
+    return float(N) * K * (8 * D + 2)
+
+
+def cpu_baseline(workload, sample_rows, budget_s):
+    """Time the oracle as it stands on a prefix of the same data, scaled to
+    ms per EM iteration at the full N (EM cost is linear in N)."""
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import oracle.gmm_oracle as O
+    from soft_clustering_amd import datagen
+    wl = datagen.WORKLOADS[workload]
+    mix = datagen.mixture(wl.law, wl.D, wl.K, seed=wl.seed)
+    n = min(sample_rows, wl.N)
+    X = datagen.sample(mix, n, seed=wl.seed).numpy()
+    rows = datagen.init_rows(n, wl.K, seed=wl.init_seed)
+    w, mu, var = O.init(X, rows, wl.var_floor)
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    iters = 0
+    while True:
+        Nk, S1, S2, ll = O.estep_stats(X, w, mu, var, method="gemm")
+        w, mu, var = O.mstep(Nk, S1, S2, n, wl.var_floor, mu, var)
+        iters += 1
+        if time.perf_counter() - t0 > budget_s or iters >= 3:
+            break
+    dt = (time.perf_counter() - t0) / iters
+    ms_full = dt * 1e3 * (wl.N / n)
+    return {"value": ms_full, "unit": "ms per EM iteration (extrapolated linearly in N)", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{iters} EM iteration(s) of the float64 numpy oracle on the first {n} rows of the "
+                      f"{workload} workload ({dt:.2f} s each), scaled by N/{n}",
+            "gflops": useful_flops(n, wl.K, wl.D) / dt / 1e9,
+            "torch_threads": torch.get_num_threads()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="large", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--path", default="auto", choices=["auto", "fused", "two_sweep"])
+    ap.add_argument("--rows", type=int, default=0, help="override N (testing only)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=250_000)
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the EM step here is built and measured "
+              "on a single MI355X, with no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from soft_clustering_amd import GMM, PATH_AUTO, PATH_FUSED, PATH_TWO_SWEEP, datagen
+
+    wl = datagen.WORKLOADS[args.workload]
+    N = args.rows or wl.N
+    K, D = wl.K, wl.D
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    mix = datagen.mixture(wl.law, D, K, seed=wl.seed)
+    t0 = time.perf_counter()
+    X = torch.empty(N, D, dtype=torch.float32, device=dev)
+    datagen.sample_into(X, mix, 0, seed=wl.seed)
+    torch.cuda.synchronize()
+    print(f"# generated {N}x{D} in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    g = GMM(K, D, dev)
+    g.set_path({"auto": PATH_AUTO, "fused": PATH_FUSED, "two_sweep": PATH_TWO_SWEEP}[args.path])
+    w, mu, var = g.init(X, datagen.init_rows(N, K, seed=wl.init_seed), wl.var_floor)
+    hist_w = torch.zeros(max(args.warmup, 1), dtype=torch.float64, device=dev)
+    if args.warmup > 0:
+        g.fit(X, w, mu, var, args.warmup, wl.var_floor, hist_w)
+    g.check()
+    torch.cuda.synchronize()
+
+    hist = torch.zeros(args.steps, dtype=torch.float64, device=dev)
+    g.profile(True)
+    g.profile_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.fit(X, w, mu, var, args.steps, wl.var_floor, hist)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    stats_ms, stats_n, logz_ms, logz_n = g.profile_read()
+    g.profile(False)
+    g.check()
+
+    ms_step = dt * 1e3 / args.steps
+    F = useful_flops(N, K, D)
+    gflops = F / (dt / args.steps) / 1e9
+    fused = logz_n == 0
+    # dominant kernel: the statistics sweep (fused: the whole E-step in one
+    # launch).  Algorithmic flops per launch: fused N*K*(8D+2); two-sweep's
+    # statistics sweep does the r^T[1,x,x^2] contraction, 2N*K*(2D+1), plus
+    # a recomputation of the logits that is not counted.
+    per_launch_flops = F if fused else float(N) * K * 2 * (2 * D + 1)
+    avg_ms = stats_ms / max(stats_n, 1)
+    achieved = per_launch_flops / (avg_ms * 1e-3) / 1e12
+    hl = hist.cpu().numpy()
+    line = {
+        "metric": "ms per EM iteration and GFLOP/s at N=100M,K=1024,D=128 fp32; % MFMA peak",
+        "value": round(gflops, 1),
+        "unit": "GFLOP/s (useful: N*K*(8D+2) per EM iteration)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded mixture, generated on the GPU)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload] if not args.rows else
+                   f"{args.workload} law with N={N}", "N": N, "K": K, "D": D,
+                   "path": "fused" if fused else "two_sweep"},
+        "pct_mfma_peak": round(100 * gflops / (MFMA_FP32_PEAK_TFLOPS * 1e3), 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "k_stats (fused E-step)" if fused else "k_stats (two-sweep statistics sweep)",
+                     "avg_launch_ms": round(avg_ms, 3), "launches": stats_n},
+        "loglik_first_last": [float(hl[0]), float(hl[-1])],
+        "x_hbm_gbs_once": round(N * D * 4 / (avg_ms * 1e-3) / 1e9, 1),
+    }
+    if not fused:
+        line["logz_sweep_avg_ms"] = round(logz_ms / max(logz_n, 1), 3)
+    del X
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_rows, args.cpu_budget_s)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

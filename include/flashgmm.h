@@ -1,0 +1,162 @@
+/*
+ * flashgmm.h - C ABI of the fused diagonal-covariance Gaussian-mixture EM step
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of "Flash-GMM: A Memory-Efficient Kernel for Scalable
+ * Soft Clustering" (Bloch et al., arXiv 2606.10896): one pass over the data
+ * computes each point's K log-densities, normalises them with a per-point
+ * log-sum-exp into responsibilities, and folds those straight into the
+ * M-step sufficient statistics, so the N x K responsibility matrix is never
+ * stored (Section 3.1 and Algorithm 1 of that paper; Section 3.2 for the
+ * memory claim).  Here the covariance is diagonal (sigma^2_kd) rather than
+ * the paper's isotropic sigma^2_k I.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked [dev] are device pointers on the context's device; [host]
+ *     are host pointers.  All arrays are dense row-major.  The caller owns
+ *     every array it passes; the library never frees or keeps them.
+ *   - X has N rows of D float32 values with a row stride of ldx floats
+ *     (ldx >= D, ldx % 4 == 0) and a 16-byte aligned base.
+ *   - Parameters: weights float32[K], means float32[K*D], vars float32[K*D]
+ *     (variances, not standard deviations), 16-byte aligned.
+ *   - Work is enqueued on the context's HIP stream and is complete when that
+ *     stream is synchronised.  Entry points that return values to the host
+ *     (gmm_soft_assign, gmm_check) synchronise the stream themselves.
+ *   - No entry point aborts or throws.  Arguments are checked before anything
+ *     is launched; a failure returns a status and leaves a message for
+ *     gmm_last_error().  A failed call leaves caller arrays unspecified only
+ *     when the status is GMM_ERR_HIP or GMM_ERR_NUMERIC.
+ *   - The same inputs on the same device and build give bit-identical
+ *     outputs: no floating-point atomics, fixed reduction trees.
+ *   - A context is not thread-safe; distinct contexts are independent.
+ */
+#ifndef FLASHGMM_H
+#define FLASHGMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gmm_ctx gmm_ctx;
+
+typedef enum {
+    GMM_OK = 0,
+    GMM_ERR_INVALID_ARG = 1, /* a pointer, size or option is out of range */
+    GMM_ERR_UNSUPPORTED = 2, /* valid request this build/device cannot run */
+    GMM_ERR_OOM = 3,         /* workspace allocation failed */
+    GMM_ERR_HIP = 4,         /* a HIP runtime call or kernel failed */
+    GMM_ERR_NUMERIC = 5,     /* non-finite log-likelihood or statistics */
+    GMM_ERR_CAPACITY = 6     /* ids_capacity smaller than the lists need */
+} gmm_status;
+
+/* Execution path of the E-step (gmm_set_path).  AUTO picks FUSED when the
+ * component groups of one row tile fit the cooperative grid, else TWO_SWEEP. */
+typedef enum {
+    GMM_PATH_AUTO = 0,
+    GMM_PATH_TWO_SWEEP = 1, /* Algorithm 1's two sweeps: log Z first, then
+                               responsibilities and statistics with the
+                               logits recomputed (Section 3.1) */
+    GMM_PATH_FUSED = 2      /* one sweep: the workgroups that share a row tile
+                               exchange per-row log-sum-exp partials, so each
+                               logit is computed once */
+} gmm_path;
+
+/* Create a context for K components of dimension D on the current HIP device.
+ * hip_stream is a hipStream_t (NULL = the null stream).  Allocates the
+ * workspace, whose size depends on K, D and the device but not on N (see
+ * gmm_workspace_bytes); nothing else is allocated later.
+ * 1 <= K <= 65536, 1 <= D <= 1024. */
+gmm_status gmm_create(gmm_ctx **out /*[host]*/, int32_t K, int32_t D, void *hip_stream);
+
+/* Release the context and its workspace.  NULL-safe. */
+void gmm_destroy(gmm_ctx *ctx);
+
+/* Message of the last failed call on ctx (a context-owned string), or of the
+ * last failed gmm_create when ctx is NULL. */
+const char *gmm_last_error(const gmm_ctx *ctx);
+
+/* Workspace bytes a context for (K, D) allocates on the current device. */
+size_t gmm_workspace_bytes(int32_t K, int32_t D);
+
+/* Select the E-step path (gmm_path).  Both paths compute the same statistics
+ * up to float rounding order. */
+gmm_status gmm_set_path(gmm_ctx *ctx, int32_t path);
+
+/* Initialisation (not on the pages, which warm-start from k-means):
+ * means_k = X[init_rows[k]] for K distinct rows; every component gets the
+ * population (ddof 0) variance of each dimension over all N rows, floored at
+ * var_floor; weights 1/K.  init_rows [host] int64[K], each in [0, N). */
+gmm_status gmm_init(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_t ldx,
+                    const int64_t *init_rows /*[host]*/, float var_floor,
+                    float *weights /*[dev] K*/, float *means /*[dev] K*D*/,
+                    float *vars /*[dev] K*D*/);
+
+/* E-step sufficient statistics (Section 2; Algorithm 1 steps 4-17):
+ *   Nk[k]   = sum_n r_nk,
+ *   S1[k,d] = sum_n r_nk x_nd,   S2[k,d] = sum_n r_nk x_nd^2,
+ *   loglik  = sum_n log sum_k pi_k N(x_n | mu_k, diag vars_k),
+ * with r_nk the responsibilities of the given parameters.  Outputs are
+ * float64 device arrays; accumulate = 0 overwrites them, 1 adds into them
+ * (for row chunks of one data set). */
+gmm_status gmm_estep_stats(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_t ldx,
+                           const float *weights, const float *means, const float *vars /*[dev]*/,
+                           double *Nk /*[dev] K*/, double *S1 /*[dev] K*D*/,
+                           double *S2 /*[dev] K*D*/, double *loglik /*[dev] 1*/,
+                           int32_t accumulate);
+
+/* M-step, Eqs. (1)-(3) of Section 2 with a diagonal covariance, in place:
+ *   weights_k = Nk_k / n_total,  means_k = S1_k / Nk_k,
+ *   vars_kd   = max(S2_kd / Nk_k - means_kd^2, var_floor)   (Eq. (3), new mean).
+ * A component with Nk_k < 1e-6 keeps its mean and variances.  float64
+ * arithmetic, float32 results.  n_total > 0, var_floor > 0. */
+gmm_status gmm_mstep(gmm_ctx *ctx, const double *Nk, const double *S1, const double *S2 /*[dev]*/,
+                     double n_total, float var_floor,
+                     float *weights, float *means, float *vars /*[dev], in/out*/);
+
+/* T EM iterations from the parameters passed in (updated in place).
+ * loglik_hist [dev] float64[T]: entry t is the log-likelihood of the
+ * parameters entering iteration t.  No host synchronisation inside. */
+gmm_status gmm_fit(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_t ldx, int32_t T,
+                   float var_floor, float *weights, float *means, float *vars /*[dev] in/out*/,
+                   double *loglik_hist /*[dev] T*/);
+
+/* Inverted lists of a soft assignment (Section 4.2 argmax assignment and the
+ * Section 4.3 multi-assignment, with the threshold and count rule below):
+ * each row goes to its highest-responsibility component (lowest index on
+ * ties) and to up to max_extra further components whose responsibility is
+ * >= threshold, those ranked by responsibility descending, then index
+ * ascending.  Output is CSR: list_offsets [dev] int64[K+1], list_ids [dev]
+ * int32[nnz] with row ids ascending within each list.  *nnz [host] receives
+ * the total.  If ids_capacity < nnz the ids are not written, *nnz is set and
+ * GMM_ERR_CAPACITY is returned.  0 < threshold <= 1, 0 <= max_extra <= 8,
+ * N < 2^31.  Synchronises the stream. */
+gmm_status gmm_soft_assign(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_t ldx,
+                           const float *weights, const float *means, const float *vars /*[dev]*/,
+                           float threshold, int32_t max_extra,
+                           int64_t *list_offsets /*[dev] K+1*/, int32_t *list_ids /*[dev]*/,
+                           int64_t ids_capacity, int64_t *nnz /*[host]*/);
+
+/* Synchronise the stream and report device-side faults recorded since the
+ * last check: GMM_ERR_NUMERIC if a log-likelihood or statistic came out
+ * non-finite, GMM_ERR_HIP if a fused-path exchange timed out. */
+gmm_status gmm_check(gmm_ctx *ctx);
+
+/* Kernel timing for measurement tools.  While enabled (enable = 1), every
+ * launch of the E-step's dominant kernel (the statistics sweep; for the
+ * two-sweep path also the log Z sweep, counted separately) is bracketed by
+ * HIP events on the context's stream.  gmm_profile_read synchronises the
+ * stream, adds up the elapsed times since the last read (milliseconds) and
+ * returns the launch counts; any pointer may be NULL.  enable = 0 stops
+ * recording and drops pending events. */
+gmm_status gmm_profile(gmm_ctx *ctx, int32_t enable);
+gmm_status gmm_profile_read(gmm_ctx *ctx, double *stats_ms, int64_t *stats_launches,
+                            double *logz_ms, int64_t *logz_launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHGMM_H */

@@ -1,0 +1,232 @@
+"""ctypes binding of libflashgmm.so (C ABI in include/flashgmm.h).
+
+Argument marshalling only: tensors are checked for dtype, device, layout and
+alignment, then their device pointers and the current HIP stream are passed
+to the library.  Every computation runs in the library's HIP kernels; there
+is no fallback of any kind, and a missing library raises at import.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflashgmm.so")
+
+GMM_OK = 0
+_STATUS = {0: "GMM_OK", 1: "GMM_ERR_INVALID_ARG", 2: "GMM_ERR_UNSUPPORTED", 3: "GMM_ERR_OOM",
+           4: "GMM_ERR_HIP", 5: "GMM_ERR_NUMERIC", 6: "GMM_ERR_CAPACITY"}
+PATH_AUTO, PATH_TWO_SWEEP, PATH_FUSED = 0, 1, 2
+
+EXPORTS = ["gmm_create", "gmm_destroy", "gmm_last_error", "gmm_workspace_bytes", "gmm_set_path",
+           "gmm_init", "gmm_estep_stats", "gmm_mstep", "gmm_fit", "gmm_soft_assign", "gmm_check",
+           "gmm_profile", "gmm_profile_read"]
+
+
+class GMMError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python soft_clustering_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double
+    sig = {
+        "gmm_create": (i32, [ctypes.POINTER(vp), i32, i32, vp]),
+        "gmm_destroy": (None, [vp]),
+        "gmm_last_error": (ctypes.c_char_p, [vp]),
+        "gmm_workspace_bytes": (ctypes.c_size_t, [i32, i32]),
+        "gmm_set_path": (i32, [vp, i32]),
+        "gmm_init": (i32, [vp, vp, i64, i64, vp, f32, vp, vp, vp]),
+        "gmm_estep_stats": (i32, [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32]),
+        "gmm_mstep": (i32, [vp, vp, vp, vp, f64, f32, vp, vp, vp]),
+        "gmm_fit": (i32, [vp, vp, i64, i64, i32, f32, vp, vp, vp, vp]),
+        "gmm_soft_assign": (i32, [vp, vp, i64, i64, vp, vp, vp, f32, i32, vp, vp, i64, vp]),
+        "gmm_check": (i32, [vp]),
+        "gmm_profile": (i32, [vp, i32]),
+        "gmm_profile_read": (i32, [vp, ctypes.POINTER(f64), ctypes.POINTER(i64), ctypes.POINTER(f64),
+                                   ctypes.POINTER(i64)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, shape, name, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _rows(X, D, device):
+    """(N, ldx) of a row-major fp32 matrix that may have a row stride > D."""
+    if not isinstance(X, torch.Tensor) or X.dtype != torch.float32 or X.dim() != 2:
+        raise TypeError("X must be a 2-D float32 tensor")
+    if X.device != device:
+        raise ValueError(f"X must be on {device}")
+    if X.shape[1] != D:
+        raise ValueError(f"X has {X.shape[1]} columns, the model has D={D}")
+    if X.stride(1) != 1:
+        raise ValueError("X rows must be contiguous (stride(1) == 1)")
+    return X.shape[0], X.stride(0) if X.shape[0] > 1 else ((D + 3) // 4) * 4
+
+
+class GMM:
+    """A context for K components of dimension D on the current HIP device."""
+
+    def __init__(self, K: int, D: int, device=None):
+        if not torch.cuda.is_available():
+            raise RuntimeError("the HIP library needs a GPU")
+        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.K, self.D = int(K), int(D)
+        with torch.cuda.device(self.device):
+            h = ctypes.c_void_p()
+            st = _lib.gmm_create(ctypes.byref(h), self.K, self.D, _stream())
+            if st != GMM_OK:
+                raise GMMError(st, _lib.gmm_last_error(None).decode())
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.gmm_destroy(self._h)
+            self._h = None
+
+    __del__ = close
+
+    def _check(self, st):
+        if st != GMM_OK:
+            raise GMMError(st, _lib.gmm_last_error(self._h).decode())
+
+    @staticmethod
+    def workspace_bytes(K: int, D: int) -> int:
+        return int(_lib.gmm_workspace_bytes(int(K), int(D)))
+
+    def set_path(self, path: int):
+        self._check(_lib.gmm_set_path(self._h, int(path)))
+
+    def params(self):
+        """Fresh fp32 (weights, means, vars) buffers on the device."""
+        K, D = self.K, self.D
+        return (torch.empty(K, dtype=torch.float32, device=self.device),
+                torch.empty(K, D, dtype=torch.float32, device=self.device),
+                torch.empty(K, D, dtype=torch.float32, device=self.device))
+
+    def _params(self, w, mu, var):
+        _need(w, torch.float32, (self.K,), "weights", self.device)
+        _need(mu, torch.float32, (self.K, self.D), "means", self.device)
+        _need(var, torch.float32, (self.K, self.D), "vars", self.device)
+
+    def init(self, X, rows, var_floor, out=None):
+        N, ldx = _rows(X, self.D, self.device)
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        if rows.shape != (self.K,):
+            raise ValueError(f"rows must have shape ({self.K},)")
+        w, mu, var = out if out is not None else self.params()
+        self._params(w, mu, var)
+        with torch.cuda.device(self.device):
+            self._check(_lib.gmm_init(self._h, _ptr(X), N, ldx, rows.ctypes.data_as(ctypes.c_void_p),
+                                      float(var_floor), _ptr(w), _ptr(mu), _ptr(var)))
+        return w, mu, var
+
+    def estep_stats(self, X, w, mu, var, out=None, accumulate=False):
+        N, ldx = _rows(X, self.D, self.device)
+        self._params(w, mu, var)
+        K, D = self.K, self.D
+        if out is None:
+            out = (torch.zeros(K, dtype=torch.float64, device=self.device),
+                   torch.zeros(K, D, dtype=torch.float64, device=self.device),
+                   torch.zeros(K, D, dtype=torch.float64, device=self.device),
+                   torch.zeros(1, dtype=torch.float64, device=self.device))
+        Nk, S1, S2, ll = out
+        _need(Nk, torch.float64, (K,), "Nk", self.device)
+        _need(S1, torch.float64, (K, D), "S1", self.device)
+        _need(S2, torch.float64, (K, D), "S2", self.device)
+        _need(ll, torch.float64, (1,), "loglik", self.device)
+        with torch.cuda.device(self.device):
+            self._check(_lib.gmm_estep_stats(self._h, _ptr(X), N, ldx, _ptr(w), _ptr(mu), _ptr(var),
+                                             _ptr(Nk), _ptr(S1), _ptr(S2), _ptr(ll), int(bool(accumulate))))
+        return Nk, S1, S2, ll
+
+    def mstep(self, Nk, S1, S2, n_total, var_floor, w, mu, var):
+        K, D = self.K, self.D
+        _need(Nk, torch.float64, (K,), "Nk", self.device)
+        _need(S1, torch.float64, (K, D), "S1", self.device)
+        _need(S2, torch.float64, (K, D), "S2", self.device)
+        self._params(w, mu, var)
+        with torch.cuda.device(self.device):
+            self._check(_lib.gmm_mstep(self._h, _ptr(Nk), _ptr(S1), _ptr(S2), float(n_total), float(var_floor),
+                                       _ptr(w), _ptr(mu), _ptr(var)))
+        return w, mu, var
+
+    def fit(self, X, w, mu, var, T, var_floor, ll_hist=None):
+        N, ldx = _rows(X, self.D, self.device)
+        self._params(w, mu, var)
+        if ll_hist is None:
+            ll_hist = torch.zeros(int(T), dtype=torch.float64, device=self.device)
+        _need(ll_hist, torch.float64, (int(T),), "loglik_hist", self.device)
+        with torch.cuda.device(self.device):
+            self._check(_lib.gmm_fit(self._h, _ptr(X), N, ldx, int(T), float(var_floor), _ptr(w), _ptr(mu),
+                                     _ptr(var), _ptr(ll_hist)))
+        return w, mu, var, ll_hist
+
+    def soft_assign(self, X, w, mu, var, threshold=0.1, max_extra=3, ids_capacity=None):
+        """CSR inverted lists: (offsets int64[K+1], ids int32[nnz])."""
+        N, ldx = _rows(X, self.D, self.device)
+        self._params(w, mu, var)
+        offsets = torch.empty(self.K + 1, dtype=torch.int64, device=self.device)
+        cap = int(ids_capacity) if ids_capacity is not None else N * (1 + int(max_extra))
+        ids = torch.empty(max(cap, 1), dtype=torch.int32, device=self.device)
+        nnz = ctypes.c_int64(0)
+        with torch.cuda.device(self.device):
+            st = _lib.gmm_soft_assign(self._h, _ptr(X), N, ldx, _ptr(w), _ptr(mu), _ptr(var), float(threshold),
+                                      int(max_extra), _ptr(offsets), _ptr(ids), cap, ctypes.byref(nnz))
+        if st == 6:
+            raise GMMError(st, f"{_lib.gmm_last_error(self._h).decode()} (nnz={nnz.value})")
+        self._check(st)
+        return offsets, ids[: nnz.value]
+
+    def profile(self, enable: bool):
+        self._check(_lib.gmm_profile(self._h, int(bool(enable))))
+
+    def profile_read(self):
+        """(stats_ms, stats_launches, logz_ms, logz_launches) since the last read."""
+        a, b, c, d = ctypes.c_double(), ctypes.c_int64(), ctypes.c_double(), ctypes.c_int64()
+        with torch.cuda.device(self.device):
+            self._check(_lib.gmm_profile_read(self._h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
+                                              ctypes.byref(d)))
+        return a.value, b.value, c.value, d.value
+
+    def check(self):
+        with torch.cuda.device(self.device):
+            self._check(_lib.gmm_check(self._h))
+
+
+def raw_library():
+    """The ctypes handle (for ABI tests)."""
+    return _lib

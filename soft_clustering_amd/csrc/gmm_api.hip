@@ -1,0 +1,379 @@
+// C ABI of the fused diagonal-GMM EM library (declared in include/flashgmm.h):
+// argument validation, the context and its workspace, and the order of
+// kernel launches for each entry point.  All device work goes through the
+// launchers in gmm_kernels.hip; nothing here computes on the host.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/flashgmm.h"
+#include "gmm_internal.h"
+
+struct gmm_ctx {
+  int device = 0;
+  hipStream_t stream = nullptr;
+  gmm::Plan plan{};
+  gmm::Workspace ws{};
+  void* base = nullptr;
+  size_t bytes = 0;
+  int path = GMM_PATH_AUTO;
+  std::string err;
+  // kernel timing (gmm_profile)
+  bool prof = false;
+  std::vector<hipEvent_t> ev_free;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_pending[2];
+  hipEvent_t ev_open[2] = {nullptr, nullptr};
+};
+
+namespace {
+
+thread_local std::string g_create_err;
+
+gmm_status fail(gmm_ctx* c, gmm_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (c)
+    c->err = buf;
+  else
+    g_create_err = buf;
+  return st;
+}
+
+gmm_status hip_fail(gmm_ctx* c, hipError_t e, const char* what) {
+  return fail(c, GMM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+gmm_status check_x(gmm_ctx* c, const float* X, int64_t N, int64_t ldx) {
+  if (!X) return fail(c, GMM_ERR_INVALID_ARG, "X is NULL");
+  if (!aligned16(X)) return fail(c, GMM_ERR_INVALID_ARG, "X must be 16-byte aligned");
+  if (N < 1) return fail(c, GMM_ERR_INVALID_ARG, "N must be >= 1 (got %lld)", (long long)N);
+  if (ldx < c->plan.D || (ldx & 3))
+    return fail(c, GMM_ERR_INVALID_ARG, "ldx must be >= D and a multiple of 4 (got %lld, D=%d)",
+                (long long)ldx, c->plan.D);
+  if (N > ((int64_t)1 << 40)) return fail(c, GMM_ERR_INVALID_ARG, "N too large");
+  return GMM_OK;
+}
+
+gmm_status check_params(gmm_ctx* c, const void* w, const void* mu, const void* var) {
+  if (!w || !mu || !var) return fail(c, GMM_ERR_INVALID_ARG, "weights/means/vars must be non-NULL");
+  if (!aligned16(w) || !aligned16(mu) || !aligned16(var))
+    return fail(c, GMM_ERR_INVALID_ARG, "weights/means/vars must be 16-byte aligned");
+  return GMM_OK;
+}
+
+template <class T>
+T* carve(char*& p, size_t count) {
+  T* r = reinterpret_cast<T*>(p);
+  size_t b = (count * sizeof(T) + 255) / 256 * 256;
+  p += b;
+  return r;
+}
+
+hipEvent_t take_event(gmm_ctx* c) {
+  if (!c->ev_free.empty()) {
+    hipEvent_t e = c->ev_free.back();
+    c->ev_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void hook_before(void* user, int which, hipStream_t s) {
+  gmm_ctx* c = (gmm_ctx*)user;
+  hipEvent_t e = take_event(c);
+  if (e && hipEventRecord(e, s) == hipSuccess) c->ev_open[which] = e;
+}
+
+void hook_after(void* user, int which, hipStream_t s) {
+  gmm_ctx* c = (gmm_ctx*)user;
+  hipEvent_t b = c->ev_open[which];
+  c->ev_open[which] = nullptr;
+  if (!b) return;
+  hipEvent_t e = take_event(c);
+  if (e && hipEventRecord(e, s) == hipSuccess)
+    c->ev_pending[which].push_back({b, e});
+  else
+    c->ev_free.push_back(b);
+}
+
+bool want_fused(const gmm_ctx* c) {
+  if (c->path == GMM_PATH_TWO_SWEEP) return false;
+  if (c->path == GMM_PATH_FUSED) return c->plan.fusedOK != 0;
+  return c->plan.fusedOK != 0 && c->plan.P <= 64;
+}
+
+gmm_status estep_into(gmm_ctx* c, const float* X, int64_t N, int64_t ldx, const float* w, const float* mu,
+                      const float* var, double* Nk, double* S1, double* S2, double* ll, int accumulate) {
+  hipStream_t s = c->stream;
+  hipError_t e = gmm::launch_precompute(c->plan, c->ws, w, mu, var, s);
+  if (e != hipSuccess) return hip_fail(c, e, "precompute launch");
+  const bool fused = want_fused(c);
+  gmm::LaunchHooks hk;
+  hk.before = hook_before;
+  hk.after = hook_after;
+  hk.user = c;
+  e = gmm::launch_estep(c->plan, c->ws, X, N, ldx, fused, s, c->prof ? &hk : nullptr);
+  if (e != hipSuccess) return hip_fail(c, e, fused ? "fused E-step launch" : "two-sweep E-step launch");
+  e = gmm::launch_reduce(c->plan, c->ws, Nk, S1, S2, ll, accumulate, fused, c->plan.Glogz, s);
+  if (e != hipSuccess) return hip_fail(c, e, "reduce launch");
+  return GMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gmm_workspace_bytes(int32_t K, int32_t D) {
+  if (K < 1 || K > 65536 || D < 1 || D > 1024) return 0;
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+  gmm::Plan p0 = gmm::make_plan(K, D, prop.multiProcessorCount, 1, 1);
+  int o1 = 1, o2 = 1;
+  if (gmm::occupancy(p0, &o1, &o2) != hipSuccess) return 0;
+  gmm::Plan p = gmm::make_plan(K, D, prop.multiProcessorCount, o1, o2);
+  return gmm::workspace_bytes(p);
+}
+
+gmm_status gmm_create(gmm_ctx** out, int32_t K, int32_t D, void* hip_stream) {
+  g_create_err.clear();
+  if (!out) return fail(nullptr, GMM_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (K < 1 || K > 65536) return fail(nullptr, GMM_ERR_INVALID_ARG, "K must be in [1, 65536] (got %d)", K);
+  if (D < 1 || D > 1024) return fail(nullptr, GMM_ERR_INVALID_ARG, "D must be in [1, 1024] (got %d)", D);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(nullptr, GMM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(nullptr, GMM_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(nullptr, GMM_ERR_UNSUPPORTED, "built for gfx950, device is %s", prop.gcnArchName);
+  gmm::Plan p0 = gmm::make_plan(K, D, prop.multiProcessorCount, 1, 1);
+  if (!gmm::plan_shape_ok(p0)) return fail(nullptr, GMM_ERR_UNSUPPORTED, "no kernel for K=%d D=%d", K, D);
+  int o1 = 1, o2 = 1;
+  e = gmm::occupancy(p0, &o1, &o2);
+  if (e != hipSuccess) return fail(nullptr, GMM_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
+  if (o1 < 1 || o2 < 1) return fail(nullptr, GMM_ERR_UNSUPPORTED, "E-step kernel does not fit a CU");
+
+  gmm_ctx* c = new (std::nothrow) gmm_ctx();
+  if (!c) return fail(nullptr, GMM_ERR_OOM, "host allocation failed");
+  c->device = dev;
+  c->stream = (hipStream_t)hip_stream;
+  c->plan = gmm::make_plan(K, D, prop.multiProcessorCount, o1, o2);
+  c->bytes = gmm::workspace_bytes(c->plan);
+  e = hipMalloc(&c->base, c->bytes);
+  if (e != hipSuccess) {
+    delete c;
+    return fail(nullptr, GMM_ERR_OOM, "workspace hipMalloc(%zu): %s", (size_t)0, hipGetErrorString(e));
+  }
+  const gmm::Plan& p = c->plan;
+  char* q = (char*)c->base;
+  c->ws.wop = carve<float>(q, (size_t)p.Kpad * 2 * p.Dp);
+  c->ws.cvec = carve<float>(q, p.Kpad);
+  c->ws.slots = carve<double>(q, (size_t)p.R * p.Kpad * p.SR);
+  c->ws.llslots = carve<double>(q, p.R > p.Glogz ? p.R : p.Glogz);
+  c->ws.logz = carve<float>(q, (size_t)p.chunk);
+  c->ws.xbuf = carve<unsigned long long>(q, (size_t)p.R * 2 * p.P * p.BN);
+  c->ws.stats = carve<double>(q, (size_t)p.K + 2 * (size_t)p.K * p.D + 1);
+  c->ws.colpart = carve<double>(q, (size_t)1024 * p.D);
+  c->ws.colmean = carve<double>(q, p.D);
+  c->ws.rows = carve<int64_t>(q, p.K);
+  c->ws.flags = carve<int>(q, 4);
+  c->ws.colG = 1024;
+  e = hipMemsetAsync(c->ws.flags, 0, 16, c->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) {
+    hipFree(c->base);
+    delete c;
+    return fail(nullptr, GMM_ERR_HIP, "workspace clear: %s", hipGetErrorString(e));
+  }
+  *out = c;
+  return GMM_OK;
+}
+
+static void drop_events(gmm_ctx* ctx) {
+  for (int w = 0; w < 2; ++w) {
+    for (auto& pr : ctx->ev_pending[w]) {
+      ctx->ev_free.push_back(pr.first);
+      ctx->ev_free.push_back(pr.second);
+    }
+    ctx->ev_pending[w].clear();
+  }
+}
+
+void gmm_destroy(gmm_ctx* ctx) {
+  if (!ctx) return;
+  hipStreamSynchronize(ctx->stream);
+  drop_events(ctx);
+  for (hipEvent_t e : ctx->ev_free) hipEventDestroy(e);
+  if (ctx->base) hipFree(ctx->base);
+  delete ctx;
+}
+
+gmm_status gmm_profile(gmm_ctx* ctx, int32_t enable) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  if (enable != 0 && enable != 1) return fail(ctx, GMM_ERR_INVALID_ARG, "enable must be 0 or 1");
+  if (!enable) {
+    hipError_t e = hipStreamSynchronize(ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "stream synchronize");
+    drop_events(ctx);
+  }
+  ctx->prof = enable != 0;
+  return GMM_OK;
+}
+
+gmm_status gmm_profile_read(gmm_ctx* ctx, double* stats_ms, int64_t* stats_launches, double* logz_ms,
+                            int64_t* logz_launches) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  hipError_t e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "stream synchronize");
+  double ms[2] = {0.0, 0.0};
+  int64_t n[2] = {0, 0};
+  for (int w = 0; w < 2; ++w) {
+    for (auto& pr : ctx->ev_pending[w]) {
+      float t = 0.f;
+      e = hipEventElapsedTime(&t, pr.first, pr.second);
+      if (e != hipSuccess) return hip_fail(ctx, e, "hipEventElapsedTime");
+      ms[w] += t;
+      n[w] += 1;
+    }
+  }
+  drop_events(ctx);
+  if (stats_ms) *stats_ms = ms[0];
+  if (stats_launches) *stats_launches = n[0];
+  if (logz_ms) *logz_ms = ms[1];
+  if (logz_launches) *logz_launches = n[1];
+  return GMM_OK;
+}
+
+const char* gmm_last_error(const gmm_ctx* ctx) { return ctx ? ctx->err.c_str() : g_create_err.c_str(); }
+
+gmm_status gmm_set_path(gmm_ctx* ctx, int32_t path) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  if (path < GMM_PATH_AUTO || path > GMM_PATH_FUSED) return fail(ctx, GMM_ERR_INVALID_ARG, "unknown path %d", path);
+  if (path == GMM_PATH_FUSED && !ctx->plan.fusedOK)
+    return fail(ctx, GMM_ERR_UNSUPPORTED, "fused path needs %d co-resident workgroups per row tile", ctx->plan.P);
+  ctx->path = path;
+  return GMM_OK;
+}
+
+gmm_status gmm_init(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, const int64_t* init_rows,
+                    float var_floor, float* weights, float* means, float* vars) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  gmm_status st = check_x(ctx, X, N, ldx);
+  if (st) return st;
+  st = check_params(ctx, weights, means, vars);
+  if (st) return st;
+  if (!init_rows) return fail(ctx, GMM_ERR_INVALID_ARG, "init_rows is NULL");
+  if (!(var_floor > 0.f) || !isfinite(var_floor)) return fail(ctx, GMM_ERR_INVALID_ARG, "var_floor must be > 0");
+  const int K = ctx->plan.K;
+  for (int k = 0; k < K; ++k)
+    if (init_rows[k] < 0 || init_rows[k] >= N)
+      return fail(ctx, GMM_ERR_INVALID_ARG, "init_rows[%d]=%lld out of [0, N)", k, (long long)init_rows[k]);
+  hipError_t e = hipMemcpyAsync(ctx->ws.rows, init_rows, (size_t)K * 8, hipMemcpyHostToDevice, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "init rows copy");
+  e = gmm::launch_init(ctx->plan, ctx->ws, X, N, ldx, var_floor, weights, means, vars, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "init launch");
+  // init_rows is a host array the caller may reuse as soon as we return
+  e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "init");
+  return GMM_OK;
+}
+
+gmm_status gmm_estep_stats(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, const float* weights,
+                           const float* means, const float* vars, double* Nk, double* S1, double* S2,
+                           double* loglik, int32_t accumulate) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  gmm_status st = check_x(ctx, X, N, ldx);
+  if (st) return st;
+  st = check_params(ctx, weights, means, vars);
+  if (st) return st;
+  if (!Nk || !S1 || !S2 || !loglik) return fail(ctx, GMM_ERR_INVALID_ARG, "statistics outputs must be non-NULL");
+  if (accumulate != 0 && accumulate != 1) return fail(ctx, GMM_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  return estep_into(ctx, X, N, ldx, weights, means, vars, Nk, S1, S2, loglik, accumulate);
+}
+
+gmm_status gmm_mstep(gmm_ctx* ctx, const double* Nk, const double* S1, const double* S2, double n_total,
+                     float var_floor, float* weights, float* means, float* vars) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  if (!Nk || !S1 || !S2) return fail(ctx, GMM_ERR_INVALID_ARG, "statistics inputs must be non-NULL");
+  gmm_status st = check_params(ctx, weights, means, vars);
+  if (st) return st;
+  if (!(n_total > 0.0) || !isfinite(n_total)) return fail(ctx, GMM_ERR_INVALID_ARG, "n_total must be > 0");
+  if (!(var_floor > 0.f) || !isfinite(var_floor)) return fail(ctx, GMM_ERR_INVALID_ARG, "var_floor must be > 0");
+  hipError_t e = gmm::launch_mstep(ctx->plan, ctx->ws, Nk, S1, S2, n_total, var_floor, weights, means, vars,
+                                   ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "mstep launch");
+  return GMM_OK;
+}
+
+gmm_status gmm_fit(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, int32_t T, float var_floor,
+                   float* weights, float* means, float* vars, double* loglik_hist) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  gmm_status st = check_x(ctx, X, N, ldx);
+  if (st) return st;
+  st = check_params(ctx, weights, means, vars);
+  if (st) return st;
+  if (T < 1) return fail(ctx, GMM_ERR_INVALID_ARG, "T must be >= 1");
+  if (!loglik_hist) return fail(ctx, GMM_ERR_INVALID_ARG, "loglik_hist is NULL");
+  if (!(var_floor > 0.f) || !isfinite(var_floor)) return fail(ctx, GMM_ERR_INVALID_ARG, "var_floor must be > 0");
+  const int K = ctx->plan.K, D = ctx->plan.D;
+  double* Nk = ctx->ws.stats;
+  double* S1 = Nk + K;
+  double* S2 = S1 + (size_t)K * D;
+  for (int t = 0; t < T; ++t) {
+    st = estep_into(ctx, X, N, ldx, weights, means, vars, Nk, S1, S2, loglik_hist + t, 0);
+    if (st) return st;
+    hipError_t e = gmm::launch_mstep(ctx->plan, ctx->ws, Nk, S1, S2, (double)N, var_floor, weights, means, vars,
+                                     ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "mstep launch");
+  }
+  return GMM_OK;
+}
+
+gmm_status gmm_soft_assign(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, const float* weights,
+                           const float* means, const float* vars, float threshold, int32_t max_extra,
+                           int64_t* list_offsets, int32_t* list_ids, int64_t ids_capacity, int64_t* nnz) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  gmm_status st = check_x(ctx, X, N, ldx);
+  if (st) return st;
+  st = check_params(ctx, weights, means, vars);
+  if (st) return st;
+  if (!(threshold > 0.f && threshold <= 1.f)) return fail(ctx, GMM_ERR_INVALID_ARG, "threshold must be in (0, 1]");
+  if (max_extra < 0 || max_extra > 8) return fail(ctx, GMM_ERR_INVALID_ARG, "max_extra must be in [0, 8]");
+  if (!list_offsets || !nnz) return fail(ctx, GMM_ERR_INVALID_ARG, "list_offsets and nnz must be non-NULL");
+  if (ids_capacity < 0) return fail(ctx, GMM_ERR_INVALID_ARG, "ids_capacity must be >= 0");
+  if (ids_capacity > 0 && !list_ids) return fail(ctx, GMM_ERR_INVALID_ARG, "list_ids is NULL");
+  if (N >= ((int64_t)1 << 31)) return fail(ctx, GMM_ERR_INVALID_ARG, "N must be < 2^31 for int32 ids");
+  return fail(ctx, GMM_ERR_UNSUPPORTED, "soft assignment not built yet");
+}
+
+gmm_status gmm_check(gmm_ctx* ctx) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  hipError_t e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "stream synchronize");
+  int flags[4] = {0, 0, 0, 0};
+  e = hipMemcpy(flags, ctx->ws.flags, sizeof flags, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(ctx, e, "flag read");
+  if (flags[0] || flags[1]) {
+    hipMemset(ctx->ws.flags, 0, sizeof flags);
+    if (flags[1]) return fail(ctx, GMM_ERR_HIP, "fused E-step exchange timed out");
+    return fail(ctx, GMM_ERR_NUMERIC, "non-finite log-likelihood or statistics");
+  }
+  return GMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Internal interface between the C ABI (gmm_api.hip) and the kernels
+// (gmm_kernels.hip).  Not installed; no torch types anywhere.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gmm {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerWG = 8;     // waves of the E-step workgroups
+constexpr int kCompsPerWave = 32;  // two 16-wide MFMA component blocks
+constexpr int kNumXCD = 8;         // MI355X: 8 accelerator complex dies
+
+// Shape of the E-step kernels, chosen once per context from (K, D).
+//   WC comp groups x WD dim segments = waves per workgroup.
+//   DPW dims per wave segment (multiple of 16); Dp = DPW * WD >= D.
+//   BN rows per tile.
+struct Plan {
+  int K, D;
+  int WC, WD, DPW, Dp, BN;
+  int Kpad;          // multiple of 32 * WC
+  int P;             // workgroups sharing one row tile (component groups)
+  int R;             // row groups (stats partial slots)
+  int G;             // stats grid = R * P
+  int Glogz;         // persistent grid of the log Z sweep
+  int SR;            // doubles per (slot, component): 2*Dp features + N_k
+  int RS;            // LDS floats per tile row
+  int fusedOK;       // cooperative grid can hold R*P workgroups
+  int64_t chunk;     // rows per two-sweep chunk (log Z buffer length)
+  size_t ldsStats, ldsLogz;
+};
+
+struct Workspace {
+  float* wop;        // Kpad * 2*Dp  MFMA-operand-ordered [a | b] per dim
+  float* cvec;       // Kpad         per-component constant (-inf for padding)
+  double* slots;     // R * Kpad * SR
+  double* llslots;   // max(R, Glogz)
+  float* logz;       // chunk
+  unsigned long long* xbuf;  // R * 2 * P * BN  tagged log-sum-exp exchange
+  double* stats;     // K + 2*K*D + 1  (fit's own statistics: Nk, S1, S2, LL)
+  double* colpart;   // colG * D  column partial sums (init)
+  double* colmean;   // D
+  int64_t* rows;     // K  init rows
+  int* flags;        // [0] numeric fault, [1] exchange timeout
+  int colG;
+};
+
+Plan make_plan(int K, int D, int numCU, int occStats, int occLogz);
+bool plan_shape_ok(const Plan& p);
+size_t workspace_bytes(const Plan& p);
+
+hipError_t occupancy(const Plan& p, int* occStats, int* occLogz);
+
+// Launchers (enqueue on stream; return the first launch error).
+hipError_t launch_precompute(const Plan& p, const Workspace& w, const float* weights,
+                             const float* means, const float* vars, hipStream_t s);
+// Optional per-launch timing hooks: called around the two E-step sweeps.
+struct LaunchHooks {
+  void (*before)(void* user, int which, hipStream_t s) = nullptr;  // which: 0 stats, 1 log Z
+  void (*after)(void* user, int which, hipStream_t s) = nullptr;
+  void* user = nullptr;
+};
+hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx,
+                        bool fused, hipStream_t s, const LaunchHooks* hooks = nullptr);
+hipError_t launch_reduce(const Plan& p, const Workspace& w, double* Nk, double* S1, double* S2,
+                         double* ll, int accumulate, bool fused, int64_t nllslots, hipStream_t s);
+hipError_t launch_mstep(const Plan& p, const Workspace& w, const double* Nk, const double* S1,
+                        const double* S2, double n_total, float var_floor, float* weights,
+                        float* means, float* vars, hipStream_t s);
+hipError_t launch_init(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx,
+                       float var_floor, float* weights, float* means, float* vars, hipStream_t s);
+// Soft assignment: lists into caller CSR arrays. sel is a device scratch of
+// N*(1+max_extra) int32 supplied by the caller of this function.
+hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* X, int64_t N,
+                                int64_t ldx, const float* weights, const float* means,
+                                const float* vars, float threshold, int max_extra, int32_t* sel,
+                                unsigned long long* counts, hipStream_t s);
+hipError_t launch_assign_csr(const Plan& p, int64_t N, int max_extra, const int32_t* sel,
+                             unsigned long long* counts, int64_t* offsets, int32_t* ids,
+                             int64_t capacity, int64_t* d_nnz, int phase, hipStream_t s);
+
+}  // namespace gmm

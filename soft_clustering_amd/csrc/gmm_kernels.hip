@@ -1,0 +1,973 @@
+// HIP kernels for gfx950 (MI355X) of the fused diagonal-covariance GMM EM step.
+//
+// Method: "Flash-GMM: A Memory-Efficient Kernel for Scalable Soft Clustering",
+// Section 3.1 and Algorithm 1 (tile the rows, per-row online log-sum-exp over
+// component blocks, responsibilities folded into sufficient statistics without
+// storing the N x K responsibility matrix), Section 2 for the model and the
+// M-step Eqs. (1)-(3).  The covariance here is diagonal.
+//
+// Design for CDNA4, not a port of the paper's Triton kernel:
+//  * Both contractions run on v_mfma_f32_16x16x4_f32.  The logit contraction
+//    L[pt][comp] = sum_f A[pt][f] W[f][comp] + c[comp] uses features
+//    A = [x^2 | x] and weights W = [-1/(2 s^2) | mu/s^2] (the expanded
+//    quadratic); its accumulator layout (lane = component, register = point)
+//    is exactly the A-operand layout of the statistics contraction
+//    S[comp][phi] += sum_pt r[comp][pt] F[pt][phi], F = [x^2 | x], so
+//    responsibilities go from registers straight into the second MFMA.
+//  * A workgroup owns 32*WC components and a strided set of row tiles; its
+//    statistics stay in registers (fp32) and are flushed into a private
+//    float64 slot every few tiles; a fixed-order pairwise tree over the slots
+//    replaces the paper's atomic adds (Algorithm 1 step 17), so results are
+//    bit-reproducible.
+//  * The per-row normaliser log Z comes either from a first sweep over all
+//    components (two-sweep, as Algorithm 1) or, in the fused path, from the P
+//    workgroups that share a row tile exchanging their per-row partial
+//    log-sum-exp through tagged 64-bit words in device memory (cooperative
+//    launch guarantees they are co-resident), so each logit is computed once.
+//  * X tiles are staged in LDS as [x^2_lo | x_lo | x^2_hi | x_hi] per row so
+//    one ds_read_b128 gives a lane four consecutive MFMA k-steps.
+#include "gmm_internal.h"
+
+#include <math.h>
+
+namespace gmm {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+static constexpr float kNegInf = -__builtin_huge_valf();
+static constexpr float kPosInf = __builtin_huge_valf();
+static constexpr double kLog2Pi = 1.8378770664093454835606594728112;
+
+__device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Butterfly over the 16 lanes of a DPP row: mirror, half-mirror, xor 2, xor 1.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<0x140>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0xB1>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0x140>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0xB1>(v);
+  return v;
+}
+
+// log(exp(a) + exp(b)) merge of two (max, sum) pairs; -inf safe.
+__device__ __forceinline__ void lse_merge(float& M, float& S, float m2, float s2) {
+  float mn = fmaxf(M, m2);
+  float ms = (mn == kNegInf) ? 0.f : mn;
+  S = S * __expf(M - ms) + s2 * __expf(m2 - ms);
+  M = mn;
+}
+__device__ __forceinline__ float lse_of(float M, float S) {
+  return (S > 0.f) ? ((M == kNegInf ? 0.f : M) + __logf(S)) : kNegInf;
+}
+
+struct EArgs {
+  const float* X;
+  int64_t ldx;
+  int64_t row0;   // first row of this launch (two-sweep chunk)
+  int64_t nrows;  // rows of this launch
+  const float* wop;
+  const float* cvec;
+  float* logz;    // two-sweep: log Z per row of the chunk
+  double* slots;
+  double* llslots;
+  unsigned long long* xbuf;
+  int* flags;
+  int K, D, Kpad, P, R, Dp;
+  int slot_acc;   // 1: add into slots / llslots
+};
+
+// ---------------------------------------------------------------------------
+// Shared device pieces, parameterised by the workgroup shape.
+template <int WC, int WD, int DPW, int BN>
+struct Shape {
+  static constexpr int NT = kWave * WC * WD;
+  static constexpr int NPB = BN / 16;         // 16-row MFMA blocks per tile
+  static constexpr int NFB = DPW / 8;         // 16-wide feature blocks per wave (2*DPW/16)
+  static constexpr int SS = 2 * DPW + 4;      // LDS floats per wave segment of a row
+  static constexpr int RS = WD * SS;          // LDS floats per row
+  static constexpr int TILE = BN * RS;        // LDS floats per tile buffer
+  // double-buffer the X tile only when each thread stages few float4s
+  static constexpr int PER_STAGE = (BN * WD * DPW / 4 + NT - 1) / NT;
+  static constexpr int NBUF = (PER_STAGE <= 8 && TILE * 8 <= 140 * 1024) ? 2 : 1;
+  static constexpr int HALF = DPW / 2;
+  static constexpr int RED = (WD > 1) ? WD * WC * NPB * 8 * kWave : 1;  // partial-logit exchange
+};
+
+// Stage rows [r0, r0+rows) of X into an LDS tile buffer in segment layout:
+// per row and wave segment [x^2 (first half dims) | x | x^2 (second half) | x].
+// Rows past `rows` and dims past D are zeros.  Split into a global-load half
+// and an LDS-store half so the loads of the next tile can be in flight while
+// the current tile's statistics contraction runs.
+template <class SH, int DPW>
+struct Stage {
+  static constexpr int Dp = DPW * (SH::RS / SH::SS);
+  static constexpr int Q4 = Dp / 4;
+  static constexpr int ITEMS = (SH::TILE / SH::RS) * Q4;  // BN * Dp/4 float4s
+  static constexpr int PER = (ITEMS + SH::NT - 1) / SH::NT;
+  f4 v[PER];
+
+  __device__ __forceinline__ void load(const float* __restrict__ X, int64_t ldx, int64_t r0, int rows, int D) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int it = threadIdx.x + k * SH::NT;
+      const int pt = it / Q4;
+      const int d = (it - pt * Q4) << 2;
+      f4 x = {0.f, 0.f, 0.f, 0.f};
+      if (it < ITEMS && pt < rows && d < D) {
+        x = *reinterpret_cast<const f4*>(X + (r0 + pt) * ldx + d);
+        if (d + 3 >= D) {
+          if (d + 1 >= D) x[1] = 0.f;
+          if (d + 2 >= D) x[2] = 0.f;
+          x[3] = 0.f;
+        }
+      }
+      v[k] = x;
+    }
+  }
+  __device__ __forceinline__ void store(float* __restrict__ xt) const {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int it = threadIdx.x + k * SH::NT;
+      if (it < ITEMS) {
+        const int pt = it / Q4;
+        const int d = (it - pt * Q4) << 2;
+        const int seg = d / DPW;
+        const int e = d - seg * DPW;
+        const int h = e / SH::HALF;
+        const int o = e - h * SH::HALF;
+        float* dst = xt + pt * SH::RS + seg * SH::SS + (2 * h) * SH::HALF + o;
+        *reinterpret_cast<f4*>(dst) = v[k] * v[k];
+        *reinterpret_cast<f4*>(dst + SH::HALF) = v[k];
+      }
+    }
+  }
+};
+
+// Partial logits of one wave: its 2 component blocks x NPB point blocks over
+// its dim segment.  acc must hold the starting value (c or 0).
+template <class SH, int DPW>
+__device__ __forceinline__ void logit_tile(const float* __restrict__ xt, const float* __restrict__ w0,
+                                           const float* __restrict__ w1, f4 (&acc)[SH::NPB][2],
+                                           int lane, int wd) {
+  const int g = lane >> 4, r16 = lane & 15;
+  const float* arow = xt + r16 * SH::RS + wd * SH::SS + g * SH::HALF;
+  constexpr int S4 = DPW / 8;
+  // W operands (from L2) are fetched one k-step group ahead of their use.
+  f4 b0 = *reinterpret_cast<const f4*>(w0 + lane * 4);
+  f4 b1 = *reinterpret_cast<const f4*>(w1 + lane * 4);
+#pragma unroll 2
+  for (int s4 = 0; s4 < S4; ++s4) {
+    const int nx = (s4 + 1 < S4) ? s4 + 1 : s4;
+    const f4 b0n = *reinterpret_cast<const f4*>(w0 + (nx * kWave + lane) * 4);
+    const f4 b1n = *reinterpret_cast<const f4*>(w1 + (nx * kWave + lane) * 4);
+    f4 a[SH::NPB];
+#pragma unroll
+    for (int pb = 0; pb < SH::NPB; ++pb)
+      a[pb] = *reinterpret_cast<const f4*>(arow + pb * 16 * SH::RS + s4 * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int pb = 0; pb < SH::NPB; ++pb) {
+        acc[pb][0] = mfma(a[pb][i], b0[i], acc[pb][0]);
+        acc[pb][1] = mfma(a[pb][i], b1[i], acc[pb][1]);
+      }
+    }
+    b0 = b0n;
+    b1 = b1n;
+  }
+}
+
+// With WD > 1 the WD waves of a component group hold partial logits over
+// their dim segments; sum them in a fixed order through LDS so every wave of
+// the group ends with bit-identical full logits.
+template <class SH, int WC, int WD>
+__device__ __forceinline__ void reduce_partial_logits(float* __restrict__ red, f4 (&acc)[SH::NPB][2],
+                                                      int lane, int wc, int wd) {
+  if constexpr (WD > 1) {
+    constexpr int PER = SH::NPB * 8;  // floats per lane
+    float* mine = red + ((wd * WC + wc) * PER) * kWave + lane;
+#pragma unroll
+    for (int pb = 0; pb < SH::NPB; ++pb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) mine[((pb * 2 + cb) * 4 + v) * kWave] = acc[pb][cb][v];
+    __syncthreads();
+#pragma unroll
+    for (int pb = 0; pb < SH::NPB; ++pb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float s = 0.f;
+#pragma unroll
+          for (int k = 0; k < WD; ++k) s += red[((k * WC + wc) * PER + (pb * 2 + cb) * 4 + v) * kWave + lane];
+          acc[pb][cb][v] = s;
+        }
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ const float* wop_block(const float* wop, int cb16, int WD, int wd, int DPW) {
+  return wop + (size_t)(cb16 * WD + wd) * (DPW / 8) * 256;
+}
+
+// Row group / member of a workgroup.  Members of one row group sit on one XCD
+// when the grid allows (consecutive workgroup ids go round-robin over the 8
+// XCDs), so the P re-reads of an X tile and the exchange stay in one L2.
+__device__ __forceinline__ void rg_member(int G, int P, int& rg, int& p) {
+  const int b = blockIdx.x;
+  const int per = G / kNumXCD;
+  if (G % kNumXCD == 0 && per % P == 0) {
+    const int xcd = b % kNumXCD, s = b / kNumXCD;
+    rg = xcd * (per / P) + s / P;
+    p = s % P;
+  } else {
+    rg = b / P;
+    p = b % P;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// E-step statistics sweep.  FUSED: per-row log Z by exchange; else from a.logz.
+template <int WC, int WD, int DPW, int BN, bool FUSED>
+__global__ void __launch_bounds__(kWave* WC* WD) k_stats(EArgs a) {
+  using SH = Shape<WC, WD, DPW, BN>;
+  constexpr int NPB = SH::NPB, NFB = SH::NFB;
+  constexpr int FLUSH = (BN >= 64) ? 16 : 64;  // tiles between fp64 flushes (~1024 rows)
+  constexpr int QP = (SH::NT / BN) > 0 ? (SH::NT / BN) : 1;
+
+  __shared__ __attribute__((aligned(16))) float xt[SH::NBUF][SH::TILE];
+  __shared__ __attribute__((aligned(16))) float red[SH::RED];
+  __shared__ __attribute__((aligned(16))) float lzt[BN];
+  __shared__ float lpart[WC][BN];
+  __shared__ float exm[QP][BN], exs[QP][BN];
+  __shared__ double llred[BN];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wc = w % WC, wd = w / WC;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int G = a.R * a.P;
+  int rg, p;
+  rg_member(G, a.P, rg, p);
+  const int compbase = p * 32 * WC + wc * 32;  // first component of this wave
+  const int cb16 = compbase >> 4;
+  const float* w0 = wop_block(a.wop, cb16, WD, wd, DPW);
+  const float* w1 = wop_block(a.wop, cb16 + 1, WD, wd, DPW);
+  const float c0 = (wd == 0) ? a.cvec[compbase + r16] : 0.f;
+  const float c1 = (wd == 0) ? a.cvec[compbase + 16 + r16] : 0.f;
+
+  const int nt = (int)((a.nrows + BN - 1) / BN);
+  f4 sacc[2][NFB];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int fb = 0; fb < NFB; ++fb) sacc[cb][fb] = f4{0.f, 0.f, 0.f, 0.f};
+  float nk0 = 0.f, nk1 = 0.f;
+  double ll = 0.0;
+  bool fresh = (a.slot_acc == 0);
+  double* sbase = a.slots + ((size_t)rg * a.Kpad + compbase) * (2 * a.Dp + 1);
+  const int SR = 2 * a.Dp + 1;
+
+  // fp32 tile partials -> this workgroup's float64 slot.  Every slot word is
+  // written by exactly one lane of one workgroup, so fire-and-forget float64
+  // atomic adds (performed in program order per address) stay deterministic.
+  auto put = [&](double* ptr, double val) {
+    if (fresh)
+      __hip_atomic_store(ptr, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      __hip_atomic_fetch_add(ptr, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto flush = [&]() {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+      for (int fb = 0; fb < NFB; ++fb) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          put(sbase + (size_t)(cb * 16 + 4 * g + v) * SR + wd * 2 * DPW + fb * 16 + r16, (double)sacc[cb][fb][v]);
+        sacc[cb][fb] = f4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    float t0 = nk0 + __shfl_xor(nk0, 16);
+    t0 += __shfl_xor(t0, 32);
+    float t1 = nk1 + __shfl_xor(nk1, 16);
+    t1 += __shfl_xor(t1, 32);
+    if (wd == 0 && g == 0) {
+      put(sbase + (size_t)r16 * SR + 2 * a.Dp, (double)t0);
+      put(sbase + (size_t)(16 + r16) * SR + 2 * a.Dp, (double)t1);
+    }
+    nk0 = nk1 = 0.f;
+    fresh = false;
+  };
+
+  Stage<SH, DPW> stg;
+  int j = 0;
+  int t = rg;
+  if (t < nt) {
+    const int rows0 = (int)min((int64_t)BN, a.nrows - (int64_t)t * BN);
+    stg.load(a.X, a.ldx, a.row0 + (int64_t)t * BN, rows0, a.D);
+    stg.store(xt[0]);
+  }
+  __syncthreads();
+  for (; t < nt; t += a.R, ++j) {
+    const int cur = (SH::NBUF == 2) ? (j & 1) : 0;
+    const int64_t trow = (int64_t)t * BN;
+    const int rows = (int)min((int64_t)BN, a.nrows - trow);
+    if constexpr (SH::NBUF == 1) {
+      if (j > 0) {
+        stg.load(a.X, a.ldx, a.row0 + trow, rows, a.D);
+        stg.store(xt[0]);
+        __syncthreads();
+      }
+    }
+    // ---- logits
+    f4 acc[NPB][2];
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb) {
+      acc[pb][0] = f4{c0, c0, c0, c0};
+      acc[pb][1] = f4{c1, c1, c1, c1};
+    }
+    logit_tile<SH, DPW>(xt[cur], w0, w1, acc, lane, wd);
+    reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
+
+    // ---- per-row log Z
+    if constexpr (FUSED) {
+      if (wd == 0) {
+#pragma unroll
+        for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float m = row16_max(fmaxf(acc[pb][0][v], acc[pb][1][v]));
+            const float ms = (m == kNegInf) ? 0.f : m;
+            float e = __expf(acc[pb][0][v] - ms) + __expf(acc[pb][1][v] - ms);
+            e = row16_sum(e);
+            if (r16 == 0) lpart[wc][pb * 16 + 4 * g + v] = (e > 0.f) ? ms + __logf(e) : kNegInf;
+          }
+      }
+      __syncthreads();
+      const unsigned tag = (unsigned)(j + 1);
+      unsigned long long* xb = a.xbuf + ((size_t)(rg * 2 + (j & 1)) * a.P) * BN;
+      if (tid < BN) {
+        float M = kNegInf, S = 0.f;
+#pragma unroll
+        for (int k = 0; k < WC; ++k) lse_merge(M, S, lpart[k][tid], 1.f);
+        const float mine = lse_of(M, S);
+        const unsigned long long word =
+            ((unsigned long long)tag << 32) | (unsigned long long)__float_as_uint(mine);
+        __hip_atomic_store(xb + (size_t)p * BN + tid, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (tid < QP * BN) {
+        const int pt = tid % BN, qp = tid / BN;
+        float M = kNegInf, S = 0.f;
+        for (int q = qp; q < a.P; q += QP) {
+          const unsigned long long* src = xb + (size_t)q * BN + pt;
+          unsigned long long word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          // Bounded wait: a peer that never publishes (impossible while all
+          // workgroups are co-resident) ends in flags[1] and a drained grid.
+          for (int spins = 0; (unsigned)(word >> 32) != tag; ++spins) {
+            if ((spins & 255) == 0 &&
+                __hip_atomic_load(&a.flags[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+              break;
+            if (spins > (1 << 20)) {
+              __hip_atomic_store(&a.flags[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+            word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          lse_merge(M, S, __uint_as_float((unsigned)(word & 0xffffffffu)), 1.f);
+        }
+        exm[qp][pt] = M;
+        exs[qp][pt] = S;
+      }
+      __syncthreads();
+      if (tid < BN) {
+        float M = kNegInf, S = 0.f;
+#pragma unroll
+        for (int k = 0; k < QP; ++k) lse_merge(M, S, exm[k][tid], exs[k][tid]);
+        const float lz = lse_of(M, S);
+        lzt[tid] = (tid < rows) ? lz : kPosInf;
+        if (p == 0 && tid < rows) ll += (double)lz;
+      }
+    } else {
+      if (tid < BN) lzt[tid] = (tid < rows) ? a.logz[trow + tid] : kPosInf;
+    }
+    __syncthreads();
+
+    // ---- prefetch the next tile while the statistics contraction runs
+    const int tn = t + a.R;
+    const bool has_next = (SH::NBUF == 2) && (tn < nt);
+    if (has_next) stg.load(a.X, a.ldx, a.row0 + (int64_t)tn * BN, (int)min((int64_t)BN, a.nrows - (int64_t)tn * BN), a.D);
+    // ---- responsibilities and statistics: r goes from the logit
+    // accumulators straight into the A operand; B operands (x^2 | x from LDS)
+    // are loaded one (block, k-step) ahead so at most 2*NFB are live.
+    const float* xs = xt[cur] + wd * SH::SS + r16 + 4 * g * SH::RS;
+    float bx[2][NFB];
+#pragma unroll
+    for (int fb = 0; fb < NFB; ++fb) bx[0][fb] = xs[fb * 16];
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb) {
+      const f4 lz = *reinterpret_cast<const f4*>(lzt + pb * 16 + 4 * g);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int step = pb * 4 + v;
+        const int cb_ = step & 1;
+        if (step + 1 < NPB * 4) {
+          const int np = (step + 1) >> 2, nv = (step + 1) & 3;
+          const float* brow = xs + (np * 16 + nv) * SH::RS;
+#pragma unroll
+          for (int fb = 0; fb < NFB; ++fb) bx[cb_ ^ 1][fb] = brow[fb * 16];
+        }
+        const float r0 = __expf(acc[pb][0][v] - lz[v]);
+        const float r1 = __expf(acc[pb][1][v] - lz[v]);
+        nk0 += r0;
+        nk1 += r1;
+#pragma unroll
+        for (int fb = 0; fb < NFB; ++fb) {
+          sacc[0][fb] = mfma(r0, bx[cb_][fb], sacc[0][fb]);
+          sacc[1][fb] = mfma(r1, bx[cb_][fb], sacc[1][fb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (has_next) stg.store(xt[cur ^ 1]);
+    if ((j + 1) % FLUSH == 0) flush();
+    __syncthreads();
+  }
+  if (j == 0 || (j % FLUSH) != 0) flush();
+
+  if constexpr (FUSED) {
+    if (p == 0) {
+      if (tid < BN) llred[tid] = ll;
+      __syncthreads();
+      for (int s = BN / 2; s > 0; s >>= 1) {
+        if (tid < s) llred[tid] += llred[tid + s];
+        __syncthreads();
+      }
+      if (tid == 0) a.llslots[rg] = a.slot_acc ? a.llslots[rg] + llred[0] : llred[0];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// First sweep of the two-sweep path: log Z of every row of the chunk, over all
+// components (Algorithm 1 steps 6-10), plus a float64 log-likelihood partial
+// per workgroup.
+template <int WC, int WD, int DPW, int BN>
+__global__ void __launch_bounds__(kWave* WC* WD) k_logz(EArgs a) {
+  using SH = Shape<WC, WD, DPW, BN>;
+  constexpr int NPB = SH::NPB;
+  __shared__ __attribute__((aligned(16))) float xt[SH::TILE];
+  __shared__ __attribute__((aligned(16))) float red[SH::RED];
+  __shared__ float lpart[WC][BN];
+  __shared__ double llred[BN];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wc = w % WC, wd = w / WC;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int ncg = a.Kpad / 32;
+  const int nt = (int)((a.nrows + BN - 1) / BN);
+  double ll = 0.0;
+
+  for (int t = blockIdx.x; t < nt; t += gridDim.x) {
+    const int64_t trow = (int64_t)t * BN;
+    const int rows = (int)min((int64_t)BN, a.nrows - trow);
+    {
+      Stage<SH, DPW> stg;
+      stg.load(a.X, a.ldx, a.row0 + trow, rows, a.D);
+      stg.store(xt);
+    }
+    __syncthreads();
+    float M[NPB][4], S[NPB][4];
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        M[pb][v] = kNegInf;
+        S[pb][v] = 0.f;
+      }
+    for (int cg = wc; cg < ncg; cg += WC) {
+      const int compbase = cg * 32;
+      const float c0 = (wd == 0) ? a.cvec[compbase + r16] : 0.f;
+      const float c1 = (wd == 0) ? a.cvec[compbase + 16 + r16] : 0.f;
+      f4 acc[NPB][2];
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) {
+        acc[pb][0] = f4{c0, c0, c0, c0};
+        acc[pb][1] = f4{c1, c1, c1, c1};
+      }
+      logit_tile<SH, DPW>(xt, wop_block(a.wop, compbase >> 4, WD, wd, DPW),
+                          wop_block(a.wop, (compbase >> 4) + 1, WD, wd, DPW), acc, lane, wd);
+      reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float mn = fmaxf(M[pb][v], fmaxf(acc[pb][0][v], acc[pb][1][v]));
+          const float ms = (mn == kNegInf) ? 0.f : mn;
+          S[pb][v] = S[pb][v] * __expf(M[pb][v] - ms) + __expf(acc[pb][0][v] - ms) +
+                     __expf(acc[pb][1][v] - ms);
+          M[pb][v] = mn;
+        }
+    }
+    if (wd == 0) {
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float mr = row16_max(M[pb][v]);
+          const float ms = (mr == kNegInf) ? 0.f : mr;
+          const float s = row16_sum(S[pb][v] * __expf(M[pb][v] - ms));
+          if (r16 == 0) lpart[wc][pb * 16 + 4 * g + v] = (s > 0.f) ? ms + __logf(s) : kNegInf;
+        }
+    }
+    __syncthreads();
+    if (tid < rows) {
+      float Mx = kNegInf, Sx = 0.f;
+#pragma unroll
+      for (int k = 0; k < WC; ++k) lse_merge(Mx, Sx, lpart[k][tid], 1.f);
+      const float lz = lse_of(Mx, Sx);
+      a.logz[trow + tid] = lz;
+      ll += (double)lz;
+    }
+    __syncthreads();
+  }
+  if (tid < BN) llred[tid] = ll;
+  __syncthreads();
+  for (int s = BN / 2; s > 0; s >>= 1) {
+    if (tid < s) llred[tid] += llred[tid + s];
+    __syncthreads();
+  }
+  if (tid == 0) a.llslots[blockIdx.x] = a.slot_acc ? a.llslots[blockIdx.x] + llred[0] : llred[0];
+}
+
+// ---------------------------------------------------------------------------
+// Parameters -> MFMA operands (Algorithm 1 step 8's log z, expanded).
+//   a_kd = -1/(2 s^2_kd), b_kd = mu_kd / s^2_kd,
+//   c_k  = log pi_k - 1/2 sum_d mu^2/s^2 - 1/2 sum_d log s^2 - D/2 log 2pi,
+// computed in float64, stored float32; padding components get c = -inf.
+__global__ void k_precompute_w(const float* __restrict__ mu, const float* __restrict__ var, float* wop,
+                               int K, int D, int Kpad, int WD, int DPW) {
+  const size_t total = (size_t)Kpad * 2 * WD * DPW;
+  const int per_cb = WD * (DPW / 8) * 256;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int cb = (int)(idx / per_cb);
+    int rem = (int)(idx - (size_t)cb * per_cb);
+    const int wd = rem / ((DPW / 8) * 256);
+    rem -= wd * (DPW / 8) * 256;
+    const int s4 = rem / 256;
+    rem -= s4 * 256;
+    const int lane = rem >> 2, i = rem & 3;
+    const int gg = lane >> 4;
+    const int comp = cb * 16 + (lane & 15);
+    const int dim = wd * DPW + (gg >> 1) * (DPW / 2) + s4 * 4 + i;
+    float val = 0.f;
+    if (comp < K && dim < D) {
+      const double s2 = (double)var[(size_t)comp * D + dim];
+      val = (gg & 1) ? (float)((double)mu[(size_t)comp * D + dim] / s2) : (float)(-0.5 / s2);
+    }
+    wop[idx] = val;
+  }
+}
+
+__global__ void k_precompute_c(const float* __restrict__ w, const float* __restrict__ mu,
+                               const float* __restrict__ var, float* cvec, int K, int D, int Kpad) {
+  const int comp = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x & 63;
+  if (comp >= Kpad) return;
+  if (comp >= K) {
+    if (lane == 0) cvec[comp] = kNegInf;
+    return;
+  }
+  double q = 0.0, ld = 0.0;
+  for (int d = lane; d < D; d += kWave) {
+    const double s2 = (double)var[(size_t)comp * D + d];
+    const double m = (double)mu[(size_t)comp * D + d];
+    q += m * m / s2;
+    ld += log(s2);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    q += __shfl_xor(q, o);
+    ld += __shfl_xor(ld, o);
+  }
+  if (lane == 0) {
+    const double wk = (double)w[comp];
+    cvec[comp] = (wk > 0.0) ? (float)(log(wk) - 0.5 * q - 0.5 * ld - 0.5 * D * kLog2Pi)
+                            : ((wk == 0.0) ? kNegInf : __builtin_nanf(""));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Deterministic pairwise sum of n values at a stride (blocks of 4, then a
+// binary-counter merge: a fixed tree that depends only on n).
+__device__ __forceinline__ double pairwise_sum(const double* p, size_t stride, int n) {
+  double st[24];
+  int sz[24];
+  int top = 0;
+  for (int i = 0; i < n; i += 4) {
+    double s = 0.0;
+    const int e = min(i + 4, n);
+    for (int k = i; k < e; ++k) s += p[(size_t)k * stride];
+    int c = 1;
+    while (top > 0 && sz[top - 1] == c) {
+      s = st[top - 1] + s;
+      c <<= 1;
+      --top;
+    }
+    st[top] = s;
+    sz[top] = c;
+    ++top;
+  }
+  double r = 0.0;
+  while (top > 0) r = st[--top] + r;
+  return r;
+}
+
+// Slots -> caller statistics (the tree that replaces Algorithm 1 step 17).
+__global__ void k_reduce(const double* __restrict__ slots, int R, int Kpad, int K, int D, int Dp, int DPW,
+                         double* Nk, double* S1, double* S2, int accumulate) {
+  const int SR = 2 * Dp + 1;
+  const size_t total = (size_t)K * SR;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int k = (int)(idx / SR);
+    const int phi = (int)(idx - (size_t)k * SR);
+    double* out;
+    if (phi == 2 * Dp) {
+      out = Nk + k;
+    } else {
+      const int seg = phi / (2 * DPW);
+      const int e = phi - seg * 2 * DPW;
+      const int sg = e / (DPW / 2);
+      const int dim = seg * DPW + (sg >> 1) * (DPW / 2) + (e - sg * (DPW / 2));
+      if (dim >= D) continue;
+      out = ((sg & 1) ? S1 : S2) + (size_t)k * D + dim;
+    }
+    const double v = pairwise_sum(slots + (size_t)k * SR + phi, (size_t)Kpad * SR, R);
+    *out = accumulate ? *out + v : v;
+  }
+}
+
+__global__ void k_reduce_ll(const double* __restrict__ llslots, int n, double* ll, int accumulate,
+                            int* flags) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    const double v = pairwise_sum(llslots, 1, n);
+    const double out = accumulate ? *ll + v : v;
+    *ll = out;
+    if (!isfinite(out)) flags[0] = 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// M-step, Eqs. (1)-(3) with a diagonal covariance and a floor; float64.
+__global__ void k_mstep(const double* __restrict__ Nk, const double* __restrict__ S1,
+                        const double* __restrict__ S2, double n_total, float floor_, float* w,
+                        float* mu, float* var, int K, int D, int* flags) {
+  const size_t total = (size_t)K * D;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int k = (int)(idx / D);
+    const int d = (int)(idx - (size_t)k * D);
+    const double nk = Nk[k];
+    if (d == 0) w[k] = (float)(nk / n_total);
+    if (!isfinite(nk)) flags[0] = 1;
+    if (nk >= 1e-6) {
+      const double m = S1[idx] / nk;
+      double v = S2[idx] / nk - m * m;
+      v = fmax(v, (double)floor_);
+      mu[idx] = (float)m;
+      var[idx] = (float)v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Initialisation: column sums (pass 0) or squared deviations (pass 1) of row
+// blocks in float64, then a pairwise tree over blocks.
+__global__ void k_colpart(const float* __restrict__ X, int64_t N, int64_t ldx, int D,
+                          const double* __restrict__ mean, double* part, int pass) {
+  const int64_t per = (N + gridDim.x - 1) / gridDim.x;
+  const int64_t r0 = (int64_t)blockIdx.x * per;
+  const int64_t r1 = min(N, r0 + per);
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    double s = 0.0;
+    const double m = pass ? mean[d] : 0.0;
+    for (int64_t r = r0; r < r1; ++r) {
+      const double x = (double)X[r * ldx + d];
+      s += pass ? (x - m) * (x - m) : x;
+    }
+    part[(size_t)blockIdx.x * D + d] = s;
+  }
+}
+
+__global__ void k_colfinal(const double* __restrict__ part, int nb, int D, double N, double* out) {
+  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  if (d < D) out[d] = pairwise_sum(part + d, (size_t)D, nb) / N;
+}
+
+__global__ void k_init_params(const float* __restrict__ X, int64_t ldx, const int64_t* __restrict__ rows,
+                              const double* __restrict__ colvar, float floor_, float* w, float* mu,
+                              float* var, int K, int D) {
+  const size_t total = (size_t)K * D;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int k = (int)(idx / D);
+    const int d = (int)(idx - (size_t)k * D);
+    mu[idx] = X[rows[k] * ldx + d];
+    var[idx] = (float)fmax(colvar[d], (double)floor_);
+    if (d == 0) w[k] = (float)(1.0 / (double)K);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side plan, instantiation table and launchers.
+template <int WC, int WD, int DPW>
+struct Kern {
+  static constexpr int BN = (WD == 1) ? 64 : 16;
+  static void* stats_fused() { return (void*)&k_stats<WC, WD, DPW, BN, true>; }
+  static void* stats_two() { return (void*)&k_stats<WC, WD, DPW, BN, false>; }
+  static void* logz() { return (void*)&k_logz<WC, WD, DPW, BN>; }
+};
+
+struct KTab {
+  void* fused;
+  void* two;
+  void* logz;
+};
+
+static bool lookup(int WC, int WD, int DPW, KTab& t) {
+#define GMM_K(wc, wd, dpw)                                                     \
+  if (WC == wc && WD == wd && DPW == dpw) {                                    \
+    t = KTab{Kern<wc, wd, dpw>::stats_fused(), Kern<wc, wd, dpw>::stats_two(), \
+             Kern<wc, wd, dpw>::logz()};                                       \
+    return true;                                                               \
+  }
+  GMM_K(1, 1, 16) GMM_K(1, 1, 32) GMM_K(1, 1, 64) GMM_K(1, 1, 128)
+  GMM_K(2, 1, 16) GMM_K(2, 1, 32) GMM_K(2, 1, 64) GMM_K(2, 1, 128)
+  GMM_K(4, 1, 16) GMM_K(4, 1, 32) GMM_K(4, 1, 64) GMM_K(4, 1, 128)
+  GMM_K(8, 1, 16) GMM_K(8, 1, 32) GMM_K(8, 1, 64) GMM_K(8, 1, 128)
+  GMM_K(1, 8, 32) GMM_K(1, 8, 64) GMM_K(1, 8, 96) GMM_K(1, 8, 128)
+#undef GMM_K
+  return false;
+}
+
+static size_t lds_stats_bytes(int WC, int WD, int DPW) {
+  const int BN = (WD == 1) ? 64 : 16;
+  const int RS = WD * (2 * DPW + 4);
+  const int NTh = 64 * WC * WD;
+  const int NBUF = ((BN * WD * DPW / 4 + NTh - 1) / NTh <= 8 && (size_t)BN * RS * 8 <= 140 * 1024) ? 2 : 1;
+  const int QP = (64 * WC * WD) / BN;
+  size_t b = (size_t)NBUF * BN * RS * 4 + (WD > 1 ? (size_t)WD * WC * (BN / 16) * 8 * 64 * 4 : 4);
+  b += BN * 4 + (size_t)WC * BN * 4 + 2 * (size_t)QP * BN * 4 + BN * 8 + 4;
+  return b;
+}
+
+Plan make_plan(int K, int D, int numCU, int occStats, int occLogz) {
+  Plan p{};
+  p.K = K;
+  p.D = D;
+  if (D <= 128) {
+    p.WD = 1;
+    p.DPW = D <= 16 ? 16 : D <= 32 ? 32 : D <= 64 ? 64 : 128;
+    const int groups = (K + 31) / 32;
+    p.WC = groups >= 8 ? 8 : groups >= 4 ? 4 : groups >= 2 ? 2 : 1;
+  } else {
+    p.WD = 8;
+    const int per = (D + 7) / 8;
+    p.DPW = per <= 32 ? 32 : per <= 64 ? 64 : per <= 96 ? 96 : 128;
+    p.WC = 1;
+  }
+  p.Dp = p.DPW * p.WD;
+  p.BN = (p.WD == 1) ? 64 : 16;
+  const int cw = 32 * p.WC;
+  p.Kpad = (K + cw - 1) / cw * cw;
+  p.P = p.Kpad / cw;
+  p.SR = 2 * p.Dp + 1;
+  p.RS = p.WD * (2 * p.DPW + 4);
+  p.ldsStats = lds_stats_bytes(p.WC, p.WD, p.DPW);
+  const int capS = numCU * (occStats > 0 ? occStats : 1);
+  p.fusedOK = (p.P <= capS) ? 1 : 0;
+  p.R = capS / p.P;
+  if (p.R < 1) p.R = 1;
+  p.G = p.R * p.P;
+  p.Glogz = numCU * (occLogz > 0 ? occLogz : 1);
+  p.chunk = (int64_t)1 << 21;
+  return p;
+}
+
+bool plan_shape_ok(const Plan& p) {
+  KTab t;
+  return lookup(p.WC, p.WD, p.DPW, t);
+}
+
+size_t workspace_bytes(const Plan& p) {
+  const size_t a = 256;
+  auto up = [&](size_t b) { return (b + a - 1) / a * a; };
+  size_t b = 0;
+  b += up((size_t)p.Kpad * 2 * p.Dp * 4);
+  b += up((size_t)p.Kpad * 4);
+  b += up((size_t)p.R * p.Kpad * p.SR * 8);
+  b += up((size_t)(p.R > p.Glogz ? p.R : p.Glogz) * 8);
+  b += up((size_t)p.chunk * 4);
+  b += up((size_t)p.R * 2 * p.P * p.BN * 8);
+  b += up(((size_t)p.K + 2 * (size_t)p.K * p.D + 1) * 8);
+  b += up((size_t)1024 * p.D * 8);
+  b += up((size_t)p.D * 8);
+  b += up((size_t)p.K * 8);
+  b += up(16);
+  return b;
+}
+
+hipError_t occupancy(const Plan& p, int* occStats, int* occLogz) {
+  KTab t;
+  if (!lookup(p.WC, p.WD, p.DPW, t)) return hipErrorInvalidValue;
+  const int nt = 64 * p.WC * p.WD;
+  int o1 = 0, o2 = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1, (const void*)t.fused, nt, 0);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o2, (const void*)t.logz, nt, 0);
+  if (e != hipSuccess) return e;
+  *occStats = o1;
+  *occLogz = o2;
+  return hipSuccess;
+}
+
+static int grid_for(size_t total, int block) {
+  size_t g = (total + block - 1) / block;
+  if (g > 65535 * 4) g = 65535 * 4;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+hipError_t launch_precompute(const Plan& p, const Workspace& w, const float* weights, const float* means,
+                             const float* vars, hipStream_t s) {
+  const size_t total = (size_t)p.Kpad * 2 * p.Dp;
+  hipLaunchKernelGGL(k_precompute_w, dim3(grid_for(total, 256)), dim3(256), 0, s, means, vars, w.wop, p.K,
+                     p.D, p.Kpad, p.WD, p.DPW);
+  hipLaunchKernelGGL(k_precompute_c, dim3((p.Kpad + 3) / 4), dim3(256), 0, s, weights, means, vars, w.cvec,
+                     p.K, p.D, p.Kpad);
+  return hipGetLastError();
+}
+
+static EArgs make_args(const Plan& p, const Workspace& w, const float* X, int64_t ldx) {
+  EArgs a{};
+  a.X = X;
+  a.ldx = ldx;
+  a.wop = w.wop;
+  a.cvec = w.cvec;
+  a.logz = w.logz;
+  a.slots = w.slots;
+  a.llslots = w.llslots;
+  a.xbuf = w.xbuf;
+  a.flags = w.flags;
+  a.K = p.K;
+  a.D = p.D;
+  a.Kpad = p.Kpad;
+  a.P = p.P;
+  a.R = p.R;
+  a.Dp = p.Dp;
+  return a;
+}
+
+__global__ void k_fill_u64(unsigned long long* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0ull;
+}
+
+hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx, bool fused,
+                        hipStream_t s, const LaunchHooks* hk) {
+  auto pre = [&](int which) {
+    if (hk && hk->before) hk->before(hk->user, which, s);
+  };
+  auto post = [&](int which) {
+    if (hk && hk->after) hk->after(hk->user, which, s);
+  };
+  KTab t;
+  if (!lookup(p.WC, p.WD, p.DPW, t)) return hipErrorInvalidValue;
+  const int nt = 64 * p.WC * p.WD;
+  EArgs a = make_args(p, w, X, ldx);
+  if (fused) {
+    const size_t nx = (size_t)p.R * 2 * p.P * p.BN;
+    hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(nx, 256)), dim3(256), 0, s, w.xbuf, nx);
+    a.row0 = 0;
+    a.nrows = N;
+    a.slot_acc = 0;
+    void* args[] = {&a};
+    pre(0);
+    hipError_t e = hipLaunchCooperativeKernel(t.fused, dim3(p.G), dim3(nt), args, 0, s);
+    if (e != hipSuccess) return e;
+    post(0);
+    return hipGetLastError();
+  }
+  for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
+    a.row0 = r0;
+    a.nrows = (N - r0 < p.chunk) ? (N - r0) : p.chunk;
+    a.slot_acc = (r0 > 0) ? 1 : 0;
+    void* args[] = {&a};
+    pre(1);
+    hipError_t e = hipLaunchKernel(t.logz, dim3(p.Glogz), dim3(nt), args, 0, s);
+    if (e != hipSuccess) return e;
+    post(1);
+    pre(0);
+    e = hipLaunchKernel(t.two, dim3(p.G), dim3(nt), args, 0, s);
+    if (e != hipSuccess) return e;
+    post(0);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const Plan& p, const Workspace& w, double* Nk, double* S1, double* S2, double* ll,
+                         int accumulate, bool fused, int64_t nllslots, hipStream_t s) {
+  const size_t total = (size_t)p.K * p.SR;
+  hipLaunchKernelGGL(k_reduce, dim3(grid_for(total, 256)), dim3(256), 0, s, w.slots, p.R, p.Kpad, p.K, p.D,
+                     p.Dp, p.DPW, Nk, S1, S2, accumulate);
+  const int n = fused ? p.R : (int)nllslots;
+  hipLaunchKernelGGL(k_reduce_ll, dim3(1), dim3(64), 0, s, w.llslots, n, ll, accumulate, w.flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_mstep(const Plan& p, const Workspace& w, const double* Nk, const double* S1,
+                        const double* S2, double n_total, float var_floor, float* weights, float* means,
+                        float* vars, hipStream_t s) {
+  const size_t total = (size_t)p.K * p.D;
+  hipLaunchKernelGGL(k_mstep, dim3(grid_for(total, 256)), dim3(256), 0, s, Nk, S1, S2, n_total, var_floor,
+                     weights, means, vars, p.K, p.D, w.flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_init(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx,
+                       float var_floor, float* weights, float* means, float* vars, hipStream_t s) {
+  const int nb = (int)((N < (int64_t)w.colG) ? N : (int64_t)w.colG);
+  const int bt = p.D >= 1024 ? 1024 : ((p.D + 63) / 64) * 64;
+  hipLaunchKernelGGL(k_colpart, dim3(nb), dim3(bt), 0, s, X, N, ldx, p.D, (const double*)nullptr, w.colpart,
+                     0);
+  hipLaunchKernelGGL(k_colfinal, dim3((p.D + 255) / 256), dim3(256), 0, s, w.colpart, nb, p.D, (double)N,
+                     w.colmean);
+  // pass 1 writes variances into colpart's partials, final into stats scratch
+  hipLaunchKernelGGL(k_colpart, dim3(nb), dim3(bt), 0, s, X, N, ldx, p.D, (const double*)w.colmean,
+                     w.colpart, 1);
+  double* colvar = w.stats;  // K + 2KD + 1 >= D doubles
+  hipLaunchKernelGGL(k_colfinal, dim3((p.D + 255) / 256), dim3(256), 0, s, w.colpart, nb, p.D, (double)N,
+                     colvar);
+  const size_t total = (size_t)p.K * p.D;
+  hipLaunchKernelGGL(k_init_params, dim3(grid_for(total, 256)), dim3(256), 0, s, X, ldx, w.rows, colvar,
+                     var_floor, weights, means, vars, p.K, p.D);
+  return hipGetLastError();
+}
+
+}  // namespace gmm

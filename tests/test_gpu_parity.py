@@ -1,0 +1,272 @@
+"""HIP path against the float64 oracle, element by element, on seeded inputs
+small enough for the oracle (several tiles and a ragged tail), through the
+C ABI.  Tolerances: tests/tolerance.py (1e-4 per iteration, 1e-3 after T)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.gmm_oracle as O
+from soft_clustering_amd import datagen
+from tests.tolerance import check_params, check_stats, data_scales
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+# name: (law, N, D, K, ldx)  -- N values leave a ragged last tile
+CASES = {
+    "tiny": ("tiny", 10_000, 8, 16, None),
+    "odd_d5_k7": ("tiny", 1_003, 5, 7, 8),
+    "mid_prefix": ("mid", 20_037, 128, 1024, None),
+    "d100_k300": ("mid", 5_001, 100, 300, None),
+    "d40_k64": ("tiny", 3_333, 40, 64, None),
+    "k16384": ("ivf", 4_101, 128, 16_384, None),
+    "d200_k100": ("mid", 2_005, 200, 100, None),
+    "embed_d768": ("embed", 2_003, 768, 512, None),
+}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+_cache = {}
+
+
+def case_data(name):
+    if name in _cache:
+        return _cache[name]
+    law, N, D, K, ldx = CASES[name]
+    mix = datagen.mixture(law, D, K, seed=0)
+    Xc = datagen.sample(mix, N, seed=0, ldx=ldx)          # CPU, possibly strided
+    rows = datagen.init_rows(N, K, seed=1)
+    Xn = Xc.contiguous().numpy()
+    floor = 1.0 / 12.0 if law == "ivf" else 1e-6
+    w, mu, var = O.init(Xn, rows, floor)
+    params = tuple(a.astype(np.float32) for a in (w, mu, var))
+    if ldx is not None:
+        buf = torch.full((N, ldx), float("nan"), dtype=torch.float32)
+        buf[:, :D] = Xc
+        Xg = buf.to(DEV)[:, :D]
+    else:
+        Xg = Xc.to(DEV)
+    out = (Xn, Xg, params, rows, floor)
+    _cache[name] = out
+    return out
+
+
+def method_for(N, D, K):
+    return "direct" if N * D * K <= 3e7 else "gemm"
+
+
+def gpu_params(params):
+    return tuple(torch.as_tensor(a).to(DEV) for a in params)
+
+
+@pytest.mark.parametrize("path", ["fused", "two_sweep"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_estep_parity(name, path):
+    from soft_clustering_amd import GMM, PATH_FUSED, PATH_TWO_SWEEP
+    Xn, Xg, params, _, _ = case_data(name)
+    N, D = Xn.shape
+    K = params[1].shape[0]
+    log(f"[estep] case={name} path={path} N={N} D={D} K={K}")
+    g = GMM(K, D)
+    try:
+        g.set_path(PATH_FUSED if path == "fused" else PATH_TWO_SWEEP)
+    except Exception as e:  # fused needs P co-resident workgroups
+        pytest.skip(f"fused path unavailable: {e}")
+    got = g.estep_stats(Xg, *gpu_params(params))
+    g.check()
+    got = [t.cpu().numpy() for t in got]
+    want = O.estep_stats(Xn, *params, method=method_for(N, D, K))
+    ms, rms = data_scales(Xn)
+    errs = check_stats((got[0], got[1], got[2], got[3][0]), want, ms, rms,
+                       np.sqrt(params[2].astype(np.float64)), 1e-4)
+    assert not errs, "\n".join(errs)
+
+
+def test_mstep_parity():
+    from soft_clustering_amd import GMM
+    Xn, Xg, params, _, floor = case_data("mid_prefix")
+    N, D = Xn.shape
+    K = params[1].shape[0]
+    Nk, S1, S2, _ = O.estep_stats(Xn, *params, method="gemm")
+    Nk = Nk.copy()
+    Nk[:3] = [0.0, 5e-7, 2e-6]  # empty-rule edge: below / above 1e-6
+    want = O.mstep(Nk, S1, S2, N, floor, params[1], params[2])
+    g = GMM(K, D)
+    w, mu, var = gpu_params(params)
+    g.mstep(*(torch.as_tensor(a).to(DEV) for a in (Nk, S1, S2)), N, floor, w, mu, var)
+    g.check()
+    for got, ref in zip((w, mu, var), want):
+        np.testing.assert_array_equal(got.cpu().numpy(), ref.astype(np.float32))
+
+
+def test_init_parity():
+    from soft_clustering_amd import GMM
+    for name in ("tiny", "odd_d5_k7", "mid_prefix"):
+        Xn, Xg, params, rows, floor = case_data(name)
+        N, D = Xn.shape
+        K = params[1].shape[0]
+        log(f"[init] case={name}")
+        g = GMM(K, D)
+        w, mu, var = g.init(Xg, rows, floor)
+        np.testing.assert_array_equal(w.cpu().numpy(), params[0])
+        np.testing.assert_array_equal(mu.cpu().numpy(), params[1])
+        np.testing.assert_allclose(var.cpu().numpy(), params[2], rtol=2e-7)
+
+
+@pytest.mark.parametrize("path", ["fused", "two_sweep"])
+def test_fit_tiny_per_iteration_and_end_to_end(path):
+    """Tiny workload in full: 10 iterations.  Per iteration (same input
+    parameters on both sides) to 1e-4; after 10 iterations of independent
+    trajectories to 1e-3."""
+    from soft_clustering_amd import GMM, PATH_FUSED, PATH_TWO_SWEEP
+    Xn, Xg, params, rows, floor = case_data("tiny")
+    N, D = Xn.shape
+    K = params[1].shape[0]
+    T = 10
+    g = GMM(K, D)
+    g.set_path(PATH_FUSED if path == "fused" else PATH_TWO_SWEEP)
+    w, mu, var = gpu_params(params)
+    ms, rms = data_scales(Xn)
+    for t in range(T):
+        log(f"[fit-step] path={path} t={t}")
+        th = tuple(a.cpu().numpy().copy() for a in (w, mu, var))
+        Nk, S1, S2, ll = O.estep_stats(Xn, *th, method="direct")
+        want = O.mstep(Nk, S1, S2, N, floor, th[1], th[2])
+        hist = torch.zeros(1, dtype=torch.float64, device=DEV)
+        g.fit(Xg, w, mu, var, 1, floor, hist)
+        g.check()
+        assert abs(hist.item() - ll) <= 1e-4 * abs(ll), (t, hist.item(), ll)
+        errs = check_params((w.cpu(), mu.cpu(), var.cpu()), want, Nk, N, 1e-4)
+        assert not errs, f"iteration {t}:\n" + "\n".join(errs)
+    # end to end
+    w2, mu2, var2 = gpu_params(params)
+    _, _, _, hist = g.fit(Xg, w2, mu2, var2, T, floor)
+    g.check()
+    rw, rmu, rvar, rhist = O.fit(Xn, *params, T, floor, method="direct")
+    np.testing.assert_allclose(hist.cpu().numpy(), rhist, rtol=1e-3)
+    errs = check_params((w2.cpu(), mu2.cpu(), var2.cpu()), (rw, rmu, rvar), np.full(K, 2.0), N, 1e-3)
+    assert not errs, "\n".join(errs)
+    assert np.all(np.diff(hist.cpu().numpy()) >= -1e-6 * np.abs(hist.cpu().numpy()[1:]))
+
+
+@pytest.mark.parametrize("name", ["mid_prefix", "d40_k64", "embed_d768"])
+def test_bit_identical_reruns_and_paths_agree(name):
+    from soft_clustering_amd import GMM, PATH_FUSED, PATH_TWO_SWEEP
+    Xn, Xg, params, _, _ = case_data(name)
+    N, D = Xn.shape
+    K = params[1].shape[0]
+    log(f"[determinism] case={name}")
+    g = GMM(K, D)
+    res = {}
+    for path in (PATH_TWO_SWEEP, PATH_FUSED):
+        try:
+            g.set_path(path)
+        except Exception:
+            continue
+        a = [t.clone() for t in g.estep_stats(Xg, *gpu_params(params))]
+        b = [t.clone() for t in g.estep_stats(Xg, *gpu_params(params))]
+        g.check()
+        for x, y in zip(a, b):
+            assert torch.equal(x, y), f"path {path} not bit-identical"
+        res[path] = [t.cpu().numpy() for t in a]
+    if len(res) == 2:
+        ms, rms = data_scales(Xn)
+        x, y = res[PATH_TWO_SWEEP], res[PATH_FUSED]
+        errs = check_stats((y[0], y[1], y[2], y[3][0]), (x[0], x[1], x[2], x[3][0]), ms, rms,
+                           np.sqrt(params[2].astype(np.float64)), 2e-5)
+        assert not errs, "\n".join(errs)
+
+
+def test_accumulate_over_row_chunks():
+    from soft_clustering_amd import GMM
+    Xn, Xg, params, _, _ = case_data("d100_k300")
+    N, D = Xn.shape
+    K = params[1].shape[0]
+    g = GMM(K, D)
+    p = gpu_params(params)
+    full = [t.cpu().numpy() for t in g.estep_stats(Xg, *p)]
+    out = g.estep_stats(Xg[:1777], *p)
+    g.estep_stats(Xg[1777:], *p, out=out, accumulate=True)
+    g.check()
+    part = [t.cpu().numpy() for t in out]
+    ms, rms = data_scales(Xn)
+    errs = check_stats((part[0], part[1], part[2], part[3][0]), (full[0], full[1], full[2], full[3][0]),
+                       ms, rms, np.sqrt(params[2].astype(np.float64)), 1e-5)
+    assert not errs, "\n".join(errs)
+
+
+def test_zero_weight_and_single_row():
+    from soft_clustering_amd import GMM
+    Xn, Xg, params, _, _ = case_data("d40_k64")
+    w = params[0].copy()
+    w[[3, 17, 40]] = 0.0
+    w = (w / w.sum()).astype(np.float32)
+    p = (w, params[1], params[2])
+    g = GMM(64, 40)
+    for rows in (1, 63, 64, 65):
+        log(f"[edge] rows={rows}")
+        got = [t.cpu().numpy() for t in g.estep_stats(Xg[:rows], *gpu_params(p))]
+        g.check()
+        want = O.estep_stats(Xn[:rows], *p, method="direct")
+        assert np.all(got[0][[3, 17, 40]] == 0.0)
+        ms, rms = data_scales(Xn)
+        errs = check_stats((got[0], got[1], got[2], got[3][0]), want, ms, rms,
+                           np.sqrt(params[2].astype(np.float64)), 1e-4)
+        assert not errs, f"rows={rows}\n" + "\n".join(errs)
+
+
+def test_numeric_fault_is_reported():
+    from soft_clustering_amd import GMM, GMMError
+    Xn, Xg, params, _, _ = case_data("tiny")
+    var = params[2].copy()
+    var[2, 3] = -1.0
+    g = GMM(16, 8)
+    g.estep_stats(Xg, *gpu_params((params[0], params[1], var)))
+    with pytest.raises(GMMError, match="NUMERIC"):
+        g.check()
+    g.check()  # flags cleared
+
+
+def test_bad_arguments_rejected():
+    from soft_clustering_amd import GMM, GMMError
+    Xn, Xg, params, _, _ = case_data("tiny")
+    g = GMM(16, 8)
+    p = gpu_params(params)
+    buf = torch.zeros(Xg.numel() + 1, device=DEV)
+    mis = buf[1:].view(Xg.shape)  # 4-byte offset: not 16-byte aligned
+    with pytest.raises(GMMError, match="INVALID_ARG"):
+        g.estep_stats(mis, *p)
+    with pytest.raises(GMMError, match="INVALID_ARG"):
+        g.fit(Xg, *p, 0, 1e-6)
+    with pytest.raises(GMMError, match="INVALID_ARG"):
+        g.mstep(*(torch.zeros(s, dtype=torch.float64, device=DEV) for s in ((16,), (16, 8), (16, 8))),
+                10.0, 0.0, *p)
+
+
+def test_workspace_is_independent_of_n():
+    """No N x K buffer: the context's device memory is fixed at creation and
+    running on 1e6 rows allocates nothing further in the library."""
+    from soft_clustering_amd import GMM
+    K, D, N = 1024, 128, 1_000_000
+    mix = datagen.mixture("mid", D, K, seed=0)
+    X = datagen.sample(mix, N, seed=0, device=DEV)
+    free0, _ = torch.cuda.mem_get_info()
+    g = GMM(K, D)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    ws = GMM.workspace_bytes(K, D)
+    assert free0 - free1 <= ws + (64 << 20)
+    w, mu, var = g.init(X, datagen.init_rows(N, K), 1e-6)
+    out = g.estep_stats(X, w, mu, var)
+    torch.cuda.synchronize()
+    free2, _ = torch.cuda.mem_get_info()
+    assert free1 - free2 <= (64 << 20), "the E-step allocated device memory"
+    assert ws < N * K * 4 / 10, "workspace must be far below one N x K float matrix"
+    g.check()
+    assert abs(out[0].sum().item() - N) <= 1e-9 * N
