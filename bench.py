@@ -76,6 +76,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="large", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "two_sweep"])
+    ap.add_argument("--precision", default="refined", choices=["refined", "fp32"])
     ap.add_argument("--rows", type=int, default=0, help="override N (testing only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=250_000)
@@ -88,7 +89,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from soft_clustering_amd import GMM, PATH_AUTO, PATH_FUSED, PATH_TWO_SWEEP, datagen
+    from soft_clustering_amd import GMM, PATH_AUTO, PATH_FUSED, PATH_TWO_SWEEP, PREC_FP32, PREC_REFINED, datagen
 
     wl = datagen.WORKLOADS[args.workload]
     N = args.rows or wl.N
@@ -104,6 +105,7 @@ def main():
 
     g = GMM(K, D, dev)
     g.set_path({"auto": PATH_AUTO, "fused": PATH_FUSED, "two_sweep": PATH_TWO_SWEEP}[args.path])
+    g.set_precision(PREC_REFINED if args.precision == "refined" else PREC_FP32)
     w, mu, var = g.init(X, datagen.init_rows(N, K, seed=wl.init_seed), wl.var_floor)
     hist_w = torch.zeros(max(args.warmup, 1), dtype=torch.float64, device=dev)
     if args.warmup > 0:
@@ -114,12 +116,14 @@ def main():
     hist = torch.zeros(args.steps, dtype=torch.float64, device=dev)
     g.profile(True)
     g.profile_read()
+    g.refine_stats()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g.fit(X, w, mu, var, args.steps, wl.var_floor, hist)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     stats_ms, stats_n, logz_ms, logz_n = g.profile_read()
+    n_ref, n_logits = g.refine_stats()
     g.profile(False)
     g.check()
 
@@ -145,7 +149,7 @@ def main():
         "dtype": "f32", "data": "synthetic (seeded mixture, generated on the GPU)",
         "config": {"workload": WORKLOAD_TEXT[args.workload] if not args.rows else
                    f"{args.workload} law with N={N}", "N": N, "K": K, "D": D,
-                   "path": "fused" if fused else "two_sweep"},
+                   "path": "fused" if fused else "two_sweep", "logit_precision": args.precision},
         "pct_mfma_peak": round(100 * gflops / (MFMA_FP32_PEAK_TFLOPS * 1e3), 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4),
@@ -153,6 +157,7 @@ def main():
                      "kernel": "k_stats (fused E-step)" if fused else "k_stats (two-sweep statistics sweep)",
                      "avg_launch_ms": round(avg_ms, 3), "launches": stats_n},
         "loglik_first_last": [float(hl[0]), float(hl[-1])],
+        "refined_logit_fraction": n_ref / max(n_logits, 1.0),
         "x_hbm_gbs_once": round(N * D * 4 / (avg_ms * 1e-3) / 1e9, 1),
     }
     if not fused:

@@ -64,6 +64,20 @@ typedef enum {
                                logit is computed once */
 } gmm_path;
 
+/* Precision of the logits (gmm_set_precision).
+ * REFINED (default): the K logits of every point come from the fp32 MFMA
+ *   contraction, and each logit that can carry a responsibility above
+ *   e^-16 of the point's largest one (judged with a rigorous bound on the
+ *   fp32 error) is recomputed in float64 before the log-sum-exp, so
+ *   responsibilities, statistics and log-likelihood carry float64-grade
+ *   logits wherever they matter.
+ * FP32: no refinement; fp32 expanded-quadratic logits throughout (errors of
+ *   1e-4..1e-2 nats on data spread over many cluster widths). */
+typedef enum {
+    GMM_PREC_REFINED = 0,
+    GMM_PREC_FP32 = 1
+} gmm_precision;
+
 /* Create a context for K components of dimension D on the current HIP device.
  * hip_stream is a hipStream_t (NULL = the null stream).  Allocates the
  * workspace, whose size depends on K, D and the device but not on N (see
@@ -84,6 +98,9 @@ size_t gmm_workspace_bytes(int32_t K, int32_t D);
 /* Select the E-step path (gmm_path).  Both paths compute the same statistics
  * up to float rounding order. */
 gmm_status gmm_set_path(gmm_ctx *ctx, int32_t path);
+
+/* Select the logit precision (gmm_precision) of later E-steps. */
+gmm_status gmm_set_precision(gmm_ctx *ctx, int32_t mode);
 
 /* Initialisation (not on the pages, which warm-start from k-means):
  * means_k = X[init_rows[k]] for K distinct rows; every component gets the
@@ -154,6 +171,11 @@ gmm_status gmm_check(gmm_ctx *ctx);
 gmm_status gmm_profile(gmm_ctx *ctx, int32_t enable);
 gmm_status gmm_profile_read(gmm_ctx *ctx, double *stats_ms, int64_t *stats_launches,
                             double *logz_ms, int64_t *logz_launches);
+
+/* Refinement statistics: synchronises the stream and returns the number of
+ * logits recomputed in float64 and the number of logits the E-step sweeps
+ * evaluated (N*K per sweep) since the previous call, then resets both. */
+gmm_status gmm_refine_stats(gmm_ctx *ctx, int64_t *refined, double *logits);
 
 #ifdef __cplusplus
 }

@@ -14,16 +14,17 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libflashgmm.so")
+LIB_PATH = os.environ.get("FLASHGMM_LIB") or os.path.join(_HERE, "libflashgmm.so")
 
 GMM_OK = 0
 _STATUS = {0: "GMM_OK", 1: "GMM_ERR_INVALID_ARG", 2: "GMM_ERR_UNSUPPORTED", 3: "GMM_ERR_OOM",
            4: "GMM_ERR_HIP", 5: "GMM_ERR_NUMERIC", 6: "GMM_ERR_CAPACITY"}
 PATH_AUTO, PATH_TWO_SWEEP, PATH_FUSED = 0, 1, 2
+PREC_REFINED, PREC_FP32 = 0, 1
 
-EXPORTS = ["gmm_create", "gmm_destroy", "gmm_last_error", "gmm_workspace_bytes", "gmm_set_path",
+EXPORTS = ["gmm_create", "gmm_destroy", "gmm_last_error", "gmm_workspace_bytes", "gmm_set_path", "gmm_set_precision",
            "gmm_init", "gmm_estep_stats", "gmm_mstep", "gmm_fit", "gmm_soft_assign", "gmm_check",
-           "gmm_profile", "gmm_profile_read"]
+           "gmm_profile", "gmm_profile_read", "gmm_refine_stats"]
 
 
 class GMMError(RuntimeError):
@@ -43,6 +44,7 @@ def _load():
         "gmm_last_error": (ctypes.c_char_p, [vp]),
         "gmm_workspace_bytes": (ctypes.c_size_t, [i32, i32]),
         "gmm_set_path": (i32, [vp, i32]),
+        "gmm_set_precision": (i32, [vp, i32]),
         "gmm_init": (i32, [vp, vp, i64, i64, vp, f32, vp, vp, vp]),
         "gmm_estep_stats": (i32, [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32]),
         "gmm_mstep": (i32, [vp, vp, vp, vp, f64, f32, vp, vp, vp]),
@@ -50,6 +52,7 @@ def _load():
         "gmm_soft_assign": (i32, [vp, vp, i64, i64, vp, vp, vp, f32, i32, vp, vp, i64, vp]),
         "gmm_check": (i32, [vp]),
         "gmm_profile": (i32, [vp, i32]),
+        "gmm_refine_stats": (i32, [vp, ctypes.POINTER(i64), ctypes.POINTER(f64)]),
         "gmm_profile_read": (i32, [vp, ctypes.POINTER(f64), ctypes.POINTER(i64), ctypes.POINTER(f64),
                                    ctypes.POINTER(i64)]),
     }
@@ -113,11 +116,18 @@ class GMM:
         self._h = h
 
     def close(self):
-        if getattr(self, "_h", None):
-            _lib.gmm_destroy(self._h)
-            self._h = None
+        h = getattr(self, "_h", None)
+        self._h = None
+        if h:
+            _lib.gmm_destroy(h)
 
-    __del__ = close
+    def __del__(self):
+        # at interpreter shutdown the module globals may already be gone; the
+        # driver releases device memory with the process then
+        try:
+            self.close()
+        except Exception:
+            pass
 
     def _check(self, st):
         if st != GMM_OK:
@@ -129,6 +139,9 @@ class GMM:
 
     def set_path(self, path: int):
         self._check(_lib.gmm_set_path(self._h, int(path)))
+
+    def set_precision(self, mode: int):
+        self._check(_lib.gmm_set_precision(self._h, int(mode)))
 
     def params(self):
         """Fresh fp32 (weights, means, vars) buffers on the device."""
@@ -221,6 +234,13 @@ class GMM:
             self._check(_lib.gmm_profile_read(self._h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
                                               ctypes.byref(d)))
         return a.value, b.value, c.value, d.value
+
+    def refine_stats(self):
+        """(refined logits, evaluated logits) since the last call."""
+        a, b = ctypes.c_int64(), ctypes.c_double()
+        with torch.cuda.device(self.device):
+            self._check(_lib.gmm_refine_stats(self._h, ctypes.byref(a), ctypes.byref(b)))
+        return a.value, b.value
 
     def check(self):
         with torch.cuda.device(self.device):

@@ -23,6 +23,7 @@ struct gmm_ctx {
   size_t bytes = 0;
   int path = GMM_PATH_AUTO;
   std::string err;
+  double logits_since = 0.0;  // N*K summed over E-steps since gmm_refine_stats
   // kernel timing (gmm_profile)
   bool prof = false;
   std::vector<hipEvent_t> ev_free;
@@ -126,7 +127,8 @@ gmm_status estep_into(gmm_ctx* c, const float* X, int64_t N, int64_t ldx, const 
   hk.user = c;
   e = gmm::launch_estep(c->plan, c->ws, X, N, ldx, fused, s, c->prof ? &hk : nullptr);
   if (e != hipSuccess) return hip_fail(c, e, fused ? "fused E-step launch" : "two-sweep E-step launch");
-  e = gmm::launch_reduce(c->plan, c->ws, Nk, S1, S2, ll, accumulate, fused, c->plan.Glogz, s);
+  e = gmm::launch_reduce(c->plan, c->ws, Nk, S1, S2, ll, accumulate, fused, c->plan.Glogz, N, s);
+  c->logits_since += (double)N * (double)c->plan.K * (fused ? 1.0 : 2.0);
   if (e != hipSuccess) return hip_fail(c, e, "reduce launch");
   return GMM_OK;
 }
@@ -183,10 +185,17 @@ gmm_status gmm_create(gmm_ctx** out, int32_t K, int32_t D, void* hip_stream) {
   char* q = (char*)c->base;
   c->ws.wop = carve<float>(q, (size_t)p.Kpad * 2 * p.Dp);
   c->ws.cvec = carve<float>(q, p.Kpad);
+  c->ws.cfull = carve<double>(q, p.Kpad);
+  c->ws.cpeak = carve<double>(q, p.Kpad);
+  c->ws.cshift = carve<double>(q, 1);
+  c->ws.w64 = carve<double2>(q, (size_t)p.Kpad * p.Dp);
+  c->ws.abmax = carve<float2>(q, p.Kpad);
+  c->ws.refine = 1;
+  c->ws.nrefined = carve<unsigned long long>(q, 1);
   c->ws.slots = carve<double>(q, (size_t)p.R * p.Kpad * p.SR);
   c->ws.llslots = carve<double>(q, p.R > p.Glogz ? p.R : p.Glogz);
   c->ws.logz = carve<float>(q, (size_t)p.chunk);
-  c->ws.xbuf = carve<unsigned long long>(q, (size_t)p.R * 2 * p.P * p.BN);
+  c->ws.xbuf = carve<unsigned long long>(q, (size_t)p.R * 4 * p.P * p.BN);
   c->ws.stats = carve<double>(q, (size_t)p.K + 2 * (size_t)p.K * p.D + 1);
   c->ws.colpart = carve<double>(q, (size_t)1024 * p.D);
   c->ws.colmean = carve<double>(q, p.D);
@@ -194,6 +203,7 @@ gmm_status gmm_create(gmm_ctx** out, int32_t K, int32_t D, void* hip_stream) {
   c->ws.flags = carve<int>(q, 4);
   c->ws.colG = 1024;
   e = hipMemsetAsync(c->ws.flags, 0, 16, c->stream);
+  if (e == hipSuccess) e = hipMemsetAsync(c->ws.nrefined, 0, 8, c->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) {
     hipFree(c->base);
@@ -267,6 +277,14 @@ gmm_status gmm_set_path(gmm_ctx* ctx, int32_t path) {
   if (path == GMM_PATH_FUSED && !ctx->plan.fusedOK)
     return fail(ctx, GMM_ERR_UNSUPPORTED, "fused path needs %d co-resident workgroups per row tile", ctx->plan.P);
   ctx->path = path;
+  return GMM_OK;
+}
+
+gmm_status gmm_set_precision(gmm_ctx* ctx, int32_t mode) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  if (mode != GMM_PREC_REFINED && mode != GMM_PREC_FP32)
+    return fail(ctx, GMM_ERR_INVALID_ARG, "unknown precision mode %d", mode);
+  ctx->ws.refine = (mode == GMM_PREC_REFINED) ? 1 : 0;
   return GMM_OK;
 }
 
@@ -359,6 +377,20 @@ gmm_status gmm_soft_assign(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx,
   if (ids_capacity > 0 && !list_ids) return fail(ctx, GMM_ERR_INVALID_ARG, "list_ids is NULL");
   if (N >= ((int64_t)1 << 31)) return fail(ctx, GMM_ERR_INVALID_ARG, "N must be < 2^31 for int32 ids");
   return fail(ctx, GMM_ERR_UNSUPPORTED, "soft assignment not built yet");
+}
+
+gmm_status gmm_refine_stats(gmm_ctx* ctx, int64_t* refined, double* logits) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  hipError_t e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "stream synchronize");
+  unsigned long long n = 0;
+  e = hipMemcpy(&n, ctx->ws.nrefined, sizeof n, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemset(ctx->ws.nrefined, 0, sizeof n);
+  if (e != hipSuccess) return hip_fail(ctx, e, "refine counter");
+  if (refined) *refined = (int64_t)n;
+  if (logits) *logits = ctx->logits_since;
+  ctx->logits_since = 0.0;
+  return GMM_OK;
 }
 
 gmm_status gmm_check(gmm_ctx* ctx) {

@@ -32,7 +32,14 @@ struct Plan {
 
 struct Workspace {
   float* wop;        // Kpad * 2*Dp  MFMA-operand-ordered [a | b] per dim
-  float* cvec;       // Kpad         per-component constant (-inf for padding)
+  float* cvec;       // Kpad         per-component constant minus the global offset C (-inf: padding)
+  double* cfull;     // Kpad         per-component constant, float64
+  double* cpeak;     // Kpad         component log-density at its mean
+  double* cshift;    // 1            global logit offset C
+  double2* w64;      // Kpad * Dp    float64 (a, b) for the logit refinement
+  float2* abmax;     // Kpad         per-component max |a|, max |b|
+  int refine;        // 1: float64 refinement of the logits that matter
+  unsigned long long* nrefined;  // refined-logit counter (gmm_refine_stats)
   double* slots;     // R * Kpad * SR
   double* llslots;   // max(R, Glogz)
   float* logz;       // chunk
@@ -63,7 +70,8 @@ struct LaunchHooks {
 hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx,
                         bool fused, hipStream_t s, const LaunchHooks* hooks = nullptr);
 hipError_t launch_reduce(const Plan& p, const Workspace& w, double* Nk, double* S1, double* S2,
-                         double* ll, int accumulate, bool fused, int64_t nllslots, hipStream_t s);
+                         double* ll, int accumulate, bool fused, int64_t nllslots, int64_t nrows,
+                         hipStream_t s);
 hipError_t launch_mstep(const Plan& p, const Workspace& w, const double* Nk, const double* S1,
                         const double* S2, double n_total, float var_floor, float* weights,
                         float* means, float* vars, hipStream_t s);

@@ -29,6 +29,7 @@
 #include "gmm_internal.h"
 
 #include <math.h>
+#include <stdlib.h>
 
 namespace gmm {
 
@@ -87,6 +88,14 @@ struct EArgs {
   int* flags;
   int K, D, Kpad, P, R, Dp;
   int slot_acc;   // 1: add into slots / llslots
+  // float64 refinement of the logits that matter
+  int refine;
+  float kappa;           // fp32 logit error bound factor ((2 Dp + 8) 2^-24)
+  const double2* w64;    // Kpad x Dp  (a, b) in float64
+  const double* cfull;   // Kpad  float64 component constants
+  const double* cshift;  // global logit offset C
+  const float2* abmax;   // Kpad  (max_d |a_kd|, max_d |b_kd|)
+  unsigned long long* nrefined;  // count of refined logits (statistics only)
 };
 
 // ---------------------------------------------------------------------------
@@ -99,9 +108,13 @@ struct Shape {
   static constexpr int SS = 2 * DPW + 4;      // LDS floats per wave segment of a row
   static constexpr int RS = WD * SS;          // LDS floats per row
   static constexpr int TILE = BN * RS;        // LDS floats per tile buffer
-  // double-buffer the X tile only when each thread stages few float4s
+  // Two workgroups per CU for 4-wave shapes (their barrier, exchange and
+  // refinement phases then overlap the other workgroup's MFMA work), one
+  // otherwise.  Double-buffer the X tile only for one-per-CU shapes whose
+  // threads stage few float4s.
+  static constexpr int WGS_PER_CU = (WC * WD == 4) ? 2 : 1;
   static constexpr int PER_STAGE = (BN * WD * DPW / 4 + NT - 1) / NT;
-  static constexpr int NBUF = (PER_STAGE <= 8 && TILE * 8 <= 140 * 1024) ? 2 : 1;
+  static constexpr int NBUF = (WGS_PER_CU == 1 && PER_STAGE <= 8 && TILE * 8 <= 140 * 1024) ? 2 : 1;
   static constexpr int HALF = DPW / 2;
   static constexpr int RED = (WD > 1) ? WD * WC * NPB * 8 * kWave : 1;  // partial-logit exchange
 };
@@ -225,6 +238,184 @@ __device__ __forceinline__ const float* wop_block(const float* wop, int cb16, in
   return wop + (size_t)(cb16 * WD + wd) * (DPW / 8) * 256;
 }
 
+// ---------------------------------------------------------------------------
+// Float64 refinement of the logits that can matter.
+//
+// The fp32 expanded quadratic c + sum_d (a x^2 + b x) cancels terms whose
+// magnitudes add up to S = sum_d (|a| x^2 + |b x|) + |c - C|, so its error is
+// bounded by E = (2 Dp + 8) 2^-24 S (Dp k-step roundings of partial sums that
+// never exceed S, plus the roundings of x^2, a, b and c).  For data spread
+// over many cluster widths that is 1e-3..1e-2 nats, too much for overlapping
+// components.  Every logit with L + E >= (a lower bound of the row's largest
+// logit) - kDelta is recomputed from float64 a, b, c and exact float64 x^2;
+// all others have responsibility < e^-kDelta relative to the row maximum, so
+// their fp32 error is immaterial.  For clustered data a row has a handful of
+// such logits, so the float64 work is a few percent of the MFMA work.
+constexpr float kDelta = 16.f;
+constexpr int kRefineCap = 256;  // list entries per component group and batch
+
+// Bound on the fp32 error of one logit: kappa (max|a_k| ||x||^2 + max|b_k| ||x||_1 + |c_k - C|).
+__device__ __forceinline__ float err_bound(float kappa, float al, float be, float cv, float2 nn) {
+  return kappa * (al * nn.x + be * nn.y + cv);
+}
+
+// Per-lane error-bound coefficients of this wave's two component blocks:
+// co = (max|a|, max|b|, |c - C|) for the lane's component in block 0, then 1.
+__device__ __forceinline__ void lane_coefs(const EArgs& a, int compbase, int r16, float (&co)[6]) {
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int k = compbase + cb * 16 + r16;
+    const float2 ab = a.abmax[k];
+    const float c = a.cvec[k];
+    co[3 * cb + 0] = ab.x;
+    co[3 * cb + 1] = ab.y;
+    co[3 * cb + 2] = (c == kNegInf) ? 0.f : fabsf(c);
+  }
+}
+
+// ||x||^2 and ||x||_1 of each staged row into nrm[pt] (slightly rounded up).
+template <class SH, int DPW>
+__device__ __forceinline__ void row_norms2(const float* __restrict__ xt, float2* __restrict__ nrm, int Dp) {
+  constexpr int BN = SH::TILE / SH::RS;
+  constexpr int TPR = SH::NT / BN;  // threads per row (power of two)
+  const int pt = threadIdx.x / TPR, sub = threadIdx.x % TPR;
+  float n2 = 0.f, n1 = 0.f;
+  if (pt < BN) {
+    const float* xrow = xt + pt * SH::RS;
+    for (int d = sub; d < Dp; d += TPR) {
+      const int seg = d / DPW;
+      const int ee = d - seg * DPW;
+      const int h = ee / SH::HALF;
+      const int o = ee - h * SH::HALF;
+      n2 += xrow[seg * SH::SS + 2 * h * SH::HALF + o];
+      n1 += fabsf(xrow[seg * SH::SS + (2 * h + 1) * SH::HALF + o]);
+    }
+  }
+#pragma unroll
+  for (int o = TPR / 2; o > 0; o >>= 1) {
+    n2 += __shfl_xor(n2, o);
+    n1 += __shfl_xor(n1, o);
+  }
+  if (pt < BN && sub == 0) nrm[pt] = make_float2(n2 * (1.f + 1e-6f), n1 * (1.f + 1e-6f));
+}
+
+// thr[pt]: the row's selection threshold (error-bound slack and kDelta
+// included): a logit L is recomputed in float64 when L >= thr[pt].
+template <class SH, int WD, int DPW>
+__device__ __forceinline__ void refine_tile(f4 (&acc)[SH::NPB][2], const float* __restrict__ thr,
+                                            const float2* __restrict__ nrm, const float (&co)[6],
+                                            const float* __restrict__ xt, int rows, const EArgs& a, double C,
+                                            int compbase, float* __restrict__ rlist,
+                                            unsigned short* __restrict__ elist, int lane, int wd) {
+  constexpr int NREG = SH::NPB * 8;
+  constexpr int DPT = DPW * WD / 16;           // dims per lane (16 lanes per logit)
+  constexpr int DCH = DPT < 4 ? DPT : 4;       // dims with loads in flight together
+  const int g = lane >> 4, r16 = lane & 15;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  // 1. one selection bit per register
+  unsigned sel = 0;
+  const bool cok0 = compbase + r16 < a.K, cok1 = compbase + 16 + r16 < a.K;
+#pragma unroll
+  for (int pb = 0; pb < SH::NPB; ++pb) {
+    const f4 t4 = *reinterpret_cast<const f4*>(thr + pb * 16 + 4 * g);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int pt = pb * 16 + 4 * g + v;
+      const bool rok = pt < rows;
+      const float2 nn = nrm[pt];
+      const float L0 = acc[pb][0][v], L1 = acc[pb][1][v];
+      const float E0 = err_bound(a.kappa, co[0], co[1], co[2], nn);
+      const float E1 = err_bound(a.kappa, co[3], co[4], co[5], nn);
+      const bool b0 = rok && cok0 && (L0 != kNegInf) && (L0 + E0 >= t4[v]);
+      const bool b1 = rok && cok1 && (L1 != kNegInf) && (L1 + E1 >= t4[v]);
+      sel |= (b0 ? 1u : 0u) << (pb * 8 + v);
+      sel |= (b1 ? 1u : 0u) << (pb * 8 + 4 + v);
+    }
+  }
+  if (wd == 0) {
+    int tot = __popc(sel);
+    for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
+    if (lane == 0 && tot > 0) atomicAdd(a.nrefined, (unsigned long long)tot);
+  }
+  int rstart = 0;
+  while (rstart < NREG) {
+    // 2. list the selected logits of registers [rstart, rend)
+    int count = 0, rend = NREG;
+#pragma unroll
+    for (int r = 0; r < NREG; ++r) {
+      if (r >= rstart && r < rend) {
+        const bool b = (sel >> r) & 1u;
+        const unsigned long long m = __ballot(b);
+        const int n = __popcll(m);
+        if (count + n > kRefineCap) {
+          rend = r;
+        } else {
+          if (b && wd == 0) elist[count + __popcll(m & below)] = (unsigned short)((r << 6) | lane);
+          count += n;
+        }
+      }
+    }
+    if (count == 0) break;  // uniform: nothing (more) selected
+    if constexpr (WD > 1) __syncthreads();
+    else { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); __builtin_amdgcn_wave_barrier(); }
+    // 3. float64 logits: 16 lanes per entry, 4 entries per pass; the WD
+    //    dim-segment waves of a component group share the passes.
+    for (int base = wd * 4; base < count; base += 4 * WD) {
+      const int e = base + g;
+      const bool live = e < count;
+      const int code = live ? (int)elist[e] : 0;
+      const int r = code >> 6, ln = code & 63;
+      const int pt = (r >> 3) * 16 + 4 * (ln >> 4) + (r & 3);
+      const int comp = compbase + ((r >> 2) & 1) * 16 + (ln & 15);
+      const float* xrow = xt + pt * SH::RS;
+      const double2* wr = a.w64 + (size_t)comp * a.Dp;
+      double t = 0.0;
+      if (live) {
+#pragma unroll
+        for (int j0 = 0; j0 < DPT; j0 += DCH) {
+          double2 ab[DCH];
+          float xv[DCH];
+#pragma unroll
+          for (int j = 0; j < DCH; ++j) {
+            const int d = r16 + 16 * (j0 + j);  // < Dp: padded dims have a = b = 0
+            const int seg = d / DPW;
+            const int ee = d - seg * DPW;
+            const int h = ee / SH::HALF;
+            ab[j] = wr[d];
+            xv[j] = xrow[seg * SH::SS + (2 * h + 1) * SH::HALF + (ee - h * SH::HALF)];
+          }
+#pragma unroll
+          for (int j = 0; j < DCH; ++j) {
+            const double x = (double)xv[j];
+            t = fma(ab[j].x, x * x, fma(ab[j].y, x, t));
+          }
+        }
+      }
+      t += __shfl_xor(t, 8);
+      t += __shfl_xor(t, 4);
+      t += __shfl_xor(t, 2);
+      t += __shfl_xor(t, 1);
+      if (live && r16 == 0) rlist[e] = (float)((a.cfull[comp] - C) + t);
+    }
+    if constexpr (WD > 1) __syncthreads();
+    else { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); __builtin_amdgcn_wave_barrier(); }
+    // 4. owners take their refined logits back
+    int c2 = 0;
+#pragma unroll
+    for (int r = 0; r < NREG; ++r) {
+      if (r >= rstart && r < rend) {
+        const bool b = (sel >> r) & 1u;
+        const unsigned long long m = __ballot(b);
+        if (b) acc[r >> 3][(r >> 2) & 1][r & 3] = rlist[c2 + __popcll(m & below)];
+        c2 += __popcll(m);
+      }
+    }
+    if constexpr (WD > 1) __syncthreads();
+    else { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); __builtin_amdgcn_wave_barrier(); }
+    rstart = rend;
+  }
+}
+
 // Row group / member of a workgroup.  Members of one row group sit on one XCD
 // when the grid allows (consecutive workgroup ids go round-robin over the 8
 // XCDs), so the P re-reads of an X tile and the exchange stay in one L2.
@@ -242,9 +433,69 @@ __device__ __forceinline__ void rg_member(int G, int P, int& rg, int& p) {
 }
 
 // ---------------------------------------------------------------------------
+// Cross-workgroup exchange of one per-row value among the P workgroups of a
+// row group (fused path).  Each workgroup publishes vin[pt] as a 64-bit word
+// (tile tag in the high half, the float in the low half) with agent-scope
+// atomic stores, then gathers the P words of each row, spinning (bounded)
+// until their tags match, and combines them in a fixed order: the maximum
+// (LSE = false) or the log-sum-exp (LSE = true).  Two rounds per tile use
+// separate slots, and slots alternate by tile parity, so a fast member never
+// overwrites a word a slower member has not read yet.
+template <int BN, int QP, bool LSE>
+__device__ __forceinline__ void row_exchange(const EArgs& a, int rg, int p, int j, int rd, const float* vin,
+                                             float (*exm)[BN], float (*exs)[BN], float* vout) {
+  const int tid = threadIdx.x;
+  const unsigned tag = (unsigned)(j + 1);
+  unsigned long long* xb = a.xbuf + ((size_t)((rg * 2 + rd) * 2 + (j & 1)) * a.P) * BN;
+  if (tid < BN) {
+    const unsigned long long word = ((unsigned long long)tag << 32) | (unsigned long long)__float_as_uint(vin[tid]);
+    __hip_atomic_store(xb + (size_t)p * BN + tid, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (tid < QP * BN) {
+    const int pt = tid % BN, qp = tid / BN;
+    float M = kNegInf, S = 0.f;
+    for (int q = qp; q < a.P; q += QP) {
+      const unsigned long long* src = xb + (size_t)q * BN + pt;
+      unsigned long long word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // Bounded wait: a peer that never publishes (impossible while all
+      // workgroups are co-resident) ends in flags[1] and a drained grid.
+      for (int spins = 0; (unsigned)(word >> 32) != tag; ++spins) {
+        if ((spins & 255) == 0 && __hip_atomic_load(&a.flags[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+          break;
+        if (spins > (1 << 20)) {
+          __hip_atomic_store(&a.flags[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      const float val = __uint_as_float((unsigned)(word & 0xffffffffu));
+      if constexpr (LSE)
+        lse_merge(M, S, val, 1.f);
+      else
+        M = fmaxf(M, val);
+    }
+    exm[qp][pt] = M;
+    exs[qp][pt] = S;
+  }
+  __syncthreads();
+  if (tid < BN) {
+    float M = kNegInf, S = 0.f;
+#pragma unroll
+    for (int k = 0; k < QP; ++k) {
+      if constexpr (LSE)
+        lse_merge(M, S, exm[k][tid], exs[k][tid]);
+      else
+        M = fmaxf(M, exm[k][tid]);
+    }
+    vout[tid] = LSE ? lse_of(M, S) : M;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // E-step statistics sweep.  FUSED: per-row log Z by exchange; else from a.logz.
-template <int WC, int WD, int DPW, int BN, bool FUSED>
-__global__ void __launch_bounds__(kWave* WC* WD) k_stats(EArgs a) {
+template <int WC, int WD, int DPW, int BN, bool FUSED, bool REFINE>
+__global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats(EArgs a) {
   using SH = Shape<WC, WD, DPW, BN>;
   constexpr int NPB = SH::NPB, NFB = SH::NFB;
   constexpr int FLUSH = (BN >= 64) ? 16 : 64;  // tiles between fp64 flushes (~1024 rows)
@@ -256,6 +507,11 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_stats(EArgs a) {
   __shared__ float lpart[WC][BN];
   __shared__ float exm[QP][BN], exs[QP][BN];
   __shared__ double llred[BN];
+  __shared__ float2 nrm[BN];
+  __shared__ __attribute__((aligned(16))) float thrs[BN];
+  __shared__ float vtmp[BN];
+  __shared__ float rlist[WC][kRefineCap];
+  __shared__ unsigned short elist[WC][kRefineCap];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wc = w % WC, wd = w / WC;
@@ -269,6 +525,9 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_stats(EArgs a) {
   const float* w1 = wop_block(a.wop, cb16 + 1, WD, wd, DPW);
   const float c0 = (wd == 0) ? a.cvec[compbase + r16] : 0.f;
   const float c1 = (wd == 0) ? a.cvec[compbase + 16 + r16] : 0.f;
+  const double C = *a.cshift;
+  float co[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if constexpr (REFINE) lane_coefs(a, compbase, r16, co);
 
   const int nt = (int)((a.nrows + BN - 1) / BN);
   f4 sacc[2][NFB];
@@ -344,6 +603,43 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_stats(EArgs a) {
     logit_tile<SH, DPW>(xt[cur], w0, w1, acc, lane, wd);
     reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
 
+    // ---- float64 refinement of the logits that can matter
+    if constexpr (REFINE) {
+      row_norms2<SH, DPW>(xt[cur], nrm, a.Dp);
+      __syncthreads();
+      if constexpr (FUSED) {
+        // round 1 of the exchange: each workgroup's largest lower bound
+        // L - E of the row's logits; their maximum bounds the row's largest
+        // true logit from below, for every workgroup of the row group alike
+        if (wd == 0) {
+#pragma unroll
+          for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float2 nn = nrm[pb * 16 + 4 * g + v];
+              const float lb = fmaxf(acc[pb][0][v] - err_bound(a.kappa, co[0], co[1], co[2], nn),
+                                     acc[pb][1][v] - err_bound(a.kappa, co[3], co[4], co[5], nn));
+              const float m = row16_max(lb);
+              if (r16 == 0) lpart[wc][pb * 16 + 4 * g + v] = m;
+            }
+        }
+        __syncthreads();
+        if (tid < BN) {
+          float m = kNegInf;
+#pragma unroll
+          for (int k = 0; k < WC; ++k) m = fmaxf(m, lpart[k][tid]);
+          vtmp[tid] = m;
+        }
+        row_exchange<BN, QP, false>(a, rg, p, j, 0, vtmp, exm, exs, thrs);
+        if (tid < BN) thrs[tid] = (tid < rows) ? thrs[tid] - kDelta : kPosInf;
+      } else {
+        // reference: the row's final log Z from the first sweep
+        if (tid < BN) thrs[tid] = ((tid < rows) ? a.logz[trow + tid] : kPosInf) - kDelta;
+      }
+      __syncthreads();
+      refine_tile<SH, WD, DPW>(acc, thrs, nrm, co, xt[cur], rows, a, C, compbase, rlist[wc], elist[wc], lane, wd);
+    }
+
     // ---- per-row log Z
     if constexpr (FUSED) {
       if (wd == 0) {
@@ -359,49 +655,17 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_stats(EArgs a) {
           }
       }
       __syncthreads();
-      const unsigned tag = (unsigned)(j + 1);
-      unsigned long long* xb = a.xbuf + ((size_t)(rg * 2 + (j & 1)) * a.P) * BN;
       if (tid < BN) {
         float M = kNegInf, S = 0.f;
 #pragma unroll
         for (int k = 0; k < WC; ++k) lse_merge(M, S, lpart[k][tid], 1.f);
-        const float mine = lse_of(M, S);
-        const unsigned long long word =
-            ((unsigned long long)tag << 32) | (unsigned long long)__float_as_uint(mine);
-        __hip_atomic_store(xb + (size_t)p * BN + tid, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        vtmp[tid] = lse_of(M, S);
       }
-      if (tid < QP * BN) {
-        const int pt = tid % BN, qp = tid / BN;
-        float M = kNegInf, S = 0.f;
-        for (int q = qp; q < a.P; q += QP) {
-          const unsigned long long* src = xb + (size_t)q * BN + pt;
-          unsigned long long word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          // Bounded wait: a peer that never publishes (impossible while all
-          // workgroups are co-resident) ends in flags[1] and a drained grid.
-          for (int spins = 0; (unsigned)(word >> 32) != tag; ++spins) {
-            if ((spins & 255) == 0 &&
-                __hip_atomic_load(&a.flags[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
-              break;
-            if (spins > (1 << 20)) {
-              __hip_atomic_store(&a.flags[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-            word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-          lse_merge(M, S, __uint_as_float((unsigned)(word & 0xffffffffu)), 1.f);
-        }
-        exm[qp][pt] = M;
-        exs[qp][pt] = S;
-      }
-      __syncthreads();
+      row_exchange<BN, QP, true>(a, rg, p, j, 1, vtmp, exm, exs, lzt);
       if (tid < BN) {
-        float M = kNegInf, S = 0.f;
-#pragma unroll
-        for (int k = 0; k < QP; ++k) lse_merge(M, S, exm[k][tid], exs[k][tid]);
-        const float lz = lse_of(M, S);
-        lzt[tid] = (tid < rows) ? lz : kPosInf;
+        const float lz = lzt[tid];
         if (p == 0 && tid < rows) ll += (double)lz;
+        if (tid >= rows) lzt[tid] = kPosInf;
       }
     } else {
       if (tid < BN) lzt[tid] = (tid < rows) ? a.logz[trow + tid] : kPosInf;
@@ -467,19 +731,24 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_stats(EArgs a) {
 // First sweep of the two-sweep path: log Z of every row of the chunk, over all
 // components (Algorithm 1 steps 6-10), plus a float64 log-likelihood partial
 // per workgroup.
-template <int WC, int WD, int DPW, int BN>
-__global__ void __launch_bounds__(kWave* WC* WD) k_logz(EArgs a) {
+template <int WC, int WD, int DPW, int BN, bool REFINE>
+__global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_logz(EArgs a) {
   using SH = Shape<WC, WD, DPW, BN>;
   constexpr int NPB = SH::NPB;
   __shared__ __attribute__((aligned(16))) float xt[SH::TILE];
   __shared__ __attribute__((aligned(16))) float red[SH::RED];
   __shared__ float lpart[WC][BN];
   __shared__ double llred[BN];
+  __shared__ float2 nrm[BN];
+  __shared__ __attribute__((aligned(16))) float thrw[WC][BN];
+  __shared__ float rlist[WC][kRefineCap];
+  __shared__ unsigned short elist[WC][kRefineCap];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wc = w % WC, wd = w / WC;
   const int g = lane >> 4, r16 = lane & 15;
   const int ncg = a.Kpad / 32;
+  const double C = *a.cshift;
   const int nt = (int)((a.nrows + BN - 1) / BN);
   double ll = 0.0;
 
@@ -492,13 +761,18 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_logz(EArgs a) {
       stg.store(xt);
     }
     __syncthreads();
-    float M[NPB][4], S[NPB][4];
+    if constexpr (REFINE) {
+      row_norms2<SH, DPW>(xt, nrm, a.Dp);
+      __syncthreads();
+    }
+    float M[NPB][4], S[NPB][4], Rlb[NPB][4];
 #pragma unroll
     for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         M[pb][v] = kNegInf;
         S[pb][v] = 0.f;
+        Rlb[pb][v] = kNegInf;
       }
     for (int cg = wc; cg < ncg; cg += WC) {
       const int compbase = cg * 32;
@@ -513,6 +787,27 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_logz(EArgs a) {
       logit_tile<SH, DPW>(xt, wop_block(a.wop, compbase >> 4, WD, wd, DPW),
                           wop_block(a.wop, (compbase >> 4) + 1, WD, wd, DPW), acc, lane, wd);
       reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
+      if constexpr (REFINE) {
+        // reference: running max over the components seen so far of the
+        // guaranteed lower bounds L - E (it only grows, so a logit left
+        // unrefined stays more than kDelta below the row's final maximum)
+        float co[6];
+        lane_coefs(a, compbase, r16, co);
+#pragma unroll
+        for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float2 nn = nrm[pb * 16 + 4 * g + v];
+            const float lb = fmaxf(acc[pb][0][v] - err_bound(a.kappa, co[0], co[1], co[2], nn),
+                                   acc[pb][1][v] - err_bound(a.kappa, co[3], co[4], co[5], nn));
+            Rlb[pb][v] = fmaxf(Rlb[pb][v], row16_max(lb));
+            if (r16 == 0 && wd == 0) thrw[wc][pb * 16 + 4 * g + v] = Rlb[pb][v] - kDelta;
+          }
+        if constexpr (WD > 1) __syncthreads();
+        else { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); __builtin_amdgcn_wave_barrier(); }
+        refine_tile<SH, WD, DPW>(acc, thrw[wc], nrm, co, xt, rows, a, C, compbase, rlist[wc], elist[wc], lane,
+                                 wd);
+      }
 #pragma unroll
       for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
@@ -586,12 +881,16 @@ __global__ void k_precompute_w(const float* __restrict__ mu, const float* __rest
 }
 
 __global__ void k_precompute_c(const float* __restrict__ w, const float* __restrict__ mu,
-                               const float* __restrict__ var, float* cvec, int K, int D, int Kpad) {
+                               const float* __restrict__ var, double* cfull, double* cpeak, int K, int D,
+                               int Kpad) {
   const int comp = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   const int lane = threadIdx.x & 63;
   if (comp >= Kpad) return;
   if (comp >= K) {
-    if (lane == 0) cvec[comp] = kNegInf;
+    if (lane == 0) {
+      cfull[comp] = -__builtin_huge_val();
+      cpeak[comp] = -__builtin_huge_val();
+    }
     return;
   }
   double q = 0.0, ld = 0.0;
@@ -607,9 +906,57 @@ __global__ void k_precompute_c(const float* __restrict__ w, const float* __restr
   }
   if (lane == 0) {
     const double wk = (double)w[comp];
-    cvec[comp] = (wk > 0.0) ? (float)(log(wk) - 0.5 * q - 0.5 * ld - 0.5 * D * kLog2Pi)
-                            : ((wk == 0.0) ? kNegInf : __builtin_nanf(""));
+    const double lw = (wk > 0.0) ? log(wk) : ((wk == 0.0) ? -__builtin_huge_val() : __builtin_nan(""));
+    // log-density of the component at its own mean, and the full constant
+    cpeak[comp] = lw - 0.5 * ld - 0.5 * D * kLog2Pi;
+    cfull[comp] = cpeak[comp] - 0.5 * q;
   }
+}
+
+// Float64 (a, b) per component and dimension for the refinement, and the
+// per-component maxima of |a| and |b| used in its error bound.
+__global__ void k_precompute_w64(const float* __restrict__ mu, const float* __restrict__ var, double2* w64,
+                                 float2* abmax, int K, int D, int Kpad, int Dp) {
+  const int comp = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x & 63;
+  if (comp >= Kpad) return;
+  double ma = 0.0, mb = 0.0;
+  for (int d = lane; d < Dp; d += kWave) {
+    double2 ab = make_double2(0.0, 0.0);
+    if (comp < K && d < D) {
+      const double s2 = (double)var[(size_t)comp * D + d];
+      ab = make_double2(-0.5 / s2, (double)mu[(size_t)comp * D + d] / s2);
+    }
+    w64[(size_t)comp * Dp + d] = ab;
+    ma = fmax(ma, fabs(ab.x));
+    mb = fmax(mb, fabs(ab.y));
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    ma = fmax(ma, __shfl_xor(ma, o));
+    mb = fmax(mb, __shfl_xor(mb, o));
+  }
+  if (lane == 0) abmax[comp] = make_float2((float)(ma * (1.0 + 1e-6)), (float)(mb * (1.0 + 1e-6)));
+}
+
+// Global logit offset C = max_k (peak log-density) - D/2: a typical logit of
+// a point near its component.  c_k - C is rounded to float32, so the fp32
+// logits (and log Z) are centred near 0 instead of carrying magnitudes of
+// hundreds to thousands of nats; the log-likelihood adds N*C back in fp64.
+__global__ void k_precompute_shift(const double* __restrict__ cfull, const double* __restrict__ cpeak,
+                                   float* cvec, double* cshift, int Kpad, int D) {
+  __shared__ double red[1024];
+  double m = -__builtin_huge_val();
+  for (int k = threadIdx.x; k < Kpad; k += blockDim.x) m = fmax(m, cpeak[k]);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int st = blockDim.x / 2; st > 0; st >>= 1) {
+    if (threadIdx.x < st) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + st]);
+    __syncthreads();
+  }
+  double C = red[0] - 0.5 * D;
+  if (!isfinite(C)) C = 0.0;
+  for (int k = threadIdx.x; k < Kpad; k += blockDim.x) cvec[k] = (float)(cfull[k] - C);
+  if (threadIdx.x == 0) *cshift = C;
 }
 
 // ---------------------------------------------------------------------------
@@ -664,9 +1011,9 @@ __global__ void k_reduce(const double* __restrict__ slots, int R, int Kpad, int 
 }
 
 __global__ void k_reduce_ll(const double* __restrict__ llslots, int n, double* ll, int accumulate,
-                            int* flags) {
+                            int* flags, const double* __restrict__ cshift, double nrows) {
   if (threadIdx.x == 0 && blockIdx.x == 0) {
-    const double v = pairwise_sum(llslots, 1, n);
+    const double v = pairwise_sum(llslots, 1, n) + nrows * (*cshift);
     const double out = accumulate ? *ll + v : v;
     *ll = out;
     if (!isfinite(out)) flags[0] = 1;
@@ -739,23 +1086,28 @@ __global__ void k_init_params(const float* __restrict__ X, int64_t ldx, const in
 template <int WC, int WD, int DPW>
 struct Kern {
   static constexpr int BN = (WD == 1) ? 64 : 16;
-  static void* stats_fused() { return (void*)&k_stats<WC, WD, DPW, BN, true>; }
-  static void* stats_two() { return (void*)&k_stats<WC, WD, DPW, BN, false>; }
-  static void* logz() { return (void*)&k_logz<WC, WD, DPW, BN>; }
+  template <bool R>
+  static void* stats_fused() { return (void*)&k_stats<WC, WD, DPW, BN, true, R>; }
+  template <bool R>
+  static void* stats_two() { return (void*)&k_stats<WC, WD, DPW, BN, false, R>; }
+  template <bool R>
+  static void* logz() { return (void*)&k_logz<WC, WD, DPW, BN, R>; }
 };
 
 struct KTab {
-  void* fused;
-  void* two;
-  void* logz;
+  void* fused[2];  // [refine]
+  void* two[2];
+  void* logz[2];
 };
 
 static bool lookup(int WC, int WD, int DPW, KTab& t) {
-#define GMM_K(wc, wd, dpw)                                                     \
-  if (WC == wc && WD == wd && DPW == dpw) {                                    \
-    t = KTab{Kern<wc, wd, dpw>::stats_fused(), Kern<wc, wd, dpw>::stats_two(), \
-             Kern<wc, wd, dpw>::logz()};                                       \
-    return true;                                                               \
+#define GMM_K(wc, wd, dpw)                                                                            \
+  if (WC == wc && WD == wd && DPW == dpw) {                                                           \
+    using KK = Kern<wc, wd, dpw>;                                                                     \
+    t = KTab{{KK::stats_fused<false>(), KK::stats_fused<true>()},                                     \
+             {KK::stats_two<false>(), KK::stats_two<true>()},                                         \
+             {KK::logz<false>(), KK::logz<true>()}};                                                  \
+    return true;                                                                                      \
   }
   GMM_K(1, 1, 16) GMM_K(1, 1, 32) GMM_K(1, 1, 64) GMM_K(1, 1, 128)
   GMM_K(2, 1, 16) GMM_K(2, 1, 32) GMM_K(2, 1, 64) GMM_K(2, 1, 128)
@@ -770,10 +1122,12 @@ static size_t lds_stats_bytes(int WC, int WD, int DPW) {
   const int BN = (WD == 1) ? 64 : 16;
   const int RS = WD * (2 * DPW + 4);
   const int NTh = 64 * WC * WD;
-  const int NBUF = ((BN * WD * DPW / 4 + NTh - 1) / NTh <= 8 && (size_t)BN * RS * 8 <= 140 * 1024) ? 2 : 1;
+  const int per_cu = (WC * WD == 4) ? 2 : 1;
+  const int NBUF = (per_cu == 1 && (BN * WD * DPW / 4 + NTh - 1) / NTh <= 8 && (size_t)BN * RS * 8 <= 140 * 1024) ? 2 : 1;
   const int QP = (64 * WC * WD) / BN;
   size_t b = (size_t)NBUF * BN * RS * 4 + (WD > 1 ? (size_t)WD * WC * (BN / 16) * 8 * 64 * 4 : 4);
   b += BN * 4 + (size_t)WC * BN * 4 + 2 * (size_t)QP * BN * 4 + BN * 8 + 4;
+  b += BN * 8 + BN * 8 + (size_t)WC * 256 * 6;
   return b;
 }
 
@@ -785,7 +1139,11 @@ Plan make_plan(int K, int D, int numCU, int occStats, int occLogz) {
     p.WD = 1;
     p.DPW = D <= 16 ? 16 : D <= 32 ? 32 : D <= 64 ? 64 : 128;
     const int groups = (K + 31) / 32;
-    p.WC = groups >= 8 ? 8 : groups >= 4 ? 4 : groups >= 2 ? 2 : 1;
+    // 4-wave workgroups, two per CU; FLASHGMM_WC=8 selects one 8-wave
+    // workgroup per CU instead (a tuning knob for measurements)
+    const char* env = getenv("FLASHGMM_WC");
+    const int wmax = (env && atoi(env) == 8) ? 8 : 4;
+    p.WC = groups >= wmax ? wmax : groups >= 4 ? 4 : groups >= 2 ? 2 : 1;
   } else {
     p.WD = 8;
     const int per = (D + 7) / 8;
@@ -821,10 +1179,12 @@ size_t workspace_bytes(const Plan& p) {
   size_t b = 0;
   b += up((size_t)p.Kpad * 2 * p.Dp * 4);
   b += up((size_t)p.Kpad * 4);
+  b += 2 * up((size_t)p.Kpad * 8) + up(8);
+  b += up((size_t)p.Kpad * p.Dp * 16) + up((size_t)p.Kpad * 8) + up(8);
   b += up((size_t)p.R * p.Kpad * p.SR * 8);
   b += up((size_t)(p.R > p.Glogz ? p.R : p.Glogz) * 8);
   b += up((size_t)p.chunk * 4);
-  b += up((size_t)p.R * 2 * p.P * p.BN * 8);
+  b += up((size_t)p.R * 4 * p.P * p.BN * 8);
   b += up(((size_t)p.K + 2 * (size_t)p.K * p.D + 1) * 8);
   b += up((size_t)1024 * p.D * 8);
   b += up((size_t)p.D * 8);
@@ -838,12 +1198,15 @@ hipError_t occupancy(const Plan& p, int* occStats, int* occLogz) {
   if (!lookup(p.WC, p.WD, p.DPW, t)) return hipErrorInvalidValue;
   const int nt = 64 * p.WC * p.WD;
   int o1 = 0, o2 = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1, (const void*)t.fused, nt, 0);
+  // the smaller occupancy of the two precision variants sizes the grids
+  int o1b = 0, o2b = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1, (const void*)t.fused[0], nt, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1b, (const void*)t.fused[1], nt, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o2, (const void*)t.logz[0], nt, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o2b, (const void*)t.logz[1], nt, 0);
   if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o2, (const void*)t.logz, nt, 0);
-  if (e != hipSuccess) return e;
-  *occStats = o1;
-  *occLogz = o2;
+  *occStats = o1 < o1b ? o1 : o1b;
+  *occLogz = o2 < o2b ? o2 : o2b;
   return hipSuccess;
 }
 
@@ -859,8 +1222,12 @@ hipError_t launch_precompute(const Plan& p, const Workspace& w, const float* wei
   const size_t total = (size_t)p.Kpad * 2 * p.Dp;
   hipLaunchKernelGGL(k_precompute_w, dim3(grid_for(total, 256)), dim3(256), 0, s, means, vars, w.wop, p.K,
                      p.D, p.Kpad, p.WD, p.DPW);
-  hipLaunchKernelGGL(k_precompute_c, dim3((p.Kpad + 3) / 4), dim3(256), 0, s, weights, means, vars, w.cvec,
-                     p.K, p.D, p.Kpad);
+  hipLaunchKernelGGL(k_precompute_c, dim3((p.Kpad + 3) / 4), dim3(256), 0, s, weights, means, vars, w.cfull,
+                     w.cpeak, p.K, p.D, p.Kpad);
+  hipLaunchKernelGGL(k_precompute_shift, dim3(1), dim3(1024), 0, s, w.cfull, w.cpeak, w.cvec, w.cshift, p.Kpad,
+                     p.D);
+  hipLaunchKernelGGL(k_precompute_w64, dim3((p.Kpad + 3) / 4), dim3(256), 0, s, means, vars, w.w64, w.abmax,
+                     p.K, p.D, p.Kpad, p.Dp);
   return hipGetLastError();
 }
 
@@ -881,6 +1248,13 @@ static EArgs make_args(const Plan& p, const Workspace& w, const float* X, int64_
   a.P = p.P;
   a.R = p.R;
   a.Dp = p.Dp;
+  a.refine = w.refine;
+  a.kappa = (float)((2.0 * p.Dp + 8.0) * 5.9604644775390625e-08);
+  a.w64 = w.w64;
+  a.cfull = w.cfull;
+  a.cshift = w.cshift;
+  a.abmax = w.abmax;
+  a.nrefined = w.nrefined;
   return a;
 }
 
@@ -902,14 +1276,14 @@ hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64
   const int nt = 64 * p.WC * p.WD;
   EArgs a = make_args(p, w, X, ldx);
   if (fused) {
-    const size_t nx = (size_t)p.R * 2 * p.P * p.BN;
+    const size_t nx = (size_t)p.R * 4 * p.P * p.BN;
     hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(nx, 256)), dim3(256), 0, s, w.xbuf, nx);
     a.row0 = 0;
     a.nrows = N;
     a.slot_acc = 0;
     void* args[] = {&a};
     pre(0);
-    hipError_t e = hipLaunchCooperativeKernel(t.fused, dim3(p.G), dim3(nt), args, 0, s);
+    hipError_t e = hipLaunchCooperativeKernel(t.fused[w.refine ? 1 : 0], dim3(p.G), dim3(nt), args, 0, s);
     if (e != hipSuccess) return e;
     post(0);
     return hipGetLastError();
@@ -920,11 +1294,11 @@ hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64
     a.slot_acc = (r0 > 0) ? 1 : 0;
     void* args[] = {&a};
     pre(1);
-    hipError_t e = hipLaunchKernel(t.logz, dim3(p.Glogz), dim3(nt), args, 0, s);
+    hipError_t e = hipLaunchKernel(t.logz[w.refine ? 1 : 0], dim3(p.Glogz), dim3(nt), args, 0, s);
     if (e != hipSuccess) return e;
     post(1);
     pre(0);
-    e = hipLaunchKernel(t.two, dim3(p.G), dim3(nt), args, 0, s);
+    e = hipLaunchKernel(t.two[w.refine ? 1 : 0], dim3(p.G), dim3(nt), args, 0, s);
     if (e != hipSuccess) return e;
     post(0);
   }
@@ -932,12 +1306,13 @@ hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64
 }
 
 hipError_t launch_reduce(const Plan& p, const Workspace& w, double* Nk, double* S1, double* S2, double* ll,
-                         int accumulate, bool fused, int64_t nllslots, hipStream_t s) {
+                         int accumulate, bool fused, int64_t nllslots, int64_t nrows, hipStream_t s) {
   const size_t total = (size_t)p.K * p.SR;
   hipLaunchKernelGGL(k_reduce, dim3(grid_for(total, 256)), dim3(256), 0, s, w.slots, p.R, p.Kpad, p.K, p.D,
                      p.Dp, p.DPW, Nk, S1, S2, accumulate);
   const int n = fused ? p.R : (int)nllslots;
-  hipLaunchKernelGGL(k_reduce_ll, dim3(1), dim3(64), 0, s, w.llslots, n, ll, accumulate, w.flags);
+  hipLaunchKernelGGL(k_reduce_ll, dim3(1), dim3(64), 0, s, w.llslots, n, ll, accumulate, w.flags, w.cshift,
+                     (double)nrows);
   return hipGetLastError();
 }
 
