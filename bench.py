@@ -81,6 +81,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=250_000)
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
+                    help="only copy GIB GiB device-to-device three times (a known-size kernel that scales "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -89,6 +92,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration * (1 << 30)) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": 3}), flush=True)
+        return
     from soft_clustering_amd import GMM, PATH_AUTO, PATH_FUSED, PATH_TWO_SWEEP, PREC_FP32, PREC_REFINED, datagen
 
     wl = datagen.WORKLOADS[args.workload]
