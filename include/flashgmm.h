@@ -147,8 +147,12 @@ gmm_status gmm_fit(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_t ld
  * >= threshold, those ranked by responsibility descending, then index
  * ascending.  Output is CSR: list_offsets [dev] int64[K+1], list_ids [dev]
  * int32[nnz] with row ids ascending within each list.  *nnz [host] receives
- * the total.  If ids_capacity < nnz the ids are not written, *nnz is set and
- * GMM_ERR_CAPACITY is returned.  0 < threshold <= 1, 0 <= max_extra <= 8,
+ * the total.  If ids_capacity < nnz the ids are not written, list_offsets
+ * and *nnz are set and GMM_ERR_CAPACITY is returned.  A row whose logits are
+ * all -inf or NaN gives GMM_ERR_NUMERIC.  Logits within max(16, 1 - log
+ * threshold) nats of a row's largest are evaluated in float64 (under
+ * GMM_PREC_REFINED), so ranks and the threshold test are float64-accurate.
+ * The result is deterministic.  0 < threshold <= 1, 0 <= max_extra <= 8,
  * N < 2^31.  Synchronises the stream. */
 gmm_status gmm_soft_assign(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_t ldx,
                            const float *weights, const float *means, const float *vars /*[dev]*/,

@@ -106,7 +106,10 @@ class GMM:
     def __init__(self, K: int, D: int, device=None):
         if not torch.cuda.is_available():
             raise RuntimeError("the HIP library needs a GPU")
-        self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        dev = torch.device(device) if device is not None else torch.device("cuda")
+        if dev.type != "cuda":
+            raise ValueError("device must be a GPU device")
+        self.device = dev if dev.index is not None else torch.device("cuda", torch.cuda.current_device())
         self.K, self.D = int(K), int(D)
         with torch.cuda.device(self.device):
             h = ctypes.c_void_p()

@@ -175,6 +175,14 @@ gmm_status gmm_create(gmm_ctx** out, int32_t K, int32_t D, void* hip_stream) {
   c->device = dev;
   c->stream = (hipStream_t)hip_stream;
   c->plan = gmm::make_plan(K, D, prop.multiProcessorCount, o1, o2);
+  int oa = 0;
+  e = gmm::assign_occupancy(c->plan, &oa);
+  if (e != hipSuccess || oa < 1) {
+    delete c;
+    return fail(nullptr, e != hipSuccess ? GMM_ERR_HIP : GMM_ERR_UNSUPPORTED, "assignment kernel occupancy: %s",
+                e != hipSuccess ? hipGetErrorString(e) : "does not fit a CU");
+  }
+  c->plan.occAssign = oa;
   c->bytes = gmm::workspace_bytes(c->plan);
   e = hipMalloc(&c->base, c->bytes);
   if (e != hipSuccess) {
@@ -202,6 +210,12 @@ gmm_status gmm_create(gmm_ctx** out, int32_t K, int32_t D, void* hip_stream) {
   c->ws.rows = carve<int64_t>(q, p.K);
   c->ws.flags = carve<int>(q, 4);
   c->ws.colG = 1024;
+  c->ws.asel = carve<int32_t>(q, (size_t)p.assignChunk * 9);
+  c->ws.acounts = carve<unsigned long long>(q, p.Kpad);
+  c->ws.acnt = carve<unsigned>(q, (size_t)p.assignBlocks * p.Kpad);
+  c->ws.atot = carve<unsigned>(q, p.Kpad);
+  c->ws.acursor = carve<int64_t>(q, p.Kpad);
+  c->ws.annz = carve<int64_t>(q, 1);
   e = hipMemsetAsync(c->ws.flags, 0, 16, c->stream);
   if (e == hipSuccess) e = hipMemsetAsync(c->ws.nrefined, 0, 8, c->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
@@ -376,7 +390,42 @@ gmm_status gmm_soft_assign(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx,
   if (ids_capacity < 0) return fail(ctx, GMM_ERR_INVALID_ARG, "ids_capacity must be >= 0");
   if (ids_capacity > 0 && !list_ids) return fail(ctx, GMM_ERR_INVALID_ARG, "list_ids is NULL");
   if (N >= ((int64_t)1 << 31)) return fail(ctx, GMM_ERR_INVALID_ARG, "N must be < 2^31 for int32 ids");
-  return fail(ctx, GMM_ERR_UNSUPPORTED, "soft assignment not built yet");
+  const gmm::Plan& p = ctx->plan;
+  hipStream_t s = ctx->stream;
+  hipError_t e = gmm::launch_precompute(p, ctx->ws, weights, means, vars, s);
+  if (e == hipSuccess) e = gmm::launch_assign_begin(p, ctx->ws, s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "soft assignment set-up");
+  const int64_t CH = p.assignChunk;
+  const bool one = N <= CH;
+  // pass A: select every row and count list sizes
+  for (int64_t r0 = 0; r0 < N; r0 += CH) {
+    const int64_t rows = (N - r0 < CH) ? N - r0 : CH;
+    e = gmm::launch_assign_select(p, ctx->ws, X, r0, rows, ldx, threshold, max_extra, true, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "assignment selection");
+  }
+  e = gmm::launch_assign_offsets(p, ctx->ws, list_offsets, s);
+  int64_t total = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&total, ctx->ws.annz, sizeof total, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "list offsets");
+  *nnz = total;
+  gmm_status chk = gmm_check(ctx);
+  if (chk != GMM_OK) return chk;
+  if (total > ids_capacity)
+    return fail(ctx, GMM_ERR_CAPACITY, "ids_capacity %lld < nnz %lld", (long long)ids_capacity, (long long)total);
+  // pass B: place rows into the lists in row order
+  for (int64_t r0 = 0; r0 < N; r0 += CH) {
+    const int64_t rows = (N - r0 < CH) ? N - r0 : CH;
+    if (!one) {
+      e = gmm::launch_assign_select(p, ctx->ws, X, r0, rows, ldx, threshold, max_extra, false, s);
+      if (e != hipSuccess) return hip_fail(ctx, e, "assignment selection");
+    }
+    e = gmm::launch_assign_scatter(p, ctx->ws, r0, rows, max_extra, list_offsets, list_ids, s);
+    if (e != hipSuccess) return hip_fail(ctx, e, "list scatter");
+  }
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(ctx, e, "soft assignment");
+  return gmm_check(ctx);
 }
 
 gmm_status gmm_refine_stats(gmm_ctx* ctx, int64_t* refined, double* logits) {
@@ -400,10 +449,11 @@ gmm_status gmm_check(gmm_ctx* ctx) {
   int flags[4] = {0, 0, 0, 0};
   e = hipMemcpy(flags, ctx->ws.flags, sizeof flags, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(ctx, e, "flag read");
-  if (flags[0] || flags[1]) {
+  if (flags[0] || flags[1] || flags[2]) {
     hipMemset(ctx->ws.flags, 0, sizeof flags);
     if (flags[1]) return fail(ctx, GMM_ERR_HIP, "fused E-step exchange timed out");
-    return fail(ctx, GMM_ERR_NUMERIC, "non-finite log-likelihood or statistics");
+    if (flags[2]) return fail(ctx, GMM_ERR_HIP, "inverted lists: second selection pass disagreed with the first");
+    return fail(ctx, GMM_ERR_NUMERIC, "non-finite log-likelihood, statistics or logits");
   }
   return GMM_OK;
 }

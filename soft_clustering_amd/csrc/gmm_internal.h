@@ -28,6 +28,10 @@ struct Plan {
   int fusedOK;       // cooperative grid can hold R*P workgroups
   int64_t chunk;     // rows per two-sweep chunk (log Z buffer length)
   size_t ldsStats, ldsLogz;
+  int numCU;
+  int occAssign;       // workgroups per CU of the soft-assignment kernel
+  int64_t assignChunk; // rows per soft-assignment chunk
+  int assignBlocks;    // row blocks per chunk for the ordered list scatter
 };
 
 struct Workspace {
@@ -48,8 +52,15 @@ struct Workspace {
   double* colpart;   // colG * D  column partial sums (init)
   double* colmean;   // D
   int64_t* rows;     // K  init rows
-  int* flags;        // [0] numeric fault, [1] exchange timeout
+  int* flags;        // [0] numeric fault, [1] exchange timeout, [2] list overflow
   int colG;
+  // soft assignment
+  int32_t* asel;                 // assignChunk * 9  per-row selections
+  unsigned long long* acounts;   // Kpad  list sizes
+  unsigned* acnt;                // assignBlocks * Kpad  per-(block, list) counts / ranks
+  unsigned* atot;                // Kpad  per-chunk list totals
+  int64_t* acursor;              // Kpad  next free position of each list
+  int64_t* annz;                 // 1
 };
 
 Plan make_plan(int K, int D, int numCU, int occStats, int occLogz);
@@ -77,14 +88,14 @@ hipError_t launch_mstep(const Plan& p, const Workspace& w, const double* Nk, con
                         float* means, float* vars, hipStream_t s);
 hipError_t launch_init(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx,
                        float var_floor, float* weights, float* means, float* vars, hipStream_t s);
-// Soft assignment: lists into caller CSR arrays. sel is a device scratch of
-// N*(1+max_extra) int32 supplied by the caller of this function.
-hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* X, int64_t N,
-                                int64_t ldx, const float* weights, const float* means,
-                                const float* vars, float threshold, int max_extra, int32_t* sel,
-                                unsigned long long* counts, hipStream_t s);
-hipError_t launch_assign_csr(const Plan& p, int64_t N, int max_extra, const int32_t* sel,
-                             unsigned long long* counts, int64_t* offsets, int32_t* ids,
-                             int64_t capacity, int64_t* d_nnz, int phase, hipStream_t s);
+// Soft assignment (gmm_assign.hip).  Pass A: select + count each chunk, then
+// offsets; pass B: select again (unless one chunk) and scatter.
+hipError_t assign_occupancy(const Plan& p, int* occ);
+hipError_t launch_assign_begin(const Plan& p, const Workspace& w, hipStream_t s);
+hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* X, int64_t row0, int64_t rows,
+                                int64_t ldx, float threshold, int max_extra, bool count, hipStream_t s);
+hipError_t launch_assign_offsets(const Plan& p, const Workspace& w, int64_t* offsets, hipStream_t s);
+hipError_t launch_assign_scatter(const Plan& p, const Workspace& w, int64_t row0, int64_t rows, int max_extra,
+                                 const int64_t* offsets, int32_t* ids, hipStream_t s);
 
 }  // namespace gmm

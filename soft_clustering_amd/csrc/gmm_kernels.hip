@@ -26,395 +26,12 @@
 //    launch guarantees they are co-resident), so each logit is computed once.
 //  * X tiles are staged in LDS as [x^2_lo | x_lo | x^2_hi | x_hi] per row so
 //    one ds_read_b128 gives a lane four consecutive MFMA k-steps.
-#include "gmm_internal.h"
+#include "gmm_device.h"
 
 #include <math.h>
 #include <stdlib.h>
 
 namespace gmm {
-
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-static constexpr float kNegInf = -__builtin_huge_valf();
-static constexpr float kPosInf = __builtin_huge_valf();
-static constexpr double kLog2Pi = 1.8378770664093454835606594728112;
-
-__device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-// Butterfly over the 16 lanes of a DPP row: mirror, half-mirror, xor 2, xor 1.
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp<0x140>(v));
-  v = fmaxf(v, dpp<0x141>(v));
-  v = fmaxf(v, dpp<0x4E>(v));
-  v = fmaxf(v, dpp<0xB1>(v));
-  return v;
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp<0x140>(v);
-  v += dpp<0x141>(v);
-  v += dpp<0x4E>(v);
-  v += dpp<0xB1>(v);
-  return v;
-}
-
-// log(exp(a) + exp(b)) merge of two (max, sum) pairs; -inf safe.
-__device__ __forceinline__ void lse_merge(float& M, float& S, float m2, float s2) {
-  float mn = fmaxf(M, m2);
-  float ms = (mn == kNegInf) ? 0.f : mn;
-  S = S * __expf(M - ms) + s2 * __expf(m2 - ms);
-  M = mn;
-}
-__device__ __forceinline__ float lse_of(float M, float S) {
-  return (S > 0.f) ? ((M == kNegInf ? 0.f : M) + __logf(S)) : kNegInf;
-}
-
-struct EArgs {
-  const float* X;
-  int64_t ldx;
-  int64_t row0;   // first row of this launch (two-sweep chunk)
-  int64_t nrows;  // rows of this launch
-  const float* wop;
-  const float* cvec;
-  float* logz;    // two-sweep: log Z per row of the chunk
-  double* slots;
-  double* llslots;
-  unsigned long long* xbuf;
-  int* flags;
-  int K, D, Kpad, P, R, Dp;
-  int slot_acc;   // 1: add into slots / llslots
-  // float64 refinement of the logits that matter
-  int refine;
-  float kappa;           // fp32 logit error bound factor ((2 Dp + 8) 2^-24)
-  const double2* w64;    // Kpad x Dp  (a, b) in float64
-  const double* cfull;   // Kpad  float64 component constants
-  const double* cshift;  // global logit offset C
-  const float2* abmax;   // Kpad  (max_d |a_kd|, max_d |b_kd|)
-  unsigned long long* nrefined;  // count of refined logits (statistics only)
-};
-
-// ---------------------------------------------------------------------------
-// Shared device pieces, parameterised by the workgroup shape.
-template <int WC, int WD, int DPW, int BN>
-struct Shape {
-  static constexpr int NT = kWave * WC * WD;
-  static constexpr int NPB = BN / 16;         // 16-row MFMA blocks per tile
-  static constexpr int NFB = DPW / 8;         // 16-wide feature blocks per wave (2*DPW/16)
-  static constexpr int SS = 2 * DPW + 4;      // LDS floats per wave segment of a row
-  static constexpr int RS = WD * SS;          // LDS floats per row
-  static constexpr int TILE = BN * RS;        // LDS floats per tile buffer
-  // Two workgroups per CU for 4-wave shapes (their barrier, exchange and
-  // refinement phases then overlap the other workgroup's MFMA work), one
-  // otherwise.  Double-buffer the X tile only for one-per-CU shapes whose
-  // threads stage few float4s.
-  static constexpr int WGS_PER_CU = (WC * WD == 4) ? 2 : 1;
-  static constexpr int PER_STAGE = (BN * WD * DPW / 4 + NT - 1) / NT;
-  static constexpr int NBUF = (WGS_PER_CU == 1 && PER_STAGE <= 8 && TILE * 8 <= 140 * 1024) ? 2 : 1;
-  static constexpr int HALF = DPW / 2;
-  static constexpr int RED = (WD > 1) ? WD * WC * NPB * 8 * kWave : 1;  // partial-logit exchange
-};
-
-// Stage rows [r0, r0+rows) of X into an LDS tile buffer in segment layout:
-// per row and wave segment [x^2 (first half dims) | x | x^2 (second half) | x].
-// Rows past `rows` and dims past D are zeros.  Split into a global-load half
-// and an LDS-store half so the loads of the next tile can be in flight while
-// the current tile's statistics contraction runs.
-template <class SH, int DPW>
-struct Stage {
-  static constexpr int Dp = DPW * (SH::RS / SH::SS);
-  static constexpr int Q4 = Dp / 4;
-  static constexpr int ITEMS = (SH::TILE / SH::RS) * Q4;  // BN * Dp/4 float4s
-  static constexpr int PER = (ITEMS + SH::NT - 1) / SH::NT;
-  f4 v[PER];
-
-  __device__ __forceinline__ void load(const float* __restrict__ X, int64_t ldx, int64_t r0, int rows, int D) {
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int it = threadIdx.x + k * SH::NT;
-      const int pt = it / Q4;
-      const int d = (it - pt * Q4) << 2;
-      f4 x = {0.f, 0.f, 0.f, 0.f};
-      if (it < ITEMS && pt < rows && d < D) {
-        x = *reinterpret_cast<const f4*>(X + (r0 + pt) * ldx + d);
-        if (d + 3 >= D) {
-          if (d + 1 >= D) x[1] = 0.f;
-          if (d + 2 >= D) x[2] = 0.f;
-          x[3] = 0.f;
-        }
-      }
-      v[k] = x;
-    }
-  }
-  __device__ __forceinline__ void store(float* __restrict__ xt) const {
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int it = threadIdx.x + k * SH::NT;
-      if (it < ITEMS) {
-        const int pt = it / Q4;
-        const int d = (it - pt * Q4) << 2;
-        const int seg = d / DPW;
-        const int e = d - seg * DPW;
-        const int h = e / SH::HALF;
-        const int o = e - h * SH::HALF;
-        float* dst = xt + pt * SH::RS + seg * SH::SS + (2 * h) * SH::HALF + o;
-        *reinterpret_cast<f4*>(dst) = v[k] * v[k];
-        *reinterpret_cast<f4*>(dst + SH::HALF) = v[k];
-      }
-    }
-  }
-};
-
-// Partial logits of one wave: its 2 component blocks x NPB point blocks over
-// its dim segment.  acc must hold the starting value (c or 0).
-template <class SH, int DPW>
-__device__ __forceinline__ void logit_tile(const float* __restrict__ xt, const float* __restrict__ w0,
-                                           const float* __restrict__ w1, f4 (&acc)[SH::NPB][2],
-                                           int lane, int wd) {
-  const int g = lane >> 4, r16 = lane & 15;
-  const float* arow = xt + r16 * SH::RS + wd * SH::SS + g * SH::HALF;
-  constexpr int S4 = DPW / 8;
-  // W operands (from L2) are fetched one k-step group ahead of their use.
-  f4 b0 = *reinterpret_cast<const f4*>(w0 + lane * 4);
-  f4 b1 = *reinterpret_cast<const f4*>(w1 + lane * 4);
-#pragma unroll 2
-  for (int s4 = 0; s4 < S4; ++s4) {
-    const int nx = (s4 + 1 < S4) ? s4 + 1 : s4;
-    const f4 b0n = *reinterpret_cast<const f4*>(w0 + (nx * kWave + lane) * 4);
-    const f4 b1n = *reinterpret_cast<const f4*>(w1 + (nx * kWave + lane) * 4);
-    f4 a[SH::NPB];
-#pragma unroll
-    for (int pb = 0; pb < SH::NPB; ++pb)
-      a[pb] = *reinterpret_cast<const f4*>(arow + pb * 16 * SH::RS + s4 * 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int pb = 0; pb < SH::NPB; ++pb) {
-        acc[pb][0] = mfma(a[pb][i], b0[i], acc[pb][0]);
-        acc[pb][1] = mfma(a[pb][i], b1[i], acc[pb][1]);
-      }
-    }
-    b0 = b0n;
-    b1 = b1n;
-  }
-}
-
-// With WD > 1 the WD waves of a component group hold partial logits over
-// their dim segments; sum them in a fixed order through LDS so every wave of
-// the group ends with bit-identical full logits.
-template <class SH, int WC, int WD>
-__device__ __forceinline__ void reduce_partial_logits(float* __restrict__ red, f4 (&acc)[SH::NPB][2],
-                                                      int lane, int wc, int wd) {
-  if constexpr (WD > 1) {
-    constexpr int PER = SH::NPB * 8;  // floats per lane
-    float* mine = red + ((wd * WC + wc) * PER) * kWave + lane;
-#pragma unroll
-    for (int pb = 0; pb < SH::NPB; ++pb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) mine[((pb * 2 + cb) * 4 + v) * kWave] = acc[pb][cb][v];
-    __syncthreads();
-#pragma unroll
-    for (int pb = 0; pb < SH::NPB; ++pb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float s = 0.f;
-#pragma unroll
-          for (int k = 0; k < WD; ++k) s += red[((k * WC + wc) * PER + (pb * 2 + cb) * 4 + v) * kWave + lane];
-          acc[pb][cb][v] = s;
-        }
-    __syncthreads();
-  }
-}
-
-__device__ __forceinline__ const float* wop_block(const float* wop, int cb16, int WD, int wd, int DPW) {
-  return wop + (size_t)(cb16 * WD + wd) * (DPW / 8) * 256;
-}
-
-// ---------------------------------------------------------------------------
-// Float64 refinement of the logits that can matter.
-//
-// The fp32 expanded quadratic c + sum_d (a x^2 + b x) cancels terms whose
-// magnitudes add up to S = sum_d (|a| x^2 + |b x|) + |c - C|, so its error is
-// bounded by E = (2 Dp + 8) 2^-24 S (Dp k-step roundings of partial sums that
-// never exceed S, plus the roundings of x^2, a, b and c).  For data spread
-// over many cluster widths that is 1e-3..1e-2 nats, too much for overlapping
-// components.  Every logit with L + E >= (a lower bound of the row's largest
-// logit) - kDelta is recomputed from float64 a, b, c and exact float64 x^2;
-// all others have responsibility < e^-kDelta relative to the row maximum, so
-// their fp32 error is immaterial.  For clustered data a row has a handful of
-// such logits, so the float64 work is a few percent of the MFMA work.
-constexpr float kDelta = 16.f;
-constexpr int kRefineCap = 256;  // list entries per component group and batch
-
-// Bound on the fp32 error of one logit: kappa (max|a_k| ||x||^2 + max|b_k| ||x||_1 + |c_k - C|).
-__device__ __forceinline__ float err_bound(float kappa, float al, float be, float cv, float2 nn) {
-  return kappa * (al * nn.x + be * nn.y + cv);
-}
-
-// Per-lane error-bound coefficients of this wave's two component blocks:
-// co = (max|a|, max|b|, |c - C|) for the lane's component in block 0, then 1.
-__device__ __forceinline__ void lane_coefs(const EArgs& a, int compbase, int r16, float (&co)[6]) {
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int k = compbase + cb * 16 + r16;
-    const float2 ab = a.abmax[k];
-    const float c = a.cvec[k];
-    co[3 * cb + 0] = ab.x;
-    co[3 * cb + 1] = ab.y;
-    co[3 * cb + 2] = (c == kNegInf) ? 0.f : fabsf(c);
-  }
-}
-
-// ||x||^2 and ||x||_1 of each staged row into nrm[pt] (slightly rounded up).
-template <class SH, int DPW>
-__device__ __forceinline__ void row_norms2(const float* __restrict__ xt, float2* __restrict__ nrm, int Dp) {
-  constexpr int BN = SH::TILE / SH::RS;
-  constexpr int TPR = SH::NT / BN;  // threads per row (power of two)
-  const int pt = threadIdx.x / TPR, sub = threadIdx.x % TPR;
-  float n2 = 0.f, n1 = 0.f;
-  if (pt < BN) {
-    const float* xrow = xt + pt * SH::RS;
-    for (int d = sub; d < Dp; d += TPR) {
-      const int seg = d / DPW;
-      const int ee = d - seg * DPW;
-      const int h = ee / SH::HALF;
-      const int o = ee - h * SH::HALF;
-      n2 += xrow[seg * SH::SS + 2 * h * SH::HALF + o];
-      n1 += fabsf(xrow[seg * SH::SS + (2 * h + 1) * SH::HALF + o]);
-    }
-  }
-#pragma unroll
-  for (int o = TPR / 2; o > 0; o >>= 1) {
-    n2 += __shfl_xor(n2, o);
-    n1 += __shfl_xor(n1, o);
-  }
-  if (pt < BN && sub == 0) nrm[pt] = make_float2(n2 * (1.f + 1e-6f), n1 * (1.f + 1e-6f));
-}
-
-// thr[pt]: the row's selection threshold (error-bound slack and kDelta
-// included): a logit L is recomputed in float64 when L >= thr[pt].
-template <class SH, int WD, int DPW>
-__device__ __forceinline__ void refine_tile(f4 (&acc)[SH::NPB][2], const float* __restrict__ thr,
-                                            const float2* __restrict__ nrm, const float (&co)[6],
-                                            const float* __restrict__ xt, int rows, const EArgs& a, double C,
-                                            int compbase, float* __restrict__ rlist,
-                                            unsigned short* __restrict__ elist, int lane, int wd) {
-  constexpr int NREG = SH::NPB * 8;
-  constexpr int DPT = DPW * WD / 16;           // dims per lane (16 lanes per logit)
-  constexpr int DCH = DPT < 4 ? DPT : 4;       // dims with loads in flight together
-  const int g = lane >> 4, r16 = lane & 15;
-  const unsigned long long below = (1ull << lane) - 1ull;
-  // 1. one selection bit per register
-  unsigned sel = 0;
-  const bool cok0 = compbase + r16 < a.K, cok1 = compbase + 16 + r16 < a.K;
-#pragma unroll
-  for (int pb = 0; pb < SH::NPB; ++pb) {
-    const f4 t4 = *reinterpret_cast<const f4*>(thr + pb * 16 + 4 * g);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int pt = pb * 16 + 4 * g + v;
-      const bool rok = pt < rows;
-      const float2 nn = nrm[pt];
-      const float L0 = acc[pb][0][v], L1 = acc[pb][1][v];
-      const float E0 = err_bound(a.kappa, co[0], co[1], co[2], nn);
-      const float E1 = err_bound(a.kappa, co[3], co[4], co[5], nn);
-      const bool b0 = rok && cok0 && (L0 != kNegInf) && (L0 + E0 >= t4[v]);
-      const bool b1 = rok && cok1 && (L1 != kNegInf) && (L1 + E1 >= t4[v]);
-      sel |= (b0 ? 1u : 0u) << (pb * 8 + v);
-      sel |= (b1 ? 1u : 0u) << (pb * 8 + 4 + v);
-    }
-  }
-  if (wd == 0) {
-    int tot = __popc(sel);
-    for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
-    if (lane == 0 && tot > 0) atomicAdd(a.nrefined, (unsigned long long)tot);
-  }
-  int rstart = 0;
-  while (rstart < NREG) {
-    // 2. list the selected logits of registers [rstart, rend)
-    int count = 0, rend = NREG;
-#pragma unroll
-    for (int r = 0; r < NREG; ++r) {
-      if (r >= rstart && r < rend) {
-        const bool b = (sel >> r) & 1u;
-        const unsigned long long m = __ballot(b);
-        const int n = __popcll(m);
-        if (count + n > kRefineCap) {
-          rend = r;
-        } else {
-          if (b && wd == 0) elist[count + __popcll(m & below)] = (unsigned short)((r << 6) | lane);
-          count += n;
-        }
-      }
-    }
-    if (count == 0) break;  // uniform: nothing (more) selected
-    if constexpr (WD > 1) __syncthreads();
-    else { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); __builtin_amdgcn_wave_barrier(); }
-    // 3. float64 logits: 16 lanes per entry, 4 entries per pass; the WD
-    //    dim-segment waves of a component group share the passes.
-    for (int base = wd * 4; base < count; base += 4 * WD) {
-      const int e = base + g;
-      const bool live = e < count;
-      const int code = live ? (int)elist[e] : 0;
-      const int r = code >> 6, ln = code & 63;
-      const int pt = (r >> 3) * 16 + 4 * (ln >> 4) + (r & 3);
-      const int comp = compbase + ((r >> 2) & 1) * 16 + (ln & 15);
-      const float* xrow = xt + pt * SH::RS;
-      const double2* wr = a.w64 + (size_t)comp * a.Dp;
-      double t = 0.0;
-      if (live) {
-#pragma unroll
-        for (int j0 = 0; j0 < DPT; j0 += DCH) {
-          double2 ab[DCH];
-          float xv[DCH];
-#pragma unroll
-          for (int j = 0; j < DCH; ++j) {
-            const int d = r16 + 16 * (j0 + j);  // < Dp: padded dims have a = b = 0
-            const int seg = d / DPW;
-            const int ee = d - seg * DPW;
-            const int h = ee / SH::HALF;
-            ab[j] = wr[d];
-            xv[j] = xrow[seg * SH::SS + (2 * h + 1) * SH::HALF + (ee - h * SH::HALF)];
-          }
-#pragma unroll
-          for (int j = 0; j < DCH; ++j) {
-            const double x = (double)xv[j];
-            t = fma(ab[j].x, x * x, fma(ab[j].y, x, t));
-          }
-        }
-      }
-      t += __shfl_xor(t, 8);
-      t += __shfl_xor(t, 4);
-      t += __shfl_xor(t, 2);
-      t += __shfl_xor(t, 1);
-      if (live && r16 == 0) rlist[e] = (float)((a.cfull[comp] - C) + t);
-    }
-    if constexpr (WD > 1) __syncthreads();
-    else { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); __builtin_amdgcn_wave_barrier(); }
-    // 4. owners take their refined logits back
-    int c2 = 0;
-#pragma unroll
-    for (int r = 0; r < NREG; ++r) {
-      if (r >= rstart && r < rend) {
-        const bool b = (sel >> r) & 1u;
-        const unsigned long long m = __ballot(b);
-        if (b) acc[r >> 3][(r >> 2) & 1][r & 3] = rlist[c2 + __popcll(m & below)];
-        c2 += __popcll(m);
-      }
-    }
-    if constexpr (WD > 1) __syncthreads();
-    else { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); __builtin_amdgcn_wave_barrier(); }
-    rstart = rend;
-  }
-}
 
 // Row group / member of a workgroup.  Members of one row group sit on one XCD
 // when the grid allows (consecutive workgroup ids go round-robin over the 8
@@ -1165,6 +782,10 @@ Plan make_plan(int K, int D, int numCU, int occStats, int occLogz) {
   p.G = p.R * p.P;
   p.Glogz = numCU * (occLogz > 0 ? occLogz : 1);
   p.chunk = (int64_t)1 << 21;
+  p.numCU = numCU;
+  p.occAssign = 1;
+  p.assignChunk = (int64_t)1 << 19;
+  p.assignBlocks = 256;
   return p;
 }
 
@@ -1190,6 +811,12 @@ size_t workspace_bytes(const Plan& p) {
   b += up((size_t)p.D * 8);
   b += up((size_t)p.K * 8);
   b += up(16);
+  b += up((size_t)p.assignChunk * 9 * 4);
+  b += up((size_t)p.Kpad * 8);
+  b += up((size_t)p.assignBlocks * p.Kpad * 4);
+  b += up((size_t)p.Kpad * 4);
+  b += up((size_t)p.Kpad * 8);
+  b += up(8);
   return b;
 }
 

@@ -1,0 +1,209 @@
+"""Soft assignment (argmax + up to m extras with r >= threshold) and its CSR
+inverted lists, HIP path against the float64 oracle through the C ABI.
+
+Both sides use the same float32 parameters (trained on the GPU for a few EM
+iterations from the oracle's init, so components overlap realistically).
+Rows are compared as sets of components; they must match exactly except rows
+the oracle flags as boundary rows (some r within 1e-5 of the threshold, an
+argmax tie within 1e-5, or a tie at the cut of the m extras)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.gmm_oracle as O
+from soft_clustering_amd import GMM, GMMError, datagen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+# name: (law, N, D, K, ldx, threshold, max_extra, em_iters)
+CASES = {
+    "tiny": ("tiny", 4_003, 8, 16, None, 0.1, 3, 3),
+    "odd_d5_k7": ("tiny", 1_003, 5, 7, 8, 0.05, 2, 2),
+    "mid_prefix": ("mid", 5_001, 128, 1024, None, 0.1, 3, 2),
+    "ivf_k16384": ("ivf", 20_011, 128, 16_384, None, 0.1, 3, 2),
+    "d200_k100": ("mid", 2_005, 200, 100, None, 0.1, 3, 2),
+    "embed_d768_m8": ("embed", 2_003, 768, 512, None, 0.01, 8, 1),
+    "argmax_only_thr1": ("tiny", 3_001, 8, 16, None, 1.0, 3, 3),
+    "argmax_only_m0": ("tiny", 3_001, 8, 16, None, 0.1, 0, 3),
+    "low_thr_m8": ("tiny", 3_001, 16, 40, None, 1e-3, 8, 2),
+}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(Xc, ldx):
+    N, D = Xc.shape
+    if ldx is None:
+        return Xc.to(DEV)
+    buf = torch.full((N, ldx), float("nan"), dtype=torch.float32)
+    buf[:, :D] = Xc
+    return buf.to(DEV)[:, :D]
+
+
+def trained_params(g, Xg, Xn, K, floor, iters):
+    w, mu, var = (torch.as_tensor(a.astype(np.float32)).to(DEV)
+                  for a in O.init(Xn, datagen.init_rows(Xn.shape[0], K, seed=1), floor))
+    if iters:
+        g.fit(Xg, w, mu, var, iters, floor)
+    torch.cuda.synchronize()
+    return w, mu, var
+
+
+def csr_rows(offsets, ids, N, width):
+    """Per-row sorted component ids as an [N, width] array padded with -1,
+    from CSR; also checks the CSR's own structure."""
+    off = offsets.cpu().numpy()
+    ids = ids.cpu().numpy().astype(np.int64)
+    K = off.shape[0] - 1
+    assert off[0] == 0 and np.all(np.diff(off) >= 0) and off[-1] == ids.shape[0]
+    counts = np.diff(off)
+    comps = np.repeat(np.arange(K), counts)
+    # ids strictly ascending within each list
+    if ids.shape[0] > 1:
+        same = comps[1:] == comps[:-1]
+        assert np.all(ids[1:][same] > ids[:-1][same]), "ids not ascending within a list"
+    assert ids.min(initial=0) >= 0 and ids.max(initial=0) < N
+    per_row = np.bincount(ids, minlength=N)
+    assert per_row.min() >= 1 and per_row.max() <= width, "every row appears 1..1+m times"
+    order = np.lexsort((comps, ids))
+    r, c = ids[order], comps[order]
+    start = np.searchsorted(r, np.arange(N))
+    out = np.full((N, width), -1, dtype=np.int64)
+    pos = np.arange(r.shape[0]) - start[r]
+    out[r, pos] = c
+    return out
+
+
+def oracle_rows(lists, width):
+    out = np.full((len(lists), width), -1, dtype=np.int64)
+    for n, lst in enumerate(lists):
+        s = np.sort(lst)
+        out[n, : s.shape[0]] = s
+    return out
+
+
+def compare(gpu_rows, lists, boundary, what):
+    ref = oracle_rows(lists, gpu_rows.shape[1])
+    diff = np.any(gpu_rows != ref, axis=1)
+    bad = np.nonzero(diff & ~boundary)[0]
+    log(f"{what}: rows {gpu_rows.shape[0]}, differing {int(diff.sum())}, boundary {int(boundary.sum())}")
+    assert bad.shape[0] == 0, (f"{what}: {bad.shape[0]} non-boundary rows differ, e.g. row {bad[0]}: "
+                               f"gpu {gpu_rows[bad[0]]} oracle {ref[bad[0]]}")
+    return int(diff.sum())
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_soft_assign_parity(name):
+    law, N, D, K, ldx, thr, m, iters = CASES[name]
+    log(f"soft_assign parity {name}: N={N} D={D} K={K} thr={thr} m={m}")
+    mix = datagen.mixture(law, D, K, seed=0)
+    Xc = datagen.sample(mix, N, seed=0)
+    Xn = Xc.numpy()
+    Xg = to_dev(Xc, ldx)
+    floor = 1.0 / 12.0 if law == "ivf" else (1e-5 if law == "embed" else 1e-6)
+    g = GMM(K, D, DEV)
+    w, mu, var = trained_params(g, Xg, Xn, K, floor, iters)
+    offsets, ids = g.soft_assign(Xg, w, mu, var, thr, m)
+    torch.cuda.synchronize()
+    wn, mun, varn = (a.cpu().numpy() for a in (w, mu, var))
+    method = "direct" if N * D * K <= 3e7 else "gemm"
+    _, _, lists, boundary = O.soft_assign(Xn, wn, mun, varn, thr, m, method=method, chunk_rows=2048)
+    gpu = csr_rows(offsets, ids, N, 1 + m)
+    nd = compare(gpu, lists, boundary, name)
+    if nd == 0:
+        ref_off, ref_ids, _, _ = O.soft_assign(Xn, wn, mun, varn, thr, m, method=method, chunk_rows=2048)
+        assert np.array_equal(offsets.cpu().numpy(), ref_off)
+        assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    if thr >= 1.0 or m == 0:
+        assert ids.shape[0] == N  # argmax only
+
+
+def test_soft_assign_chunks_compose():
+    """Rows past the first 2^19-row chunk go through the second selection
+    pass and the list cursors: the lists of X equal the lists of its two
+    halves, the second's row ids shifted."""
+    N1, N2, D, K = (1 << 19), 3_001, 16, 64
+    log(f"soft_assign chunking: N={N1 + N2} D={D} K={K}")
+    mix = datagen.mixture("tiny", D, K, seed=3)
+    X = torch.empty(N1 + N2, D, dtype=torch.float32, device=DEV)
+    datagen.sample_into(X, mix, 0, seed=3)
+    g = GMM(K, D, DEV)
+    Xn_small = X[:20_000].cpu().numpy()
+    w, mu, var = (torch.as_tensor(a.astype(np.float32)).to(DEV)
+                  for a in O.init(Xn_small, datagen.init_rows(20_000, K, seed=1), 1e-6))
+    g.fit(X, w, mu, var, 2, 1e-6)
+    off, ids = g.soft_assign(X, w, mu, var, 0.1, 3)
+    offa, idsa = g.soft_assign(X[:N1], w, mu, var, 0.1, 3)
+    offb, idsb = g.soft_assign(X[N1:], w, mu, var, 0.1, 3)
+    off, ids, offa, idsa, offb, idsb = (t.cpu().numpy() for t in (off, ids, offa, idsa, offb, idsb))
+    assert np.array_equal(off, offa + offb)
+    for k in range(K):
+        want = np.concatenate((idsa[offa[k]:offa[k + 1]], idsb[offb[k]:offb[k + 1]] + N1))
+        assert np.array_equal(ids[off[k]:off[k + 1]], want), f"list {k}"
+
+
+def test_soft_assign_deterministic_and_capacity():
+    law, N, D, K = "tiny", 4_003, 8, 16
+    mix = datagen.mixture(law, D, K, seed=0)
+    Xc = datagen.sample(mix, N, seed=0)
+    Xg = Xc.to(DEV)
+    g = GMM(K, D, DEV)
+    w, mu, var = trained_params(g, Xg, Xc.numpy(), K, 1e-6, 2)
+    o1, i1 = g.soft_assign(Xg, w, mu, var, 0.05, 3)
+    o2, i2 = g.soft_assign(Xg, w, mu, var, 0.05, 3)
+    assert torch.equal(o1, o2) and torch.equal(i1, i2)
+    nnz = i1.shape[0]
+    with pytest.raises(GMMError) as ei:
+        g.soft_assign(Xg, w, mu, var, 0.05, 3, ids_capacity=nnz - 1)
+    assert ei.value.status == 6 and f"nnz={nnz}" in str(ei.value)
+    o3, i3 = g.soft_assign(Xg, w, mu, var, 0.05, 3, ids_capacity=nnz)
+    assert torch.equal(o1, o3) and torch.equal(i1, i3)
+
+
+def test_soft_assign_rejects_bad_arguments():
+    g = GMM(16, 8, DEV)
+    X = torch.zeros(100, 8, device=DEV)
+    w = torch.full((16,), 1 / 16, device=DEV)
+    mu = torch.zeros(16, 8, device=DEV)
+    var = torch.ones(16, 8, device=DEV)
+    for thr, m in ((0.0, 3), (1.5, 3), (0.1, -1), (0.1, 9)):
+        with pytest.raises(GMMError) as ei:
+            g.soft_assign(X, w, mu, var, thr, m)
+        assert ei.value.status == 1
+
+
+def test_soft_assign_ivf_full_size():
+    """The IVF workload at its real size: K=16384 trained on a 1e6-row sample
+    (3 EM iterations here), then 1e7 base rows assigned.  CSR structure is
+    checked on every row; a random sample of 1500 rows is checked against the
+    oracle row by row."""
+    wl = datagen.WORKLOADS["ivf"]
+    K, D, N = wl.K, wl.D, wl.N
+    ntrain = wl.extra["train_rows"]
+    thr, m = wl.extra["threshold"], wl.extra["max_extra"]
+    log(f"soft_assign ivf full size: N={N} train={ntrain} K={K}")
+    mix = datagen.mixture(wl.law, D, K, seed=wl.seed)
+    Xt = torch.empty(ntrain, D, dtype=torch.float32, device=DEV)
+    datagen.sample_into(Xt, mix, 0, seed=wl.seed, stream=1)
+    g = GMM(K, D, DEV)
+    w, mu, var = g.init(Xt, datagen.init_rows(ntrain, K, seed=wl.init_seed), wl.var_floor)
+    g.fit(Xt, w, mu, var, 3, wl.var_floor)
+    del Xt
+    X = torch.empty(N, D, dtype=torch.float32, device=DEV)
+    datagen.sample_into(X, mix, 0, seed=wl.seed)
+    offsets, ids = g.soft_assign(X, w, mu, var, thr, m)
+    torch.cuda.synchronize()
+    gpu = csr_rows(offsets, ids, N, 1 + m)
+    log(f"nnz {ids.shape[0]} ({ids.shape[0] / N:.3f} lists per row)")
+    rng = np.random.default_rng(7)
+    sample = np.sort(rng.choice(N, 1500, replace=False))
+    Xs = X[torch.as_tensor(sample, device=DEV)].cpu().numpy()
+    wn, mun, varn = (a.cpu().numpy() for a in (w, mu, var))
+    _, _, lists, boundary = O.soft_assign(Xs, wn, mun, varn, thr, m, method="gemm", chunk_rows=256)
+    compare(gpu[sample], lists, boundary, "ivf sample")
