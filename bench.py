@@ -29,6 +29,8 @@ WORKLOAD_TEXT = {
     "mid": "mid EM: N=1,000,000, D=128, K=1024, fp32, diagonal covariance, 30 EM iterations",
     "tiny": "tiny EM: N=10,000, D=8, K=16, fp32, diagonal covariance, 10 EM iterations",
     "embed": "embedding-like EM: N=10,000,000, D=768, K=4096, fp32, diagonal covariance, 20 EM iterations",
+    "ivf": "IVF: EM on a 1,000,000-row sample, D=128, K=16384, integer values 0..255, 10 EM iterations; "
+           "then soft assignment (argmax + up to 3 with r >= 0.1) of 10,000,000 base rows into CSR lists",
 }
 
 
@@ -60,11 +62,12 @@ def cpu_baseline(workload, sample_rows, budget_s):
         if time.perf_counter() - t0 > budget_s or iters >= 3:
             break
     dt = (time.perf_counter() - t0) / iters
-    ms_full = dt * 1e3 * (wl.N / n)
+    n_full = wl.extra.get("train_rows", wl.N)  # EM runs on the training sample for ivf
+    ms_full = dt * 1e3 * (n_full / n)
     return {"value": ms_full, "unit": "ms per EM iteration (extrapolated linearly in N)", "cores": cores,
             "kind": "oracle",
             "sample": f"{iters} EM iteration(s) of the float64 numpy oracle on the first {n} rows of the "
-                      f"{workload} workload ({dt:.2f} s each), scaled by N/{n}",
+                      f"{workload} workload ({dt:.2f} s each), scaled by {n_full}/{n}",
             "gflops": useful_flops(n, wl.K, wl.D) / dt / 1e9,
             "torch_threads": torch.get_num_threads()}
 
@@ -104,14 +107,15 @@ def main():
     from soft_clustering_amd import GMM, PATH_AUTO, PATH_FUSED, PATH_TWO_SWEEP, PREC_FP32, PREC_REFINED, datagen
 
     wl = datagen.WORKLOADS[args.workload]
-    N = args.rows or wl.N
+    ivf = args.workload == "ivf"
+    N = args.rows or (wl.extra["train_rows"] if ivf else wl.N)
     K, D = wl.K, wl.D
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     mix = datagen.mixture(wl.law, D, K, seed=wl.seed)
     t0 = time.perf_counter()
     X = torch.empty(N, D, dtype=torch.float32, device=dev)
-    datagen.sample_into(X, mix, 0, seed=wl.seed)
+    datagen.sample_into(X, mix, 0, seed=wl.seed, stream=1 if ivf else 0)
     torch.cuda.synchronize()
     print(f"# generated {N}x{D} in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
 
@@ -176,6 +180,22 @@ def main():
         line["logz_sweep_avg_ms"] = round(logz_ms / max(logz_n, 1), 3)
     del X
     torch.cuda.empty_cache()
+    if ivf:
+        # soft assignment of the base rows with the trained parameters
+        nb = wl.N
+        Xb = torch.empty(nb, D, dtype=torch.float32, device=dev)
+        datagen.sample_into(Xb, mix, 0, seed=wl.seed)
+        thr, m = wl.extra["threshold"], wl.extra["max_extra"]
+        g.soft_assign(Xb, w, mu, var, thr, m)  # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        offsets, ids = g.soft_assign(Xb, w, mu, var, thr, m)
+        torch.cuda.synchronize()
+        dt_a = time.perf_counter() - t0
+        line["soft_assign"] = {"rows": nb, "ms": round(dt_a * 1e3, 1), "lists_per_row": round(ids.shape[0] / nb, 4),
+                               "logit_tflops_two_sweeps": round(2 * 4.0 * nb * K * D / dt_a / 1e12, 2)}
+        del Xb, offsets, ids
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_rows, args.cpu_budget_s)
     print(json.dumps(line), flush=True)

@@ -11,7 +11,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/flashgmm.h"
+#include "flashgmm.h"
 #include "gmm_internal.h"
 
 struct gmm_ctx {
@@ -125,9 +125,11 @@ gmm_status estep_into(gmm_ctx* c, const float* X, int64_t N, int64_t ldx, const 
   hk.before = hook_before;
   hk.after = hook_after;
   hk.user = c;
-  e = gmm::launch_estep(c->plan, c->ws, X, N, ldx, fused, s, c->prof ? &hk : nullptr);
+  int nslots = 0;
+  e = gmm::launch_estep(c->plan, c->ws, X, N, ldx, fused, s, c->prof ? &hk : nullptr, &nslots);
   if (e != hipSuccess) return hip_fail(c, e, fused ? "fused E-step launch" : "two-sweep E-step launch");
-  e = gmm::launch_reduce(c->plan, c->ws, Nk, S1, S2, ll, accumulate, fused, c->plan.Glogz, N, s);
+  e = gmm::launch_reduce(c->plan, c->ws, Nk, S1, S2, ll, accumulate, nslots, fused ? nslots : c->plan.Glogz, N,
+                         s);
   c->logits_since += (double)N * (double)c->plan.K * (fused ? 1.0 : 2.0);
   if (e != hipSuccess) return hip_fail(c, e, "reduce launch");
   return GMM_OK;
@@ -177,10 +179,9 @@ gmm_status gmm_create(gmm_ctx** out, int32_t K, int32_t D, void* hip_stream) {
   c->plan = gmm::make_plan(K, D, prop.multiProcessorCount, o1, o2);
   int oa = 0;
   e = gmm::assign_occupancy(c->plan, &oa);
-  if (e != hipSuccess || oa < 1) {
+  if (e != hipSuccess) {
     delete c;
-    return fail(nullptr, e != hipSuccess ? GMM_ERR_HIP : GMM_ERR_UNSUPPORTED, "assignment kernel occupancy: %s",
-                e != hipSuccess ? hipGetErrorString(e) : "does not fit a CU");
+    return fail(nullptr, GMM_ERR_HIP, "assignment kernel occupancy: %s", hipGetErrorString(e));
   }
   c->plan.occAssign = oa;
   c->bytes = gmm::workspace_bytes(c->plan);
@@ -391,6 +392,7 @@ gmm_status gmm_soft_assign(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx,
   if (ids_capacity > 0 && !list_ids) return fail(ctx, GMM_ERR_INVALID_ARG, "list_ids is NULL");
   if (N >= ((int64_t)1 << 31)) return fail(ctx, GMM_ERR_INVALID_ARG, "N must be < 2^31 for int32 ids");
   const gmm::Plan& p = ctx->plan;
+  if (p.occAssign < 1) return fail(ctx, GMM_ERR_UNSUPPORTED, "no soft-assignment kernel for this context's shape");
   hipStream_t s = ctx->stream;
   hipError_t e = gmm::launch_precompute(p, ctx->ws, weights, means, vars, s);
   if (e == hipSuccess) e = gmm::launch_assign_begin(p, ctx->ws, s);

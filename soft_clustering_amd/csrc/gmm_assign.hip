@@ -84,8 +84,8 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
   __shared__ float lpart[WC][BN];
   __shared__ float2 nrm[BN];
   __shared__ __attribute__((aligned(16))) float thrw[WC][BN];
-  __shared__ float rlist[WC][kRefineCap];
-  __shared__ unsigned short elist[WC][kRefineCap];
+  __shared__ float rlist[SH::COOP ? WC : WC * WD][kRefineCap];  // refinement lists (per group or wave)
+  __shared__ unsigned short elist[SH::COOP ? WC : WC * WD][kRefineCap];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wc = w % WC, wd = w / WC;
@@ -94,6 +94,7 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
   const double C = *a.cshift;
   const int nt = (int)((a.nrows + BN - 1) / BN);
   const int stride = 1 + s.m;
+  unsigned nsel = 0;  // refined logits of this wave (counted once at the end)
 
   for (int t = blockIdx.x; t < nt; t += gridDim.x) {
     const int64_t trow = (int64_t)t * BN;
@@ -156,8 +157,8 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
           }
         if constexpr (WD > 1) __syncthreads();
         else wave_sync();
-        refine_tile<SH, WD, DPW>(acc, thrw[wc], nrm, co, xt, rows, a, C, compbase, rlist[wc], elist[wc], lane,
-                                 wd);
+        refine_tile<SH, WD, DPW>(acc, thrw[wc], nrm, co, xt, rows, a, C, compbase, rlist[SH::COOP ? wc : w], elist[SH::COOP ? wc : w], lane,
+                                 wd, nsel);
       }
 #pragma unroll
       for (int pb = 0; pb < NPB; ++pb)
@@ -245,6 +246,7 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
     }
     __syncthreads();
   }
+  if constexpr (REFINE) count_refined(a, nsel);
 }
 
 // ---------------------------------------------------------------------------
@@ -362,7 +364,7 @@ static int grid_n(size_t n) {
 
 template <int WC, int WD, int DPW>
 struct AKern {
-  static constexpr int BN = (WD == 1) ? 64 : 16;
+  static constexpr int BN = bn_for(WD, DPW);
   template <bool R>
   static void* assign() { return (void*)&k_assign<WC, WD, DPW, BN, R>; }
 };
@@ -395,7 +397,8 @@ static int assign_wc(const Plan& p) {
 hipError_t assign_occupancy(const Plan& p, int* occ) {
   void* t[2];
   const int wc = assign_wc(p);
-  if (!alookup(wc, p.WD, p.DPW, t)) return hipErrorInvalidValue;
+  *occ = 0;
+  if (!alookup(wc, p.WD, p.DPW, t)) return hipSuccess;  // no assignment kernel for this shape
   int o0 = 0, o1 = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o0, (const void*)t[0], 64 * wc * p.WD, 0);
   if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1, (const void*)t[1], 64 * wc * p.WD, 0);

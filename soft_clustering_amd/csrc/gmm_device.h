@@ -92,9 +92,13 @@ struct Shape {
   // threads stage few float4s.
   static constexpr int WGS_PER_CU = (WC * WD == 4) ? 2 : 1;
   static constexpr int PER_STAGE = (BN * WD * DPW / 4 + NT - 1) / NT;
-  static constexpr int NBUF = (WGS_PER_CU == 1 && PER_STAGE <= 8 && TILE * 8 <= 140 * 1024) ? 2 : 1;
-  static constexpr int HALF = DPW / 2;
   static constexpr int RED = (WD > 1) ? WD * WC * NPB * 8 * kWave : 1;  // partial-logit exchange
+  static constexpr int NBUF =
+      (WGS_PER_CU == 1 && PER_STAGE <= 8 && TILE * 8 + RED * 4 <= 140 * 1024) ? 2 : 1;
+  static constexpr int HALF = DPW / 2;
+  // refinement: the WD waves of a component group share the float64 passes
+  // when the group is the whole workgroup, else each wave refines its copy
+  static constexpr bool COOP = (WD > 1) && (WC == 1);
 };
 
 // Stage rows [r0, r0+rows) of X into an LDS tile buffer in segment layout:
@@ -118,7 +122,8 @@ struct Stage {
       const int d = (it - pt * Q4) << 2;
       f4 x = {0.f, 0.f, 0.f, 0.f};
       if (it < ITEMS && pt < rows && d < D) {
-        x = *reinterpret_cast<const f4*>(X + (r0 + pt) * ldx + d);
+        // streamed once: a non-temporal load leaves the caches to the parameters
+        x = __builtin_nontemporal_load(reinterpret_cast<const f4*>(X + (r0 + pt) * ldx + d));
         if (d + 3 >= D) {
           if (d + 1 >= D) x[1] = 0.f;
           if (d + 2 >= D) x[2] = 0.f;
@@ -148,7 +153,10 @@ struct Stage {
 };
 
 // Partial logits of one wave: its 2 component blocks x NPB point blocks over
-// its dim segment.  acc must hold the starting value (c or 0).
+// its dim segment.  acc must hold the starting value (c or 0).  Per group of
+// four k-steps the A operands (one ds_read_b128 per point block) are consumed
+// point block by point block, so only two are live; the W operands (B, from
+// L2) are fetched one group ahead.
 template <class SH, int DPW>
 __device__ __forceinline__ void logit_tile(const float* __restrict__ xt, const float* __restrict__ w0,
                                            const float* __restrict__ w1, f4 (&acc)[SH::NPB][2],
@@ -156,7 +164,6 @@ __device__ __forceinline__ void logit_tile(const float* __restrict__ xt, const f
   const int g = lane >> 4, r16 = lane & 15;
   const float* arow = xt + r16 * SH::RS + wd * SH::SS + g * SH::HALF;
   constexpr int S4 = DPW / 8;
-  // W operands (from L2) are fetched one k-step group ahead of their use.
   f4 b0 = *reinterpret_cast<const f4*>(w0 + lane * 4);
   f4 b1 = *reinterpret_cast<const f4*>(w1 + lane * 4);
 #pragma unroll 2
@@ -164,16 +171,15 @@ __device__ __forceinline__ void logit_tile(const float* __restrict__ xt, const f
     const int nx = (s4 + 1 < S4) ? s4 + 1 : s4;
     const f4 b0n = *reinterpret_cast<const f4*>(w0 + (nx * kWave + lane) * 4);
     const f4 b1n = *reinterpret_cast<const f4*>(w1 + (nx * kWave + lane) * 4);
-    f4 a[SH::NPB];
+    f4 an = *reinterpret_cast<const f4*>(arow + s4 * 4);
 #pragma unroll
-    for (int pb = 0; pb < SH::NPB; ++pb)
-      a[pb] = *reinterpret_cast<const f4*>(arow + pb * 16 * SH::RS + s4 * 4);
+    for (int pb = 0; pb < SH::NPB; ++pb) {
+      const f4 a = an;
+      if (pb + 1 < SH::NPB) an = *reinterpret_cast<const f4*>(arow + (pb + 1) * 16 * SH::RS + s4 * 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int pb = 0; pb < SH::NPB; ++pb) {
-        acc[pb][0] = mfma(a[pb][i], b0[i], acc[pb][0]);
-        acc[pb][1] = mfma(a[pb][i], b1[i], acc[pb][1]);
+      for (int i = 0; i < 4; ++i) {
+        acc[pb][0] = mfma(a[i], b0[i], acc[pb][0]);
+        acc[pb][1] = mfma(a[i], b1[i], acc[pb][1]);
       }
     }
     b0 = b0n;
@@ -252,21 +258,28 @@ __device__ __forceinline__ void lane_coefs(const EArgs& a, int compbase, int r16
 }
 
 // ||x||^2 and ||x||_1 of each staged row into nrm[pt] (slightly rounded up).
+// A row's segment holds [x^2 lo | x lo | x^2 hi | x hi] (HALF floats each);
+// TPR threads per row read it as float4s and combine with shuffles.
 template <class SH, int DPW>
 __device__ __forceinline__ void row_norms2(const float* __restrict__ xt, float2* __restrict__ nrm, int Dp) {
   constexpr int BN = SH::TILE / SH::RS;
   constexpr int TPR = SH::NT / BN;  // threads per row (power of two)
+  constexpr int WDN = SH::RS / SH::SS;
+  constexpr int H4 = SH::HALF / 4;  // float4s per half
+  constexpr int PER = WDN * 2 * H4; // float4s of x^2 (and of x) per row
   const int pt = threadIdx.x / TPR, sub = threadIdx.x % TPR;
   float n2 = 0.f, n1 = 0.f;
   if (pt < BN) {
     const float* xrow = xt + pt * SH::RS;
-    for (int d = sub; d < Dp; d += TPR) {
-      const int seg = d / DPW;
-      const int ee = d - seg * DPW;
-      const int h = ee / SH::HALF;
-      const int o = ee - h * SH::HALF;
-      n2 += xrow[seg * SH::SS + 2 * h * SH::HALF + o];
-      n1 += fabsf(xrow[seg * SH::SS + (2 * h + 1) * SH::HALF + o]);
+#pragma unroll
+    for (int q = sub; q < PER; q += TPR) {
+      const int seg = q / (2 * H4), hq = q % (2 * H4);
+      const int h = hq / H4, o = (hq % H4) * 4;
+      const float* base = xrow + seg * SH::SS + 2 * h * SH::HALF + o;
+      const f4 sq = *reinterpret_cast<const f4*>(base);
+      const f4 xv = *reinterpret_cast<const f4*>(base + SH::HALF);
+      n2 += (sq[0] + sq[1]) + (sq[2] + sq[3]);
+      n1 += (fabsf(xv[0]) + fabsf(xv[1])) + (fabsf(xv[2]) + fabsf(xv[3]));
     }
   }
 #pragma unroll
@@ -284,12 +297,12 @@ __device__ __forceinline__ void refine_tile(f4 (&acc)[SH::NPB][2], const float* 
                                             const float2* __restrict__ nrm, const float (&co)[6],
                                             const float* __restrict__ xt, int rows, const EArgs& a, double C,
                                             int compbase, float* __restrict__ rlist,
-                                            unsigned short* __restrict__ elist, int lane, int wd) {
+                                            unsigned short* __restrict__ elist, int lane, int wd,
+                                            unsigned& nsel) {
   constexpr int NREG = SH::NPB * 8;
   constexpr int DPT = DPW * WD / 16;           // dims per lane (16 lanes per logit)
   constexpr int DCH = DPT < 4 ? DPT : 4;       // dims with loads in flight together
   const int g = lane >> 4, r16 = lane & 15;
-  const unsigned long long below = (1ull << lane) - 1ull;
   // 1. one selection bit per register
   unsigned sel = 0;
   const bool cok0 = compbase + r16 < a.K, cok1 = compbase + 16 + r16 < a.K;
@@ -309,36 +322,40 @@ __device__ __forceinline__ void refine_tile(f4 (&acc)[SH::NPB][2], const float* 
       sel |= (b0 ? 1u : 0u) << (pb * 8 + v);
       sel |= (b1 ? 1u : 0u) << (pb * 8 + 4 + v);
     }
+    __builtin_amdgcn_sched_barrier(0);  // bounds the LDS loads in flight (registers)
   }
-  if (wd == 0) {
-    int tot = __popc(sel);
-    for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
-    if (lane == 0 && tot > 0) atomicAdd(a.nrefined, (unsigned long long)tot);
-  }
-  int rstart = 0;
-  while (rstart < NREG) {
-    // 2. list the selected logits of registers [rstart, rend)
-    int count = 0, rend = NREG;
+  // 2. lane-major list: lane l's selected registers, in register order, take
+  //    positions [pre, pre + popc(sel)) where pre is the exclusive prefix of
+  //    the per-lane counts, built bit-slice by bit-slice from six ballots.
+  const int c = __popc(sel);
+  int pre = 0, total = 0;
 #pragma unroll
-    for (int r = 0; r < NREG; ++r) {
-      if (r >= rstart && r < rend) {
-        const bool b = (sel >> r) & 1u;
-        const unsigned long long m = __ballot(b);
-        const int n = __popcll(m);
-        if (count + n > kRefineCap) {
-          rend = r;
-        } else {
-          if (b && wd == 0) elist[count + __popcll(m & below)] = (unsigned short)((r << 6) | lane);
-          count += n;
-        }
+  for (int b = 0; b < 6; ++b) {
+    const unsigned long long m = __ballot((c >> b) & 1);
+    // set bits of m in lanes below this one
+    pre += (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u)) << b;
+    total += __popcll(m) << b;
+  }
+  if (total == 0) return;  // uniform over the component group
+  if (wd == 0) nsel += (unsigned)total;
+  for (int b0 = 0; b0 < total; b0 += kRefineCap) {
+    const int count = min(kRefineCap, total - b0);
+    if (!SH::COOP || wd == 0) {
+      // walk the set bits (a lane rarely has more than a few)
+      unsigned bits = sel;
+      int idx = pre - b0;
+      while (bits) {
+        const int r = __ffs(bits) - 1;
+        bits &= bits - 1u;
+        if (idx >= 0 && idx < kRefineCap) elist[idx] = (unsigned short)((r << 6) | lane);
+        ++idx;
       }
     }
-    if (count == 0) break;  // uniform: nothing (more) selected
-    if constexpr (WD > 1) __syncthreads();
+    if constexpr (SH::COOP) __syncthreads();
     else { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); __builtin_amdgcn_wave_barrier(); }
-    // 3. float64 logits: 16 lanes per entry, 4 entries per pass; the WD
-    //    dim-segment waves of a component group share the passes.
-    for (int base = wd * 4; base < count; base += 4 * WD) {
+    // 3. float64 logits: 16 lanes per entry, 4 entries per pass; in COOP
+    //    mode the WD dim-segment waves of the group share the passes.
+    for (int base = SH::COOP ? wd * 4 : 0; base < count; base += SH::COOP ? 4 * WD : 4) {
       const int e = base + g;
       const bool live = e < count;
       const int code = live ? (int)elist[e] : 0;
@@ -347,6 +364,7 @@ __device__ __forceinline__ void refine_tile(f4 (&acc)[SH::NPB][2], const float* 
       const int comp = compbase + ((r >> 2) & 1) * 16 + (ln & 15);
       const float* xrow = xt + pt * SH::RS;
       const double2* wr = a.w64 + (size_t)comp * a.Dp;
+      const double cf = (live && r16 == 0) ? a.cfull[comp] : 0.0;  // issued with the (a, b) loads
       double t = 0.0;
       if (live) {
 #pragma unroll
@@ -373,24 +391,45 @@ __device__ __forceinline__ void refine_tile(f4 (&acc)[SH::NPB][2], const float* 
       t += __shfl_xor(t, 4);
       t += __shfl_xor(t, 2);
       t += __shfl_xor(t, 1);
-      if (live && r16 == 0) rlist[e] = (float)((a.cfull[comp] - C) + t);
+      if (live && r16 == 0) rlist[e] = (float)((cf - C) + t);
     }
-    if constexpr (WD > 1) __syncthreads();
+    if constexpr (SH::COOP) __syncthreads();
     else { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); __builtin_amdgcn_wave_barrier(); }
-    // 4. owners take their refined logits back
-    int c2 = 0;
+    // 4. owners take their refined logits back, in the same order
+    {
+      int idx = pre - b0;
 #pragma unroll
-    for (int r = 0; r < NREG; ++r) {
-      if (r >= rstart && r < rend) {
-        const bool b = (sel >> r) & 1u;
-        const unsigned long long m = __ballot(b);
-        if (b) acc[r >> 3][(r >> 2) & 1][r & 3] = rlist[c2 + __popcll(m & below)];
-        c2 += __popcll(m);
-      }
+      for (int r = 0; r < NREG; ++r)
+        if ((sel >> r) & 1u) {
+          if (idx >= 0 && idx < kRefineCap) acc[r >> 3][(r >> 2) & 1][r & 3] = rlist[idx];
+          ++idx;
+        }
     }
-    if constexpr (WD > 1) __syncthreads();
+    if constexpr (SH::COOP) __syncthreads();
     else { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); __builtin_amdgcn_wave_barrier(); }
-    rstart = rend;
+  }
+}
+
+// Add a wave's refined-logit count to the global counter once per launch
+// (one atomic per wave instead of one per tile keeps the counter off the
+// critical path).
+__device__ __forceinline__ void count_refined(const EArgs& a, unsigned nsel) {
+  if ((threadIdx.x & 63) == 0 && nsel) atomicAdd(a.nrefined, (unsigned long long)nsel);
+}
+
+// Row group / member of a workgroup.  Members of one row group sit on one XCD
+// when the grid allows (consecutive workgroup ids go round-robin over the 8
+// XCDs), so the P re-reads of an X tile and the exchange stay in one L2.
+__device__ __forceinline__ void rg_member(int G, int P, int& rg, int& p) {
+  const int b = blockIdx.x;
+  const int per = G / kNumXCD;
+  if (G % kNumXCD == 0 && per % P == 0) {
+    const int xcd = b % kNumXCD, s = b / kNumXCD;
+    rg = xcd * (per / P) + s / P;
+    p = s % P;
+  } else {
+    rg = b / P;
+    p = b % P;
   }
 }
 

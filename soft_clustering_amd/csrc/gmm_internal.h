@@ -11,6 +11,10 @@ constexpr int kWavesPerWG = 8;     // waves of the E-step workgroups
 constexpr int kCompsPerWave = 32;  // two 16-wide MFMA component blocks
 constexpr int kNumXCD = 8;         // MI355X: 8 accelerator complex dies
 
+// Rows per tile: 64 while a row's features fit one 128-dim wave segment set,
+// 16 for wide rows (their tiles would not fit LDS).
+constexpr int bn_for(int WD, int DPW) { return WD * DPW <= 128 ? 64 : 16; }
+
 // Shape of the E-step kernels, chosen once per context from (K, D).
 //   WC comp groups x WD dim segments = waves per workgroup.
 //   DPW dims per wave segment (multiple of 16); Dp = DPW * WD >= D.
@@ -78,11 +82,13 @@ struct LaunchHooks {
   void (*after)(void* user, int which, hipStream_t s) = nullptr;
   void* user = nullptr;
 };
+// *nslots receives the number of statistics slots (row groups) written.
 hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx,
-                        bool fused, hipStream_t s, const LaunchHooks* hooks = nullptr);
+                        bool fused, hipStream_t s, const LaunchHooks* hooks, int* nslots);
 hipError_t launch_reduce(const Plan& p, const Workspace& w, double* Nk, double* S1, double* S2,
-                         double* ll, int accumulate, bool fused, int64_t nllslots, int64_t nrows,
+                         double* ll, int accumulate, int nslots, int nllslots, int64_t nrows,
                          hipStream_t s);
+
 hipError_t launch_mstep(const Plan& p, const Workspace& w, const double* Nk, const double* S1,
                         const double* S2, double n_total, float var_floor, float* weights,
                         float* means, float* vars, hipStream_t s);

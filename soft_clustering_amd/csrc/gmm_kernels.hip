@@ -33,22 +33,6 @@
 
 namespace gmm {
 
-// Row group / member of a workgroup.  Members of one row group sit on one XCD
-// when the grid allows (consecutive workgroup ids go round-robin over the 8
-// XCDs), so the P re-reads of an X tile and the exchange stay in one L2.
-__device__ __forceinline__ void rg_member(int G, int P, int& rg, int& p) {
-  const int b = blockIdx.x;
-  const int per = G / kNumXCD;
-  if (G % kNumXCD == 0 && per % P == 0) {
-    const int xcd = b % kNumXCD, s = b / kNumXCD;
-    rg = xcd * (per / P) + s / P;
-    p = s % P;
-  } else {
-    rg = b / P;
-    p = b % P;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Cross-workgroup exchange of one per-row value among the P workgroups of a
 // row group (fused path).  Each workgroup publishes vin[pt] as a 64-bit word
@@ -115,7 +99,7 @@ template <int WC, int WD, int DPW, int BN, bool FUSED, bool REFINE>
 __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats(EArgs a) {
   using SH = Shape<WC, WD, DPW, BN>;
   constexpr int NPB = SH::NPB, NFB = SH::NFB;
-  constexpr int FLUSH = (BN >= 64) ? 16 : 64;  // tiles between fp64 flushes (~1024 rows)
+  constexpr int FLUSH = (BN >= 64) ? 32 : 128;  // tiles between fp64 flushes (2048 rows)
   constexpr int QP = (SH::NT / BN) > 0 ? (SH::NT / BN) : 1;
 
   __shared__ __attribute__((aligned(16))) float xt[SH::NBUF][SH::TILE];
@@ -127,8 +111,8 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   __shared__ float2 nrm[BN];
   __shared__ __attribute__((aligned(16))) float thrs[BN];
   __shared__ float vtmp[BN];
-  __shared__ float rlist[WC][kRefineCap];
-  __shared__ unsigned short elist[WC][kRefineCap];
+  __shared__ float rlist[SH::COOP ? WC : WC * WD][kRefineCap];  // refinement lists (per group or wave)
+  __shared__ unsigned short elist[SH::COOP ? WC : WC * WD][kRefineCap];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wc = w % WC, wd = w / WC;
@@ -145,6 +129,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   const double C = *a.cshift;
   float co[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if constexpr (REFINE) lane_coefs(a, compbase, r16, co);
+  unsigned nsel = 0;  // refined logits of this wave (counted once at the end)
 
   const int nt = (int)((a.nrows + BN - 1) / BN);
   f4 sacc[2][NFB];
@@ -204,7 +189,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
     const int64_t trow = (int64_t)t * BN;
     const int rows = (int)min((int64_t)BN, a.nrows - trow);
     if constexpr (SH::NBUF == 1) {
-      if (j > 0) {
+      if (j > 0) {  // single buffer: the previous tile is done (end-of-tile barrier)
         stg.load(a.X, a.ldx, a.row0 + trow, rows, a.D);
         stg.store(xt[0]);
         __syncthreads();
@@ -238,6 +223,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
                                      acc[pb][1][v] - err_bound(a.kappa, co[3], co[4], co[5], nn));
               const float m = row16_max(lb);
               if (r16 == 0) lpart[wc][pb * 16 + 4 * g + v] = m;
+              if (v == 3) __builtin_amdgcn_sched_barrier(0);
             }
         }
         __syncthreads();
@@ -254,7 +240,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
         if (tid < BN) thrs[tid] = ((tid < rows) ? a.logz[trow + tid] : kPosInf) - kDelta;
       }
       __syncthreads();
-      refine_tile<SH, WD, DPW>(acc, thrs, nrm, co, xt[cur], rows, a, C, compbase, rlist[wc], elist[wc], lane, wd);
+      refine_tile<SH, WD, DPW>(acc, thrs, nrm, co, xt[cur], rows, a, C, compbase, rlist[SH::COOP ? wc : w], elist[SH::COOP ? wc : w], lane, wd, nsel);
     }
 
     // ---- per-row log Z
@@ -289,7 +275,8 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
     }
     __syncthreads();
 
-    // ---- prefetch the next tile while the statistics contraction runs
+    // ---- prefetch the next tile (double-buffered shapes) while the
+    //      statistics contraction runs
     const int tn = t + a.R;
     const bool has_next = (SH::NBUF == 2) && (tn < nt);
     if (has_next) stg.load(a.X, a.ldx, a.row0 + (int64_t)tn * BN, (int)min((int64_t)BN, a.nrows - (int64_t)tn * BN), a.D);
@@ -297,30 +284,38 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
     // accumulators straight into the A operand; B operands (x^2 | x from LDS)
     // are loaded one (block, k-step) ahead so at most 2*NFB are live.
     const float* xs = xt[cur] + wd * SH::SS + r16 + 4 * g * SH::RS;
-    float bx[2][NFB];
-#pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) bx[0][fb] = xs[fb * 16];
+    // responsibilities in place (the logits are not needed afterwards), so
+    // the MFMA loop below issues no transcendental work
 #pragma unroll
     for (int pb = 0; pb < NPB; ++pb) {
       const f4 lz = *reinterpret_cast<const f4*>(lzt + pb * 16 + 4 * g);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int step = pb * 4 + v;
-        const int cb_ = step & 1;
-        if (step + 1 < NPB * 4) {
-          const int np = (step + 1) >> 2, nv = (step + 1) & 3;
-          const float* brow = xs + (np * 16 + nv) * SH::RS;
+        acc[pb][0][v] = __expf(acc[pb][0][v] - lz[v]);
+        acc[pb][1][v] = __expf(acc[pb][1][v] - lz[v]);
+        nk0 += acc[pb][0][v];
+        nk1 += acc[pb][1][v];
+      }
+    }
+    // one B operand per feature block: each is reloaded for the next point
+    // step right after its two MFMAs have read it
+    float bx[NFB];
 #pragma unroll
-          for (int fb = 0; fb < NFB; ++fb) bx[cb_ ^ 1][fb] = brow[fb * 16];
-        }
-        const float r0 = __expf(acc[pb][0][v] - lz[v]);
-        const float r1 = __expf(acc[pb][1][v] - lz[v]);
-        nk0 += r0;
-        nk1 += r1;
+    for (int fb = 0; fb < NFB; ++fb) bx[fb] = xs[fb * 16];
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int step = pb * 4 + v;
+        const int np = (step + 1) >> 2, nv = (step + 1) & 3;
+        const float* brow = xs + (np * 16 + nv) * SH::RS;
+        const float r0 = acc[pb][0][v];
+        const float r1 = acc[pb][1][v];
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb) {
-          sacc[0][fb] = mfma(r0, bx[cb_][fb], sacc[0][fb]);
-          sacc[1][fb] = mfma(r1, bx[cb_][fb], sacc[1][fb]);
+          sacc[0][fb] = mfma(r0, bx[fb], sacc[0][fb]);
+          sacc[1][fb] = mfma(r1, bx[fb], sacc[1][fb]);
+          if (step + 1 < NPB * 4) bx[fb] = brow[fb * 16];
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -330,6 +325,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
     __syncthreads();
   }
   if (j == 0 || (j % FLUSH) != 0) flush();
+  if constexpr (REFINE) count_refined(a, nsel);
 
   if constexpr (FUSED) {
     if (p == 0) {
@@ -358,8 +354,8 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_logz(
   __shared__ double llred[BN];
   __shared__ float2 nrm[BN];
   __shared__ __attribute__((aligned(16))) float thrw[WC][BN];
-  __shared__ float rlist[WC][kRefineCap];
-  __shared__ unsigned short elist[WC][kRefineCap];
+  __shared__ float rlist[SH::COOP ? WC : WC * WD][kRefineCap];  // refinement lists (per group or wave)
+  __shared__ unsigned short elist[SH::COOP ? WC : WC * WD][kRefineCap];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wc = w % WC, wd = w / WC;
@@ -368,6 +364,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_logz(
   const double C = *a.cshift;
   const int nt = (int)((a.nrows + BN - 1) / BN);
   double ll = 0.0;
+  unsigned nsel = 0;  // refined logits of this wave (counted once at the end)
 
   for (int t = blockIdx.x; t < nt; t += gridDim.x) {
     const int64_t trow = (int64_t)t * BN;
@@ -422,8 +419,8 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_logz(
           }
         if constexpr (WD > 1) __syncthreads();
         else { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); __builtin_amdgcn_wave_barrier(); }
-        refine_tile<SH, WD, DPW>(acc, thrw[wc], nrm, co, xt, rows, a, C, compbase, rlist[wc], elist[wc], lane,
-                                 wd);
+        refine_tile<SH, WD, DPW>(acc, thrw[wc], nrm, co, xt, rows, a, C, compbase, rlist[SH::COOP ? wc : w], elist[SH::COOP ? wc : w], lane,
+                                 wd, nsel);
       }
 #pragma unroll
       for (int pb = 0; pb < NPB; ++pb)
@@ -458,6 +455,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_logz(
     }
     __syncthreads();
   }
+  if constexpr (REFINE) count_refined(a, nsel);
   if (tid < BN) llred[tid] = ll;
   __syncthreads();
   for (int s = BN / 2; s > 0; s >>= 1) {
@@ -702,7 +700,7 @@ __global__ void k_init_params(const float* __restrict__ X, int64_t ldx, const in
 // Host-side plan, instantiation table and launchers.
 template <int WC, int WD, int DPW>
 struct Kern {
-  static constexpr int BN = (WD == 1) ? 64 : 16;
+  static constexpr int BN = bn_for(WD, DPW);
   template <bool R>
   static void* stats_fused() { return (void*)&k_stats<WC, WD, DPW, BN, true, R>; }
   template <bool R>
@@ -736,15 +734,17 @@ static bool lookup(int WC, int WD, int DPW, KTab& t) {
 }
 
 static size_t lds_stats_bytes(int WC, int WD, int DPW) {
-  const int BN = (WD == 1) ? 64 : 16;
+  const int BN = bn_for(WD, DPW);
   const int RS = WD * (2 * DPW + 4);
   const int NTh = 64 * WC * WD;
   const int per_cu = (WC * WD == 4) ? 2 : 1;
-  const int NBUF = (per_cu == 1 && (BN * WD * DPW / 4 + NTh - 1) / NTh <= 8 && (size_t)BN * RS * 8 <= 140 * 1024) ? 2 : 1;
+  const size_t red = WD > 1 ? (size_t)WD * WC * (BN / 16) * 8 * 64 * 4 : 4;
+  const int NBUF =
+      (per_cu == 1 && (BN * WD * DPW / 4 + NTh - 1) / NTh <= 8 && (size_t)BN * RS * 8 + red <= 140 * 1024) ? 2 : 1;
   const int QP = (64 * WC * WD) / BN;
-  size_t b = (size_t)NBUF * BN * RS * 4 + (WD > 1 ? (size_t)WD * WC * (BN / 16) * 8 * 64 * 4 : 4);
+  size_t b = (size_t)NBUF * BN * RS * 4 + red;
   b += BN * 4 + (size_t)WC * BN * 4 + 2 * (size_t)QP * BN * 4 + BN * 8 + 4;
-  b += BN * 8 + BN * 8 + (size_t)WC * 256 * 6;
+  b += BN * 8 + BN * 8 + (size_t)((WD > 1 && WC == 1) ? WC : WC * WD) * 256 * 6;
   return b;
 }
 
@@ -756,10 +756,13 @@ Plan make_plan(int K, int D, int numCU, int occStats, int occLogz) {
     p.WD = 1;
     p.DPW = D <= 16 ? 16 : D <= 32 ? 32 : D <= 64 ? 64 : 128;
     const int groups = (K + 31) / 32;
-    // 4-wave workgroups, two per CU; FLASHGMM_WC=8 selects one 8-wave
-    // workgroup per CU instead (a tuning knob for measurements)
+    // one 8-wave workgroup per CU (256 components); FLASHGMM_WC=4 selects
+    // 4-wave workgroups, two per CU (a tuning knob for measurements)
     const char* env = getenv("FLASHGMM_WC");
-    const int wmax = (env && atoi(env) == 8) ? 8 : 4;
+    int wmax = (env && atoi(env) == 4) ? 4 : 8;
+    // ... unless padding K to 256 wastes much more than padding it to 128
+    const int pad8 = (K + 255) / 256 * 256 - K, pad4 = (K + 127) / 128 * 128 - K;
+    if (pad8 > pad4 + K / 8) wmax = 4;
     p.WC = groups >= wmax ? wmax : groups >= 4 ? 4 : groups >= 2 ? 2 : 1;
   } else {
     p.WD = 8;
@@ -768,7 +771,7 @@ Plan make_plan(int K, int D, int numCU, int occStats, int occLogz) {
     p.WC = 1;
   }
   p.Dp = p.DPW * p.WD;
-  p.BN = (p.WD == 1) ? 64 : 16;
+  p.BN = bn_for(p.WD, p.DPW);
   const int cw = 32 * p.WC;
   p.Kpad = (K + cw - 1) / cw * cw;
   p.P = p.Kpad / cw;
@@ -891,7 +894,7 @@ __global__ void k_fill_u64(unsigned long long* p, size_t n) {
 }
 
 hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx, bool fused,
-                        hipStream_t s, const LaunchHooks* hk) {
+                        hipStream_t s, const LaunchHooks* hk, int* nslots) {
   auto pre = [&](int which) {
     if (hk && hk->before) hk->before(hk->user, which, s);
   };
@@ -903,7 +906,8 @@ hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64
   const int nt = 64 * p.WC * p.WD;
   EArgs a = make_args(p, w, X, ldx);
   if (fused) {
-    const size_t nx = (size_t)p.R * 4 * p.P * p.BN;
+    const int R = p.R;
+    const size_t nx = (size_t)R * 4 * p.P * p.BN;
     hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(nx, 256)), dim3(256), 0, s, w.xbuf, nx);
     a.row0 = 0;
     a.nrows = N;
@@ -913,6 +917,7 @@ hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64
     hipError_t e = hipLaunchCooperativeKernel(t.fused[w.refine ? 1 : 0], dim3(p.G), dim3(nt), args, 0, s);
     if (e != hipSuccess) return e;
     post(0);
+    *nslots = R;
     return hipGetLastError();
   }
   for (int64_t r0 = 0; r0 < N; r0 += p.chunk) {
@@ -929,16 +934,16 @@ hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64
     if (e != hipSuccess) return e;
     post(0);
   }
+  *nslots = p.R;
   return hipGetLastError();
 }
 
 hipError_t launch_reduce(const Plan& p, const Workspace& w, double* Nk, double* S1, double* S2, double* ll,
-                         int accumulate, bool fused, int64_t nllslots, int64_t nrows, hipStream_t s) {
+                         int accumulate, int nslots, int nllslots, int64_t nrows, hipStream_t s) {
   const size_t total = (size_t)p.K * p.SR;
-  hipLaunchKernelGGL(k_reduce, dim3(grid_for(total, 256)), dim3(256), 0, s, w.slots, p.R, p.Kpad, p.K, p.D,
+  hipLaunchKernelGGL(k_reduce, dim3(grid_for(total, 256)), dim3(256), 0, s, w.slots, nslots, p.Kpad, p.K, p.D,
                      p.Dp, p.DPW, Nk, S1, S2, accumulate);
-  const int n = fused ? p.R : (int)nllslots;
-  hipLaunchKernelGGL(k_reduce_ll, dim3(1), dim3(64), 0, s, w.llslots, n, ll, accumulate, w.flags, w.cshift,
+  hipLaunchKernelGGL(k_reduce_ll, dim3(1), dim3(64), 0, s, w.llslots, nllslots, ll, accumulate, w.flags, w.cshift,
                      (double)nrows);
   return hipGetLastError();
 }

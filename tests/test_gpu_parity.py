@@ -65,17 +65,21 @@ def gpu_params(params):
     return tuple(torch.as_tensor(a).to(DEV) for a in params)
 
 
-@pytest.mark.parametrize("path", ["fused", "two_sweep"])
+@pytest.mark.parametrize("path", ["fused", "fused_wc4", "two_sweep"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_estep_parity(name, path):
+def test_estep_parity(name, path, monkeypatch):
+    """fused: the default fused kernel (8-wave workgroups where K allows);
+    fused_wc4: 4-wave workgroups, two per CU."""
     from soft_clustering_amd import GMM, PATH_FUSED, PATH_TWO_SWEEP
+    if path == "fused_wc4":
+        monkeypatch.setenv("FLASHGMM_WC", "4")
     Xn, Xg, params, _, _ = case_data(name)
     N, D = Xn.shape
     K = params[1].shape[0]
     log(f"[estep] case={name} path={path} N={N} D={D} K={K}")
     g = GMM(K, D)
     try:
-        g.set_path(PATH_FUSED if path == "fused" else PATH_TWO_SWEEP)
+        g.set_path(PATH_TWO_SWEEP if path.startswith("two_sweep") else PATH_FUSED)
     except Exception as e:  # fused needs P co-resident workgroups
         pytest.skip(f"fused path unavailable: {e}")
     got = g.estep_stats(Xg, *gpu_params(params))
