@@ -99,7 +99,10 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
   for (int t = blockIdx.x; t < nt; t += gridDim.x) {
     const int64_t trow = (int64_t)t * BN;
     const int rows = (int)min((int64_t)BN, a.nrows - trow);
-    {
+    if (a.dma) {
+      stage_dma<SH>(xt, a.X, a.ldx, a.row0 + trow, rows);
+      dma_wait();
+    } else {
       Stage<SH, DPW> stg;
       stg.load(a.X, a.ldx, a.row0 + trow, rows, a.D);
       stg.store(xt);
@@ -433,6 +436,7 @@ hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* 
   a.cshift = w.cshift;
   a.abmax = w.abmax;
   a.nrefined = w.nrefined;
+  a.dma = (p.D == p.Dp) ? 1 : 0;
   AArgs sa{};
   sa.sel = w.asel;
   sa.counts = count ? w.acounts : nullptr;

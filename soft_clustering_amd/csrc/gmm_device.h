@@ -74,6 +74,7 @@ struct EArgs {
   const double* cshift;  // global logit offset C
   const float2* abmax;   // Kpad  (max_d |a_kd|, max_d |b_kd|)
   unsigned long long* nrefined;  // count of refined logits (statistics only)
+  int dma;               // 1: X tiles by LDS DMA (D == Dp)
 };
 
 // ---------------------------------------------------------------------------
@@ -83,33 +84,29 @@ struct Shape {
   static constexpr int NT = kWave * WC * WD;
   static constexpr int NPB = BN / 16;         // 16-row MFMA blocks per tile
   static constexpr int NFB = DPW / 8;         // 16-wide feature blocks per wave (2*DPW/16)
-  static constexpr int SS = 2 * DPW + 4;      // LDS floats per wave segment of a row
-  static constexpr int RS = WD * SS;          // LDS floats per row
+  static constexpr int SS = DPW;              // LDS floats per wave segment of a row (its dims)
+  static constexpr int RS = WD * SS + 4;      // LDS floats per row: x (Dp) + 4 pad (rows 4 banks apart)
   static constexpr int TILE = BN * RS;        // LDS floats per tile buffer
+  static constexpr int CPR = WD * SS / 4;     // 16-byte chunks of x per row
   // Two workgroups per CU for 4-wave shapes (their barrier, exchange and
   // refinement phases then overlap the other workgroup's MFMA work), one
-  // otherwise.  Double-buffer the X tile only for one-per-CU shapes whose
-  // threads stage few float4s.
+  // otherwise.
   static constexpr int WGS_PER_CU = (WC * WD == 4) ? 2 : 1;
-  static constexpr int PER_STAGE = (BN * WD * DPW / 4 + NT - 1) / NT;
   static constexpr int RED = (WD > 1) ? WD * WC * NPB * 8 * kWave : 1;  // partial-logit exchange
-  static constexpr int NBUF =
-      (WGS_PER_CU == 1 && PER_STAGE <= 8 && TILE * 8 + RED * 4 <= 140 * 1024) ? 2 : 1;
+  static constexpr int NBUF = (TILE * 8 + RED * 4 <= (WGS_PER_CU == 1 ? 140 : 68) * 1024) ? 2 : 1;
   static constexpr int HALF = DPW / 2;
   // refinement: the WD waves of a component group share the float64 passes
   // when the group is the whole workgroup, else each wave refines its copy
   static constexpr bool COOP = (WD > 1) && (WC == 1);
 };
 
-// Stage rows [r0, r0+rows) of X into an LDS tile buffer in segment layout:
-// per row and wave segment [x^2 (first half dims) | x | x^2 (second half) | x].
-// Rows past `rows` and dims past D are zeros.  Split into a global-load half
-// and an LDS-store half so the loads of the next tile can be in flight while
-// the current tile's statistics contraction runs.
+// Stage rows [r0, r0+rows) of X into an LDS tile buffer: row p holds x
+// (Dp floats, dims past D zero) at p * RS; rows past `rows` are zero.  x^2 is
+// formed where it is used.  Register path, for any D; split into a
+// global-load half and an LDS-store half.
 template <class SH, int DPW>
 struct Stage {
-  static constexpr int Dp = DPW * (SH::RS / SH::SS);
-  static constexpr int Q4 = Dp / 4;
+  static constexpr int Q4 = SH::CPR;
   static constexpr int ITEMS = (SH::TILE / SH::RS) * Q4;  // BN * Dp/4 float4s
   static constexpr int PER = (ITEMS + SH::NT - 1) / SH::NT;
   f4 v[PER];
@@ -139,18 +136,43 @@ struct Stage {
       const int it = threadIdx.x + k * SH::NT;
       if (it < ITEMS) {
         const int pt = it / Q4;
-        const int d = (it - pt * Q4) << 2;
-        const int seg = d / DPW;
-        const int e = d - seg * DPW;
-        const int h = e / SH::HALF;
-        const int o = e - h * SH::HALF;
-        float* dst = xt + pt * SH::RS + seg * SH::SS + (2 * h) * SH::HALF + o;
-        *reinterpret_cast<f4*>(dst) = v[k] * v[k];
-        *reinterpret_cast<f4*>(dst + SH::HALF) = v[k];
+        const int c = it - pt * Q4;
+        *reinterpret_cast<f4*>(xt + pt * SH::RS + c * 4) = v[k];
       }
     }
   }
 };
+
+// The same tile by LDS DMA (global_load_lds_dwordx4): no registers held, no
+// VALU work; usable when every row has D == Dp valid floats (no dims to zero).
+// One instruction moves up to 64 consecutive 16-byte chunks of one row (lane
+// i -> LDS address M0 + 16 i, M0 = the row segment's start); rows past `rows`
+// repeat the last valid row (finite, never used).  Completion is tracked by
+// vmcnt: dma_wait() before the barrier that precedes reading the tile.
+template <class SH>
+__device__ __forceinline__ void stage_dma(float* __restrict__ xt, const float* __restrict__ X, int64_t ldx,
+                                          int64_t r0, int rows) {
+  constexpr int BN = SH::TILE / SH::RS;
+  constexpr int IPR = (SH::CPR + 63) / 64;  // instructions per row
+  constexpr int NW = SH::NT / kWave;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = w; i < BN * IPR; i += NW) {
+    const int pt = i / IPR, part = i - pt * IPR;
+    const int c = part * 64 + lane;
+    const int row = pt < rows ? pt : rows - 1;
+    if (c < SH::CPR) {
+      const float* src = X + (r0 + row) * ldx + c * 4;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(xt + pt * SH::RS + part * 256), 16,
+                                       0, 0);
+    }
+  }
+}
+
+// Wait for this wave's outstanding global memory operations (LDS DMA
+// included): s_waitcnt vmcnt(0).
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Partial logits of one wave: its 2 component blocks x NPB point blocks over
 // its dim segment.  acc must hold the starting value (c or 0).  Per group of
@@ -162,7 +184,10 @@ __device__ __forceinline__ void logit_tile(const float* __restrict__ xt, const f
                                            const float* __restrict__ w1, f4 (&acc)[SH::NPB][2],
                                            int lane, int wd) {
   const int g = lane >> 4, r16 = lane & 15;
-  const float* arow = xt + r16 * SH::RS + wd * SH::SS + g * SH::HALF;
+  // MFMA k index g: g = 0, 1 take dims [0, HALF) of the segment (x^2, x),
+  // g = 2, 3 dims [HALF, DPW)
+  const bool sq = (g & 1) == 0;
+  const float* arow = xt + r16 * SH::RS + wd * DPW + (g >> 1) * SH::HALF;
   constexpr int S4 = DPW / 8;
   f4 b0 = *reinterpret_cast<const f4*>(w0 + lane * 4);
   f4 b1 = *reinterpret_cast<const f4*>(w1 + lane * 4);
@@ -171,11 +196,14 @@ __device__ __forceinline__ void logit_tile(const float* __restrict__ xt, const f
     const int nx = (s4 + 1 < S4) ? s4 + 1 : s4;
     const f4 b0n = *reinterpret_cast<const f4*>(w0 + (nx * kWave + lane) * 4);
     const f4 b1n = *reinterpret_cast<const f4*>(w1 + (nx * kWave + lane) * 4);
-    f4 an = *reinterpret_cast<const f4*>(arow + s4 * 4);
+    auto ld = [&](int pb) { return *reinterpret_cast<const f4*>(arow + pb * 16 * SH::RS + s4 * 4); };
+    f4 an = ld(0);
 #pragma unroll
     for (int pb = 0; pb < SH::NPB; ++pb) {
-      const f4 a = an;
-      if (pb + 1 < SH::NPB) an = *reinterpret_cast<const f4*>(arow + (pb + 1) * 16 * SH::RS + s4 * 4);
+      f4 a = an;
+      if (pb + 1 < SH::NPB) an = ld(pb + 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sq ? a[i] * a[i] : a[i];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[pb][0] = mfma(a[i], b0[i], acc[pb][0]);
@@ -258,27 +286,19 @@ __device__ __forceinline__ void lane_coefs(const EArgs& a, int compbase, int r16
 }
 
 // ||x||^2 and ||x||_1 of each staged row into nrm[pt] (slightly rounded up).
-// A row's segment holds [x^2 lo | x lo | x^2 hi | x hi] (HALF floats each);
-// TPR threads per row read it as float4s and combine with shuffles.
+// TPR threads per row read its chunks (any order) and combine with shuffles.
 template <class SH, int DPW>
 __device__ __forceinline__ void row_norms2(const float* __restrict__ xt, float2* __restrict__ nrm, int Dp) {
   constexpr int BN = SH::TILE / SH::RS;
   constexpr int TPR = SH::NT / BN;  // threads per row (power of two)
-  constexpr int WDN = SH::RS / SH::SS;
-  constexpr int H4 = SH::HALF / 4;  // float4s per half
-  constexpr int PER = WDN * 2 * H4; // float4s of x^2 (and of x) per row
   const int pt = threadIdx.x / TPR, sub = threadIdx.x % TPR;
   float n2 = 0.f, n1 = 0.f;
   if (pt < BN) {
     const float* xrow = xt + pt * SH::RS;
 #pragma unroll
-    for (int q = sub; q < PER; q += TPR) {
-      const int seg = q / (2 * H4), hq = q % (2 * H4);
-      const int h = hq / H4, o = (hq % H4) * 4;
-      const float* base = xrow + seg * SH::SS + 2 * h * SH::HALF + o;
-      const f4 sq = *reinterpret_cast<const f4*>(base);
-      const f4 xv = *reinterpret_cast<const f4*>(base + SH::HALF);
-      n2 += (sq[0] + sq[1]) + (sq[2] + sq[3]);
+    for (int q = sub; q < SH::CPR; q += TPR) {
+      const f4 xv = *reinterpret_cast<const f4*>(xrow + q * 4);
+      n2 += (xv[0] * xv[0] + xv[1] * xv[1]) + (xv[2] * xv[2] + xv[3] * xv[3]);
       n1 += (fabsf(xv[0]) + fabsf(xv[1])) + (fabsf(xv[2]) + fabsf(xv[3]));
     }
   }
@@ -362,7 +382,6 @@ __device__ __forceinline__ void refine_tile(f4 (&acc)[SH::NPB][2], const float* 
       const int r = code >> 6, ln = code & 63;
       const int pt = (r >> 3) * 16 + 4 * (ln >> 4) + (r & 3);
       const int comp = compbase + ((r >> 2) & 1) * 16 + (ln & 15);
-      const float* xrow = xt + pt * SH::RS;
       const double2* wr = a.w64 + (size_t)comp * a.Dp;
       const double cf = (live && r16 == 0) ? a.cfull[comp] : 0.0;  // issued with the (a, b) loads
       double t = 0.0;
@@ -374,11 +393,8 @@ __device__ __forceinline__ void refine_tile(f4 (&acc)[SH::NPB][2], const float* 
 #pragma unroll
           for (int j = 0; j < DCH; ++j) {
             const int d = r16 + 16 * (j0 + j);  // < Dp: padded dims have a = b = 0
-            const int seg = d / DPW;
-            const int ee = d - seg * DPW;
-            const int h = ee / SH::HALF;
             ab[j] = wr[d];
-            xv[j] = xrow[seg * SH::SS + (2 * h + 1) * SH::HALF + (ee - h * SH::HALF)];
+            xv[j] = xt[pt * SH::RS + d];
           }
 #pragma unroll
           for (int j = 0; j < DCH; ++j) {

@@ -175,26 +175,35 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
     fresh = false;
   };
 
-  Stage<SH, DPW> stg;
+  // X tiles: by LDS DMA where rows need no zero padding (the next tile then
+  // streams in behind this tile's work), else through registers between
+  // tiles (holding a prefetch across the statistics would cost registers)
+  auto stage_now = [&](float* buf, int tile) {
+    const int64_t r0 = (int64_t)tile * BN;
+    const int rws = (int)min((int64_t)BN, a.nrows - r0);
+    if (a.dma) {
+      stage_dma<SH>(buf, a.X, a.ldx, a.row0 + r0, rws);
+      dma_wait();
+    } else {
+      Stage<SH, DPW> stg;
+      stg.load(a.X, a.ldx, a.row0 + r0, rws, a.D);
+      stg.store(buf);
+    }
+  };
   int j = 0;
   int t = rg;
-  if (t < nt) {
-    const int rows0 = (int)min((int64_t)BN, a.nrows - (int64_t)t * BN);
-    stg.load(a.X, a.ldx, a.row0 + (int64_t)t * BN, rows0, a.D);
-    stg.store(xt[0]);
-  }
+  if (t < nt) stage_now(xt[0], t);
   __syncthreads();
   for (; t < nt; t += a.R, ++j) {
     const int cur = (SH::NBUF == 2) ? (j & 1) : 0;
     const int64_t trow = (int64_t)t * BN;
     const int rows = (int)min((int64_t)BN, a.nrows - trow);
-    if constexpr (SH::NBUF == 1) {
-      if (j > 0) {  // single buffer: the previous tile is done (end-of-tile barrier)
-        stg.load(a.X, a.ldx, a.row0 + trow, rows, a.D);
-        stg.store(xt[0]);
-        __syncthreads();
-      }
-    }
+    const int tn = t + a.R;
+    const bool has_next = tn < nt;
+    const bool async_next = (SH::NBUF == 2) && has_next && a.dma;
+    if (async_next)  // the other buffer was released by the last end-of-tile barrier
+      stage_dma<SH>(xt[cur ^ 1], a.X, a.ldx, a.row0 + (int64_t)tn * BN,
+                    (int)min((int64_t)BN, a.nrows - (int64_t)tn * BN));
     // ---- logits
     f4 acc[NPB][2];
 #pragma unroll
@@ -275,15 +284,28 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
     }
     __syncthreads();
 
-    // ---- prefetch the next tile (double-buffered shapes) while the
-    //      statistics contraction runs
-    const int tn = t + a.R;
-    const bool has_next = (SH::NBUF == 2) && (tn < nt);
-    if (has_next) stg.load(a.X, a.ldx, a.row0 + (int64_t)tn * BN, (int)min((int64_t)BN, a.nrows - (int64_t)tn * BN), a.D);
     // ---- responsibilities and statistics: r goes from the logit
-    // accumulators straight into the A operand; B operands (x^2 | x from LDS)
-    // are loaded one (block, k-step) ahead so at most 2*NFB are live.
-    const float* xs = xt[cur] + wd * SH::SS + r16 + 4 * g * SH::RS;
+    // accumulators straight into the A operand; B operands are this lane's
+    // feature of the step's point (x^2 formed here), loaded one step ahead.
+    // Feature f of the segment: quarter q = f / HALF holds x^2 (q even) or x
+    // of dims (q / 2) * HALF + f % HALF.
+    // lane (g, r16) feeds feature f = fb * 16 + r16 of its segment for point
+    // 4g + v of each 16-point block: offsets from xs are compile-time except
+    // for DPW = 16, whose 8-dim halves split a 16-lane block
+    constexpr bool NARROW = SH::HALF < 16;
+    const float* xs = xt[cur] + wd * DPW + (NARROW ? (r16 & 7) : r16) + 4 * g * SH::RS;
+    auto fdim = [&](int fb) {  // dim offset of feature block fb (minus the lane part)
+      if constexpr (NARROW) return fb * 8;
+      else return ((fb * 16 / SH::HALF) >> 1) * SH::HALF + (fb * 16) % SH::HALF;
+    };
+    auto fsq = [&](int fb) {  // x^2 feature?
+      if constexpr (NARROW) return r16 < 8;
+      else return ((fb * 16 / SH::HALF) & 1) == 0;
+    };
+    auto bload = [&](int fb, int pt) {
+      const float x = xs[pt * SH::RS + fdim(fb)];
+      return fsq(fb) ? x * x : x;
+    };
     // responsibilities in place (the logits are not needed afterwards), so
     // the MFMA loop below issues no transcendental work
 #pragma unroll
@@ -301,26 +323,33 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
     // step right after its two MFMAs have read it
     float bx[NFB];
 #pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) bx[fb] = xs[fb * 16];
+    for (int fb = 0; fb < NFB; ++fb) bx[fb] = bload(fb, 0);
 #pragma unroll
     for (int pb = 0; pb < NPB; ++pb) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int step = pb * 4 + v;
         const int np = (step + 1) >> 2, nv = (step + 1) & 3;
-        const float* brow = xs + (np * 16 + nv) * SH::RS;
+        const int ptn = np * 16 + nv;  // relative to the lane's 4g
         const float r0 = acc[pb][0][v];
         const float r1 = acc[pb][1][v];
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb) {
           sacc[0][fb] = mfma(r0, bx[fb], sacc[0][fb]);
           sacc[1][fb] = mfma(r1, bx[fb], sacc[1][fb]);
-          if (step + 1 < NPB * 4) bx[fb] = brow[fb * 16];
+          if (step + 1 < NPB * 4) bx[fb] = bload(fb, ptn);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (has_next) stg.store(xt[cur ^ 1]);
+    if (has_next) {
+      if (async_next) {
+        dma_wait();  // this wave's share of the next tile has landed
+      } else {
+        if constexpr (SH::NBUF == 1) __syncthreads();  // every wave is done with the buffer
+        stage_now(xt[(SH::NBUF == 2) ? (cur ^ 1) : 0], tn);
+      }
+    }
     if ((j + 1) % FLUSH == 0) flush();
     __syncthreads();
   }
@@ -369,7 +398,10 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_logz(
   for (int t = blockIdx.x; t < nt; t += gridDim.x) {
     const int64_t trow = (int64_t)t * BN;
     const int rows = (int)min((int64_t)BN, a.nrows - trow);
-    {
+    if (a.dma) {
+      stage_dma<SH>(xt, a.X, a.ldx, a.row0 + trow, rows);
+      dma_wait();
+    } else {
       Stage<SH, DPW> stg;
       stg.load(a.X, a.ldx, a.row0 + trow, rows, a.D);
       stg.store(xt);
@@ -735,12 +767,10 @@ static bool lookup(int WC, int WD, int DPW, KTab& t) {
 
 static size_t lds_stats_bytes(int WC, int WD, int DPW) {
   const int BN = bn_for(WD, DPW);
-  const int RS = WD * (2 * DPW + 4);
-  const int NTh = 64 * WC * WD;
+  const int RS = WD * DPW + 4;  // mirrors Shape
   const int per_cu = (WC * WD == 4) ? 2 : 1;
   const size_t red = WD > 1 ? (size_t)WD * WC * (BN / 16) * 8 * 64 * 4 : 4;
-  const int NBUF =
-      (per_cu == 1 && (BN * WD * DPW / 4 + NTh - 1) / NTh <= 8 && (size_t)BN * RS * 8 + red <= 140 * 1024) ? 2 : 1;
+  const int NBUF = ((size_t)BN * RS * 8 + red <= (size_t)(per_cu == 1 ? 140 : 68) * 1024) ? 2 : 1;
   const int QP = (64 * WC * WD) / BN;
   size_t b = (size_t)NBUF * BN * RS * 4 + red;
   b += BN * 4 + (size_t)WC * BN * 4 + 2 * (size_t)QP * BN * 4 + BN * 8 + 4;
@@ -885,6 +915,10 @@ static EArgs make_args(const Plan& p, const Workspace& w, const float* X, int64_
   a.cshift = w.cshift;
   a.abmax = w.abmax;
   a.nrefined = w.nrefined;
+  // LDS DMA staging needs every row's Dp floats to be data (no dims to zero);
+  // FLASHGMM_DMA=0 forces the register path (for measurements)
+  const char* env = getenv("FLASHGMM_DMA");
+  a.dma = (p.D == p.Dp && !(env && atoi(env) == 0)) ? 1 : 0;
   return a;
 }
 
