@@ -72,10 +72,15 @@ typedef enum {
  *   responsibilities, statistics and log-likelihood carry float64-grade
  *   logits wherever they matter.
  * FP32: no refinement; fp32 expanded-quadratic logits throughout (errors of
- *   1e-4..1e-2 nats on data spread over many cluster widths). */
+ *   1e-4..1e-2 nats on data spread over many cluster widths).
+ * FP64: every logit from a float64 MFMA contraction (v_mfma_f64, half the
+ *   fp32 matrix rate), rounded once to fp32; for data whose responsibilities
+ *   are diffuse, where REFINED would recompute a large share of the logits.
+ *   Runs the two-sweep path. */
 typedef enum {
     GMM_PREC_REFINED = 0,
-    GMM_PREC_FP32 = 1
+    GMM_PREC_FP32 = 1,
+    GMM_PREC_FP64 = 2
 } gmm_precision;
 
 /* Create a context for K components of dimension D on the current HIP device.

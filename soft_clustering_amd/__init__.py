@@ -4,8 +4,8 @@ The compute runs in the HIP kernels of libflashgmm.so; this package holds the
 ctypes binding (argument marshalling only) and the seeded input generators.
 Importing it fails loudly when the library has not been built.
 """
-from ._lib import (GMM, GMMError, PATH_AUTO, PATH_FUSED, PATH_TWO_SWEEP, PREC_FP32, PREC_REFINED,  # noqa: F401
+from ._lib import (GMM, GMMError, PATH_AUTO, PATH_FUSED, PATH_TWO_SWEEP, PREC_FP32, PREC_FP64, PREC_REFINED,  # noqa: F401
                    EXPORTS, LIB_PATH, raw_library)
 
-__all__ = ["GMM", "GMMError", "PATH_AUTO", "PATH_FUSED", "PATH_TWO_SWEEP", "PREC_FP32", "PREC_REFINED", "EXPORTS",
+__all__ = ["GMM", "GMMError", "PATH_AUTO", "PATH_FUSED", "PATH_TWO_SWEEP", "PREC_FP32", "PREC_FP64", "PREC_REFINED", "EXPORTS",
            "LIB_PATH", "raw_library"]

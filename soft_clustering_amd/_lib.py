@@ -20,7 +20,7 @@ GMM_OK = 0
 _STATUS = {0: "GMM_OK", 1: "GMM_ERR_INVALID_ARG", 2: "GMM_ERR_UNSUPPORTED", 3: "GMM_ERR_OOM",
            4: "GMM_ERR_HIP", 5: "GMM_ERR_NUMERIC", 6: "GMM_ERR_CAPACITY"}
 PATH_AUTO, PATH_TWO_SWEEP, PATH_FUSED = 0, 1, 2
-PREC_REFINED, PREC_FP32 = 0, 1
+PREC_REFINED, PREC_FP32, PREC_FP64 = 0, 1, 2
 
 EXPORTS = ["gmm_create", "gmm_destroy", "gmm_last_error", "gmm_workspace_bytes", "gmm_set_path", "gmm_set_precision",
            "gmm_init", "gmm_estep_stats", "gmm_mstep", "gmm_fit", "gmm_soft_assign", "gmm_check",

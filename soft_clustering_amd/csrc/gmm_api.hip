@@ -110,7 +110,7 @@ void hook_after(void* user, int which, hipStream_t s) {
 }
 
 bool want_fused(const gmm_ctx* c) {
-  if (c->path == GMM_PATH_TWO_SWEEP) return false;
+  if (c->path == GMM_PATH_TWO_SWEEP || c->ws.f64) return false;  // float64 logits: two-sweep only
   if (c->path == GMM_PATH_FUSED) return c->plan.fusedOK != 0;
   return c->plan.fusedOK != 0 && c->plan.P <= 64;
 }
@@ -198,6 +198,9 @@ gmm_status gmm_create(gmm_ctx** out, int32_t K, int32_t D, void* hip_stream) {
   c->ws.cpeak = carve<double>(q, p.Kpad);
   c->ws.cshift = carve<double>(q, 1);
   c->ws.w64 = carve<double2>(q, (size_t)p.Kpad * p.Dp);
+  c->ws.wop64 = carve<double>(q, (size_t)p.Kpad * 2 * p.Dp);
+  c->ws.cvec64 = carve<double>(q, p.Kpad);
+  c->ws.f64 = 0;
   c->ws.abmax = carve<float2>(q, p.Kpad);
   c->ws.refine = 1;
   c->ws.nrefined = carve<unsigned long long>(q, 1);
@@ -297,9 +300,10 @@ gmm_status gmm_set_path(gmm_ctx* ctx, int32_t path) {
 
 gmm_status gmm_set_precision(gmm_ctx* ctx, int32_t mode) {
   if (!ctx) return GMM_ERR_INVALID_ARG;
-  if (mode != GMM_PREC_REFINED && mode != GMM_PREC_FP32)
+  if (mode != GMM_PREC_REFINED && mode != GMM_PREC_FP32 && mode != GMM_PREC_FP64)
     return fail(ctx, GMM_ERR_INVALID_ARG, "unknown precision mode %d", mode);
   ctx->ws.refine = (mode == GMM_PREC_REFINED) ? 1 : 0;
+  ctx->ws.f64 = (mode == GMM_PREC_FP64) ? 1 : 0;
   return GMM_OK;
 }
 

@@ -71,15 +71,17 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int WC, int WD, int DPW, int BN, bool REFINE>
+template <int WC, int WD, int DPW, int BN, int MODE>
 __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
   using SH = Shape<WC, WD, DPW, BN>;
+  constexpr bool REFINE = MODE == MODE_REFINE, F64 = MODE == MODE_FP64;
   constexpr int NPB = SH::NPB;
   constexpr int TLW = 16 * (BN + 1);        // one wave's transposed 16-component block
   constexpr int LSTW = 2 * kTopN * BN;      // one wave's lists (values, indices)
   constexpr int TBW = TLW > LSTW ? TLW : LSTW;
   __shared__ __attribute__((aligned(16))) float xt[SH::TILE];
-  __shared__ __attribute__((aligned(16))) float red[SH::RED];
+  __shared__ __attribute__((aligned(16))) float red[F64 ? 1 : SH::RED];
+  __shared__ double red64[F64 ? SH::RED : 1];
   __shared__ float tbuf[WC][TBW];
   __shared__ float lpart[WC][BN];
   __shared__ float2 nrm[BN];
@@ -131,17 +133,24 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
     float* tl = tbuf[wc];
     for (int cg = wc; cg < ncg; cg += WC) {
       const int compbase = cg * 32;
-      const float c0 = (wd == 0) ? a.cvec[compbase + r16] : 0.f;
-      const float c1 = (wd == 0) ? a.cvec[compbase + 16 + r16] : 0.f;
       f4 acc[NPB][2];
+      if constexpr (F64) {
+        logits_f64<SH, WC, WD, DPW>(xt, wop_block(a.wop64, compbase >> 4, WD, wd, DPW),
+                                    wop_block(a.wop64, (compbase >> 4) + 1, WD, wd, DPW),
+                                    wd == 0 ? a.cvec64[compbase + r16] : 0.0,
+                                    wd == 0 ? a.cvec64[compbase + 16 + r16] : 0.0, acc, red64, lane, wc, wd);
+      } else {
+        const float c0 = (wd == 0) ? a.cvec[compbase + r16] : 0.f;
+        const float c1 = (wd == 0) ? a.cvec[compbase + 16 + r16] : 0.f;
 #pragma unroll
-      for (int pb = 0; pb < NPB; ++pb) {
-        acc[pb][0] = f4{c0, c0, c0, c0};
-        acc[pb][1] = f4{c1, c1, c1, c1};
+        for (int pb = 0; pb < NPB; ++pb) {
+          acc[pb][0] = f4{c0, c0, c0, c0};
+          acc[pb][1] = f4{c1, c1, c1, c1};
+        }
+        logit_tile<SH, DPW>(xt, wop_block(a.wop, compbase >> 4, WD, wd, DPW),
+                            wop_block(a.wop, (compbase >> 4) + 1, WD, wd, DPW), acc, lane, wd);
+        reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
       }
-      logit_tile<SH, DPW>(xt, wop_block(a.wop, compbase >> 4, WD, wd, DPW),
-                          wop_block(a.wop, (compbase >> 4) + 1, WD, wd, DPW), acc, lane, wd);
-      reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
       if constexpr (REFINE) {
         // running maximum of guaranteed lower bounds L - E of the row's
         // logits; anything that can be selected lies within delta of the
@@ -368,15 +377,16 @@ static int grid_n(size_t n) {
 template <int WC, int WD, int DPW>
 struct AKern {
   static constexpr int BN = bn_for(WD, DPW);
-  template <bool R>
-  static void* assign() { return (void*)&k_assign<WC, WD, DPW, BN, R>; }
+  template <int M>
+  static void* assign() { return (void*)&k_assign<WC, WD, DPW, BN, M>; }
 };
 
-static bool alookup(int WC, int WD, int DPW, void* (&t)[2]) {
+static bool alookup(int WC, int WD, int DPW, void* (&t)[3]) {
 #define GMM_A(wc, wd, dpw)                                           \
   if (WC == wc && WD == wd && DPW == dpw) {                          \
-    t[0] = AKern<wc, wd, dpw>::assign<false>();                      \
-    t[1] = AKern<wc, wd, dpw>::assign<true>();                       \
+    t[0] = AKern<wc, wd, dpw>::assign<0>();                          \
+    t[1] = AKern<wc, wd, dpw>::assign<1>();                          \
+    t[2] = AKern<wc, wd, dpw>::assign<2>();                          \
     return true;                                                     \
   }
   GMM_A(1, 1, 16) GMM_A(1, 1, 32) GMM_A(1, 1, 64) GMM_A(1, 1, 128)
@@ -398,7 +408,7 @@ static int assign_wc(const Plan& p) {
 }
 
 hipError_t assign_occupancy(const Plan& p, int* occ) {
-  void* t[2];
+  void* t[3];
   const int wc = assign_wc(p);
   *occ = 0;
   if (!alookup(wc, p.WD, p.DPW, t)) return hipSuccess;  // no assignment kernel for this shape
@@ -412,7 +422,7 @@ hipError_t assign_occupancy(const Plan& p, int* occ) {
 
 hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* X, int64_t row0, int64_t rows,
                                 int64_t ldx, float threshold, int max_extra, bool count, hipStream_t s) {
-  void* t[2];
+  void* t[3];
   const int wc = assign_wc(p);
   if (!alookup(wc, p.WD, p.DPW, t)) return hipErrorInvalidValue;
   EArgs a{};
@@ -437,6 +447,8 @@ hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* 
   a.abmax = w.abmax;
   a.nrefined = w.nrefined;
   a.dma = (p.D == p.Dp) ? 1 : 0;
+  a.wop64 = w.wop64;
+  a.cvec64 = w.cvec64;
   AArgs sa{};
   sa.sel = w.asel;
   sa.counts = count ? w.acounts : nullptr;
@@ -448,7 +460,7 @@ hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* 
   const int64_t tiles = (rows + p.BN - 1) / p.BN;
   const int64_t gmax = (int64_t)p.numCU * (p.occAssign > 0 ? p.occAssign : 1);
   const int grid = (int)(tiles < gmax ? tiles : gmax);
-  return hipLaunchKernel(t[w.refine ? 1 : 0], dim3(grid), dim3(64 * wc * p.WD), args, 0, s);
+  return hipLaunchKernel(t[w.f64 ? 2 : (w.refine ? 1 : 0)], dim3(grid), dim3(64 * wc * p.WD), args, 0, s);
 }
 
 hipError_t launch_assign_begin(const Plan& p, const Workspace& w, hipStream_t s) {

@@ -12,10 +12,19 @@
 namespace gmm {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef double d4 __attribute__((ext_vector_type(4)));
 
 static constexpr float kNegInf = -__builtin_huge_valf();
 static constexpr float kPosInf = __builtin_huge_valf();
 static constexpr double kLog2Pi = 1.8378770664093454835606594728112;
+
+// Logit precision of a kernel variant: float32 MFMA; float32 MFMA with the
+// logits near each row's maximum recomputed in float64; float64 MFMA.
+enum { MODE_FP32 = 0, MODE_REFINE = 1, MODE_FP64 = 2 };
+
+__device__ __forceinline__ d4 mfma64(double a, double b, d4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -75,6 +84,8 @@ struct EArgs {
   const float2* abmax;   // Kpad  (max_d |a_kd|, max_d |b_kd|)
   unsigned long long* nrefined;  // count of refined logits (statistics only)
   int dma;               // 1: X tiles by LDS DMA (D == Dp)
+  const double* wop64;   // Kpad x 2 Dp  [a | b] in float64, MFMA-operand order (as wop)
+  const double* cvec64;  // Kpad  c_k - C in float64 (-inf: padding)
 };
 
 // ---------------------------------------------------------------------------
@@ -246,8 +257,80 @@ __device__ __forceinline__ void reduce_partial_logits(float* __restrict__ red, f
   }
 }
 
-__device__ __forceinline__ const float* wop_block(const float* wop, int cb16, int WD, int wd, int DPW) {
+template <class T>
+__device__ __forceinline__ const T* wop_block(const T* wop, int cb16, int WD, int wd, int DPW) {
   return wop + (size_t)(cb16 * WD + wd) * (DPW / 8) * 256;
+}
+
+// Float64 logits of one wave's 2 component blocks x NPB point blocks on
+// v_mfma_f64_16x16x4_f64: A = x converted exactly, squared exactly for the x^2
+// features; B = [a | b] in float64.  The f64 instruction's accumulator puts
+// row g + 4v of the 16x16 result in lane g*16 + column, register v (the f32
+// one puts row 4g + v there), so A's row r takes point 4 (r % 4) + r / 4 and
+// the registers come out in the f32 point order.  With WD > 1 the dim-segment partials are
+// summed in a fixed order through LDS (red64: WD*WC*NPB*8*64 doubles).  The
+// result, (c_k - C) + sum, is rounded once to float32 into acc.
+template <class SH, int WC, int WD, int DPW>
+__device__ __forceinline__ void logits_f64(const float* __restrict__ xt, const double* __restrict__ w0,
+                                           const double* __restrict__ w1, double c0, double c1,
+                                           f4 (&acc)[SH::NPB][2], double* __restrict__ red64, int lane, int wc,
+                                           int wd) {
+  const int g = lane >> 4, r16 = lane & 15;
+  const bool sq = (g & 1) == 0;
+  const int prow = 4 * (r16 & 3) + (r16 >> 2);
+  const float* arow = xt + prow * SH::RS + wd * DPW + (g >> 1) * SH::HALF;
+  constexpr int S4 = DPW / 8;
+  d4 p[SH::NPB][2];
+#pragma unroll
+  for (int pb = 0; pb < SH::NPB; ++pb) {
+    p[pb][0] = d4{c0, c0, c0, c0};
+    p[pb][1] = d4{c1, c1, c1, c1};
+  }
+#pragma unroll 2
+  for (int s4 = 0; s4 < S4; ++s4) {
+    const d4 b0 = *reinterpret_cast<const d4*>(w0 + (s4 * kWave + lane) * 4);
+    const d4 b1 = *reinterpret_cast<const d4*>(w1 + (s4 * kWave + lane) * 4);
+#pragma unroll
+    for (int pb = 0; pb < SH::NPB; ++pb) {
+      const f4 a = *reinterpret_cast<const f4*>(arow + pb * 16 * SH::RS + s4 * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double x = (double)a[i];
+        const double ai = sq ? x * x : x;
+        p[pb][0] = mfma64(ai, b0[i], p[pb][0]);
+        p[pb][1] = mfma64(ai, b1[i], p[pb][1]);
+      }
+    }
+  }
+  if constexpr (WD > 1) {
+    constexpr int PER = SH::NPB * 8;  // doubles per lane
+    double* mine = red64 + ((wd * WC + wc) * PER) * kWave + lane;
+#pragma unroll
+    for (int pb = 0; pb < SH::NPB; ++pb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) mine[((pb * 2 + cb) * 4 + v) * kWave] = p[pb][cb][v];
+    __syncthreads();
+#pragma unroll
+    for (int pb = 0; pb < SH::NPB; ++pb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          double t = 0.0;
+#pragma unroll
+          for (int k = 0; k < WD; ++k) t += red64[((k * WC + wc) * PER + (pb * 2 + cb) * 4 + v) * kWave + lane];
+          p[pb][cb][v] = t;
+        }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int pb = 0; pb < SH::NPB; ++pb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[pb][cb][v] = (float)p[pb][cb][v];
 }
 
 // ---------------------------------------------------------------------------

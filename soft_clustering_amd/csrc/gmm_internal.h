@@ -47,6 +47,9 @@ struct Workspace {
   double2* w64;      // Kpad * Dp    float64 (a, b) for the logit refinement
   float2* abmax;     // Kpad         per-component max |a|, max |b|
   int refine;        // 1: float64 refinement of the logits that matter
+  int f64;           // 1: float64 MFMA logits (two-sweep path)
+  double* wop64;     // Kpad * 2*Dp  as wop, float64
+  double* cvec64;    // Kpad         cfull - C, float64 (-inf: padding)
   unsigned long long* nrefined;  // refined-logit counter (gmm_refine_stats)
   double* slots;     // R * Kpad * SR
   double* llslots;   // max(R, Glogz)

@@ -95,15 +95,17 @@ __device__ __forceinline__ void row_exchange(const EArgs& a, int rg, int p, int 
 
 // ---------------------------------------------------------------------------
 // E-step statistics sweep.  FUSED: per-row log Z by exchange; else from a.logz.
-template <int WC, int WD, int DPW, int BN, bool FUSED, bool REFINE>
+template <int WC, int WD, int DPW, int BN, bool FUSED, int MODE>
 __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats(EArgs a) {
   using SH = Shape<WC, WD, DPW, BN>;
+  constexpr bool REFINE = MODE == MODE_REFINE, F64 = MODE == MODE_FP64;
   constexpr int NPB = SH::NPB, NFB = SH::NFB;
   constexpr int FLUSH = (BN >= 64) ? 32 : 128;  // tiles between fp64 flushes (2048 rows)
   constexpr int QP = (SH::NT / BN) > 0 ? (SH::NT / BN) : 1;
 
   __shared__ __attribute__((aligned(16))) float xt[SH::NBUF][SH::TILE];
-  __shared__ __attribute__((aligned(16))) float red[SH::RED];
+  __shared__ __attribute__((aligned(16))) float red[F64 ? 1 : SH::RED];
+  __shared__ double red64[F64 ? SH::RED : 1];
   __shared__ __attribute__((aligned(16))) float lzt[BN];
   __shared__ float lpart[WC][BN];
   __shared__ float exm[QP][BN], exs[QP][BN];
@@ -128,6 +130,10 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   const float c1 = (wd == 0) ? a.cvec[compbase + 16 + r16] : 0.f;
   const double C = *a.cshift;
   float co[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const double* w0d = F64 ? wop_block(a.wop64, cb16, WD, wd, DPW) : nullptr;
+  const double* w1d = F64 ? wop_block(a.wop64, cb16 + 1, WD, wd, DPW) : nullptr;
+  const double c0d = (F64 && wd == 0) ? a.cvec64[compbase + r16] : 0.0;
+  const double c1d = (F64 && wd == 0) ? a.cvec64[compbase + 16 + r16] : 0.0;
   if constexpr (REFINE) lane_coefs(a, compbase, r16, co);
   unsigned nsel = 0;  // refined logits of this wave (counted once at the end)
 
@@ -206,13 +212,17 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
                     (int)min((int64_t)BN, a.nrows - (int64_t)tn * BN));
     // ---- logits
     f4 acc[NPB][2];
+    if constexpr (F64) {
+      logits_f64<SH, WC, WD, DPW>(xt[cur], w0d, w1d, c0d, c1d, acc, red64, lane, wc, wd);
+    } else {
 #pragma unroll
-    for (int pb = 0; pb < NPB; ++pb) {
-      acc[pb][0] = f4{c0, c0, c0, c0};
-      acc[pb][1] = f4{c1, c1, c1, c1};
+      for (int pb = 0; pb < NPB; ++pb) {
+        acc[pb][0] = f4{c0, c0, c0, c0};
+        acc[pb][1] = f4{c1, c1, c1, c1};
+      }
+      logit_tile<SH, DPW>(xt[cur], w0, w1, acc, lane, wd);
+      reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
     }
-    logit_tile<SH, DPW>(xt[cur], w0, w1, acc, lane, wd);
-    reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
 
     // ---- float64 refinement of the logits that can matter
     if constexpr (REFINE) {
@@ -373,12 +383,14 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
 // First sweep of the two-sweep path: log Z of every row of the chunk, over all
 // components (Algorithm 1 steps 6-10), plus a float64 log-likelihood partial
 // per workgroup.
-template <int WC, int WD, int DPW, int BN, bool REFINE>
+template <int WC, int WD, int DPW, int BN, int MODE>
 __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_logz(EArgs a) {
   using SH = Shape<WC, WD, DPW, BN>;
+  constexpr bool REFINE = MODE == MODE_REFINE, F64 = MODE == MODE_FP64;
   constexpr int NPB = SH::NPB;
   __shared__ __attribute__((aligned(16))) float xt[SH::TILE];
-  __shared__ __attribute__((aligned(16))) float red[SH::RED];
+  __shared__ __attribute__((aligned(16))) float red[F64 ? 1 : SH::RED];
+  __shared__ double red64[F64 ? SH::RED : 1];
   __shared__ float lpart[WC][BN];
   __shared__ double llred[BN];
   __shared__ float2 nrm[BN];
@@ -422,17 +434,24 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_logz(
       }
     for (int cg = wc; cg < ncg; cg += WC) {
       const int compbase = cg * 32;
-      const float c0 = (wd == 0) ? a.cvec[compbase + r16] : 0.f;
-      const float c1 = (wd == 0) ? a.cvec[compbase + 16 + r16] : 0.f;
       f4 acc[NPB][2];
+      if constexpr (F64) {
+        logits_f64<SH, WC, WD, DPW>(xt, wop_block(a.wop64, compbase >> 4, WD, wd, DPW),
+                                    wop_block(a.wop64, (compbase >> 4) + 1, WD, wd, DPW),
+                                    wd == 0 ? a.cvec64[compbase + r16] : 0.0,
+                                    wd == 0 ? a.cvec64[compbase + 16 + r16] : 0.0, acc, red64, lane, wc, wd);
+      } else {
+        const float c0 = (wd == 0) ? a.cvec[compbase + r16] : 0.f;
+        const float c1 = (wd == 0) ? a.cvec[compbase + 16 + r16] : 0.f;
 #pragma unroll
-      for (int pb = 0; pb < NPB; ++pb) {
-        acc[pb][0] = f4{c0, c0, c0, c0};
-        acc[pb][1] = f4{c1, c1, c1, c1};
+        for (int pb = 0; pb < NPB; ++pb) {
+          acc[pb][0] = f4{c0, c0, c0, c0};
+          acc[pb][1] = f4{c1, c1, c1, c1};
+        }
+        logit_tile<SH, DPW>(xt, wop_block(a.wop, compbase >> 4, WD, wd, DPW),
+                            wop_block(a.wop, (compbase >> 4) + 1, WD, wd, DPW), acc, lane, wd);
+        reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
       }
-      logit_tile<SH, DPW>(xt, wop_block(a.wop, compbase >> 4, WD, wd, DPW),
-                          wop_block(a.wop, (compbase >> 4) + 1, WD, wd, DPW), acc, lane, wd);
-      reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
       if constexpr (REFINE) {
         // reference: running max over the components seen so far of the
         // guaranteed lower bounds L - E (it only grows, so a logit left
@@ -502,7 +521,8 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_logz(
 //   a_kd = -1/(2 s^2_kd), b_kd = mu_kd / s^2_kd,
 //   c_k  = log pi_k - 1/2 sum_d mu^2/s^2 - 1/2 sum_d log s^2 - D/2 log 2pi,
 // computed in float64, stored float32; padding components get c = -inf.
-__global__ void k_precompute_w(const float* __restrict__ mu, const float* __restrict__ var, float* wop,
+template <class T>
+__global__ void k_precompute_w(const float* __restrict__ mu, const float* __restrict__ var, T* wop,
                                int K, int D, int Kpad, int WD, int DPW) {
   const size_t total = (size_t)Kpad * 2 * WD * DPW;
   const int per_cb = WD * (DPW / 8) * 256;
@@ -518,12 +538,12 @@ __global__ void k_precompute_w(const float* __restrict__ mu, const float* __rest
     const int gg = lane >> 4;
     const int comp = cb * 16 + (lane & 15);
     const int dim = wd * DPW + (gg >> 1) * (DPW / 2) + s4 * 4 + i;
-    float val = 0.f;
+    double val = 0.0;
     if (comp < K && dim < D) {
       const double s2 = (double)var[(size_t)comp * D + dim];
-      val = (gg & 1) ? (float)((double)mu[(size_t)comp * D + dim] / s2) : (float)(-0.5 / s2);
+      val = (gg & 1) ? (double)mu[(size_t)comp * D + dim] / s2 : -0.5 / s2;
     }
-    wop[idx] = val;
+    wop[idx] = (T)val;
   }
 }
 
@@ -590,7 +610,7 @@ __global__ void k_precompute_w64(const float* __restrict__ mu, const float* __re
 // logits (and log Z) are centred near 0 instead of carrying magnitudes of
 // hundreds to thousands of nats; the log-likelihood adds N*C back in fp64.
 __global__ void k_precompute_shift(const double* __restrict__ cfull, const double* __restrict__ cpeak,
-                                   float* cvec, double* cshift, int Kpad, int D) {
+                                   float* cvec, double* cvec64, double* cshift, int Kpad, int D) {
   __shared__ double red[1024];
   double m = -__builtin_huge_val();
   for (int k = threadIdx.x; k < Kpad; k += blockDim.x) m = fmax(m, cpeak[k]);
@@ -602,7 +622,10 @@ __global__ void k_precompute_shift(const double* __restrict__ cfull, const doubl
   }
   double C = red[0] - 0.5 * D;
   if (!isfinite(C)) C = 0.0;
-  for (int k = threadIdx.x; k < Kpad; k += blockDim.x) cvec[k] = (float)(cfull[k] - C);
+  for (int k = threadIdx.x; k < Kpad; k += blockDim.x) {
+    cvec[k] = (float)(cfull[k] - C);
+    cvec64[k] = cfull[k] - C;
+  }
   if (threadIdx.x == 0) *cshift = C;
 }
 
@@ -733,27 +756,29 @@ __global__ void k_init_params(const float* __restrict__ X, int64_t ldx, const in
 template <int WC, int WD, int DPW>
 struct Kern {
   static constexpr int BN = bn_for(WD, DPW);
-  template <bool R>
-  static void* stats_fused() { return (void*)&k_stats<WC, WD, DPW, BN, true, R>; }
-  template <bool R>
-  static void* stats_two() { return (void*)&k_stats<WC, WD, DPW, BN, false, R>; }
-  template <bool R>
-  static void* logz() { return (void*)&k_logz<WC, WD, DPW, BN, R>; }
+  template <int M>
+  static void* stats_fused() { return (void*)&k_stats<WC, WD, DPW, BN, true, M>; }
+  template <int M>
+  static void* stats_two() { return (void*)&k_stats<WC, WD, DPW, BN, false, M>; }
+  template <int M>
+  static void* logz() { return (void*)&k_logz<WC, WD, DPW, BN, M>; }
 };
 
+// Kernel variants of one shape, indexed by logit precision mode (the fused
+// kernel has no float64-logit variant: that mode runs the two-sweep path).
 struct KTab {
-  void* fused[2];  // [refine]
-  void* two[2];
-  void* logz[2];
+  void* fused[2];
+  void* two[3];
+  void* logz[3];
 };
 
 static bool lookup(int WC, int WD, int DPW, KTab& t) {
 #define GMM_K(wc, wd, dpw)                                                                            \
   if (WC == wc && WD == wd && DPW == dpw) {                                                           \
     using KK = Kern<wc, wd, dpw>;                                                                     \
-    t = KTab{{KK::stats_fused<false>(), KK::stats_fused<true>()},                                     \
-             {KK::stats_two<false>(), KK::stats_two<true>()},                                         \
-             {KK::logz<false>(), KK::logz<true>()}};                                                  \
+    t = KTab{{KK::stats_fused<0>(), KK::stats_fused<1>()},                                             \
+             {KK::stats_two<0>(), KK::stats_two<1>(), KK::stats_two<2>()},                                \
+             {KK::logz<0>(), KK::logz<1>(), KK::logz<2>()}};                                              \
     return true;                                                                                      \
   }
   GMM_K(1, 1, 16) GMM_K(1, 1, 32) GMM_K(1, 1, 64) GMM_K(1, 1, 128)
@@ -835,6 +860,7 @@ size_t workspace_bytes(const Plan& p) {
   b += up((size_t)p.Kpad * 4);
   b += 2 * up((size_t)p.Kpad * 8) + up(8);
   b += up((size_t)p.Kpad * p.Dp * 16) + up((size_t)p.Kpad * 8) + up(8);
+  b += up((size_t)p.Kpad * 2 * p.Dp * 8) + up((size_t)p.Kpad * 8);  // wop64, cvec64
   b += up((size_t)p.R * p.Kpad * p.SR * 8);
   b += up((size_t)(p.R > p.Glogz ? p.R : p.Glogz) * 8);
   b += up((size_t)p.chunk * 4);
@@ -880,11 +906,14 @@ static int grid_for(size_t total, int block) {
 hipError_t launch_precompute(const Plan& p, const Workspace& w, const float* weights, const float* means,
                              const float* vars, hipStream_t s) {
   const size_t total = (size_t)p.Kpad * 2 * p.Dp;
-  hipLaunchKernelGGL(k_precompute_w, dim3(grid_for(total, 256)), dim3(256), 0, s, means, vars, w.wop, p.K,
+  hipLaunchKernelGGL(k_precompute_w<float>, dim3(grid_for(total, 256)), dim3(256), 0, s, means, vars, w.wop, p.K,
                      p.D, p.Kpad, p.WD, p.DPW);
+  if (w.f64)
+    hipLaunchKernelGGL(k_precompute_w<double>, dim3(grid_for(total, 256)), dim3(256), 0, s, means, vars, w.wop64,
+                       p.K, p.D, p.Kpad, p.WD, p.DPW);
   hipLaunchKernelGGL(k_precompute_c, dim3((p.Kpad + 3) / 4), dim3(256), 0, s, weights, means, vars, w.cfull,
                      w.cpeak, p.K, p.D, p.Kpad);
-  hipLaunchKernelGGL(k_precompute_shift, dim3(1), dim3(1024), 0, s, w.cfull, w.cpeak, w.cvec, w.cshift, p.Kpad,
+  hipLaunchKernelGGL(k_precompute_shift, dim3(1), dim3(1024), 0, s, w.cfull, w.cpeak, w.cvec, w.cvec64, w.cshift, p.Kpad,
                      p.D);
   hipLaunchKernelGGL(k_precompute_w64, dim3((p.Kpad + 3) / 4), dim3(256), 0, s, means, vars, w.w64, w.abmax,
                      p.K, p.D, p.Kpad, p.Dp);
@@ -919,6 +948,8 @@ static EArgs make_args(const Plan& p, const Workspace& w, const float* X, int64_
   // FLASHGMM_DMA=0 forces the register path (for measurements)
   const char* env = getenv("FLASHGMM_DMA");
   a.dma = (p.D == p.Dp && !(env && atoi(env) == 0)) ? 1 : 0;
+  a.wop64 = w.wop64;
+  a.cvec64 = w.cvec64;
   return a;
 }
 
@@ -939,6 +970,8 @@ hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64
   if (!lookup(p.WC, p.WD, p.DPW, t)) return hipErrorInvalidValue;
   const int nt = 64 * p.WC * p.WD;
   EArgs a = make_args(p, w, X, ldx);
+  const int mode = w.f64 ? 2 : (w.refine ? 1 : 0);
+  if (fused && mode == 2) return hipErrorInvalidValue;  // no fused float64-logit kernel
   if (fused) {
     const int R = p.R;
     const size_t nx = (size_t)R * 4 * p.P * p.BN;
@@ -960,11 +993,11 @@ hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64
     a.slot_acc = (r0 > 0) ? 1 : 0;
     void* args[] = {&a};
     pre(1);
-    hipError_t e = hipLaunchKernel(t.logz[w.refine ? 1 : 0], dim3(p.Glogz), dim3(nt), args, 0, s);
+    hipError_t e = hipLaunchKernel(t.logz[mode], dim3(p.Glogz), dim3(nt), args, 0, s);
     if (e != hipSuccess) return e;
     post(1);
     pre(0);
-    e = hipLaunchKernel(t.two[w.refine ? 1 : 0], dim3(p.G), dim3(nt), args, 0, s);
+    e = hipLaunchKernel(t.two[mode], dim3(p.G), dim3(nt), args, 0, s);
     if (e != hipSuccess) return e;
     post(0);
   }

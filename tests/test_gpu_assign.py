@@ -29,6 +29,8 @@ CASES = {
     "argmax_only_thr1": ("tiny", 3_001, 8, 16, None, 1.0, 3, 3),
     "argmax_only_m0": ("tiny", 3_001, 8, 16, None, 0.1, 0, 3),
     "low_thr_m8": ("tiny", 3_001, 16, 40, None, 1e-3, 8, 2),
+    "fp64_logits_d200": ("mid", 2_005, 200, 100, None, 0.1, 3, 2),
+    "fp64_logits_embed": ("embed", 2_003, 768, 512, None, 0.01, 8, 1),
 }
 
 
@@ -108,6 +110,9 @@ def test_soft_assign_parity(name):
     Xg = to_dev(Xc, ldx)
     floor = 1.0 / 12.0 if law == "ivf" else (1e-5 if law == "embed" else 1e-6)
     g = GMM(K, D, DEV)
+    if name.startswith("fp64_logits"):
+        from soft_clustering_amd import PREC_FP64
+        g.set_precision(PREC_FP64)
     w, mu, var = trained_params(g, Xg, Xn, K, floor, iters)
     offsets, ids = g.soft_assign(Xg, w, mu, var, thr, m)
     torch.cuda.synchronize()

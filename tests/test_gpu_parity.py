@@ -65,12 +65,13 @@ def gpu_params(params):
     return tuple(torch.as_tensor(a).to(DEV) for a in params)
 
 
-@pytest.mark.parametrize("path", ["fused", "fused_wc4", "two_sweep"])
+@pytest.mark.parametrize("path", ["fused", "fused_wc4", "two_sweep", "two_sweep_fp64"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_estep_parity(name, path, monkeypatch):
     """fused: the default fused kernel (8-wave workgroups where K allows);
-    fused_wc4: 4-wave workgroups, two per CU."""
-    from soft_clustering_amd import GMM, PATH_FUSED, PATH_TWO_SWEEP
+    fused_wc4: 4-wave workgroups, two per CU; two_sweep_fp64: float64 MFMA
+    logits (GMM_PREC_FP64)."""
+    from soft_clustering_amd import GMM, PATH_FUSED, PATH_TWO_SWEEP, PREC_FP64
     if path == "fused_wc4":
         monkeypatch.setenv("FLASHGMM_WC", "4")
     Xn, Xg, params, _, _ = case_data(name)
@@ -82,6 +83,8 @@ def test_estep_parity(name, path, monkeypatch):
         g.set_path(PATH_TWO_SWEEP if path.startswith("two_sweep") else PATH_FUSED)
     except Exception as e:  # fused needs P co-resident workgroups
         pytest.skip(f"fused path unavailable: {e}")
+    if path.endswith("_fp64"):
+        g.set_precision(PREC_FP64)
     got = g.estep_stats(Xg, *gpu_params(params))
     g.check()
     got = [t.cpu().numpy() for t in got]
