@@ -716,19 +716,63 @@ __global__ void k_mstep(const double* __restrict__ Nk, const double* __restrict_
 // ---------------------------------------------------------------------------
 // Initialisation: column sums (pass 0) or squared deviations (pass 1) of row
 // blocks in float64, then a pairwise tree over blocks.
-__global__ void k_colpart(const float* __restrict__ X, int64_t N, int64_t ldx, int D,
-                          const double* __restrict__ mean, double* part, int pass) {
+// Column sums of X over a row range per workgroup (init: the global
+// per-dimension variance): pass 0 sums x, pass 1 sums (x - mean)^2.  256 threads:
+// CG float4 column groups x RL row lanes; each thread keeps two independent
+// float64 accumulators per column (rows alternate), so the float4 loads
+// stream; the RL row lanes are then combined in a fixed order through LDS.
+// Deterministic: the row range and summation order depend only on N and the
+// grid.
+__global__ void __launch_bounds__(256) k_colpart(const float* __restrict__ X, int64_t N, int64_t ldx, int D,
+                                                 const double* __restrict__ mean, double* part, int pass) {
+  __shared__ double red[256 * 4];
+  const int D4 = (D + 3) >> 2;
+  int CG = 1;
+  while (CG < D4 && CG < 256) CG <<= 1;
+  const int RL = 256 / CG;
+  const int tid = threadIdx.x, cg0 = tid % CG, rl = tid / CG;
   const int64_t per = (N + gridDim.x - 1) / gridDim.x;
   const int64_t r0 = (int64_t)blockIdx.x * per;
   const int64_t r1 = min(N, r0 + per);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    double s = 0.0;
-    const double m = pass ? mean[d] : 0.0;
-    for (int64_t r = r0; r < r1; ++r) {
-      const double x = (double)X[r * ldx + d];
-      s += pass ? (x - m) * (x - m) : x;
+  for (int c4 = cg0; c4 < D4 + (CG - D4 % CG) % CG; c4 += CG) {  // uniform trip count
+    const bool live = c4 < D4;
+    const int d0 = c4 * 4;
+    double m[4] = {0.0, 0.0, 0.0, 0.0};
+    if (pass && live)
+      for (int e = 0; e < 4; ++e) m[e] = (d0 + e < D) ? mean[d0 + e] : 0.0;
+    double sa[4] = {0.0, 0.0, 0.0, 0.0}, sb[4] = {0.0, 0.0, 0.0, 0.0};
+    if (live) {
+      int64_t r = r0 + rl;
+      for (; r + RL < r1; r += 2 * RL) {
+        const f4 xa = __builtin_nontemporal_load(reinterpret_cast<const f4*>(X + r * ldx + d0));
+        const f4 xb = __builtin_nontemporal_load(reinterpret_cast<const f4*>(X + (r + RL) * ldx + d0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double a = (double)xa[e] - m[e], b = (double)xb[e] - m[e];
+          sa[e] += pass ? a * a : a;
+          sb[e] += pass ? b * b : b;
+        }
+      }
+      if (r < r1) {
+        const f4 xa = __builtin_nontemporal_load(reinterpret_cast<const f4*>(X + r * ldx + d0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double a = (double)xa[e] - m[e];
+          sa[e] += pass ? a * a : a;
+        }
+      }
     }
-    part[(size_t)blockIdx.x * D + d] = s;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[(rl * CG + cg0) * 4 + e] = sa[e] + sb[e];
+    __syncthreads();
+    if (rl == 0 && live) {
+      for (int e = 0; e < 4; ++e) {
+        double t = 0.0;
+        for (int q = 0; q < RL; ++q) t += red[(q * CG + cg0) * 4 + e];
+        if (d0 + e < D) part[(size_t)blockIdx.x * D + d0 + e] = t;
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -1027,7 +1071,7 @@ hipError_t launch_mstep(const Plan& p, const Workspace& w, const double* Nk, con
 hipError_t launch_init(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx,
                        float var_floor, float* weights, float* means, float* vars, hipStream_t s) {
   const int nb = (int)((N < (int64_t)w.colG) ? N : (int64_t)w.colG);
-  const int bt = p.D >= 1024 ? 1024 : ((p.D + 63) / 64) * 64;
+  const int bt = 256;
   hipLaunchKernelGGL(k_colpart, dim3(nb), dim3(bt), 0, s, X, N, ldx, p.D, (const double*)nullptr, w.colpart,
                      0);
   hipLaunchKernelGGL(k_colfinal, dim3((p.D + 255) / 256), dim3(256), 0, s, w.colpart, nb, p.D, (double)N,
