@@ -39,6 +39,41 @@ def useful_flops(N, K, D):
     return float(N) * K * (8 * D + 2)
 
 
+TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "k_stats_fused_large_traffic.md")
+KERNEL_SOURCES = ("gmm_kernels.hip", "gmm_device.h", "gmm_internal.h")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "soft_clustering_amd", "csrc")
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(base, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused E-step on the large workload, from the
+    committed FETCH_SIZE + WRITE_SIZE counter summary (each counter scaled by
+    what it reads for a copy of known size), or None when the kernel sources
+    have changed since those counters were taken."""
+    try:
+        with open(TRAFFIC_PROFILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    fields = {}
+    for ln in text.splitlines():
+        if ":" in ln and ln.split(":", 1)[0] in ("traffic_bytes_per_launch", "source_hash"):
+            k, v = ln.split(":", 1)
+            fields[k] = v.strip()
+    if fields.get("source_hash") != kernel_source_hash() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(workload, sample_rows, budget_s):
     """Time the oracle as it stands on a prefix of the same data, scaled to
     ms per EM iteration at the full N (EM cost is linear in N)."""
@@ -160,6 +195,9 @@ def main():
     avg_ms = stats_ms / max(stats_n, 1)
     achieved = F / (kern_ms * 1e-3) / 1e12
     hl = hist.cpu().numpy()
+    traffic = None
+    if fused and args.workload == "large" and args.precision == "refined" and not args.rows:
+        traffic = measured_traffic()
     line = {
         "metric": "ms per EM iteration and GFLOP/s at N=100M,K=1024,D=128 fp32; % MFMA peak",
         "value": round(gflops, 1),
@@ -174,7 +212,8 @@ def main():
         "pct_mfma_peak": round(100 * gflops / (MFMA_FP32_PEAK_TFLOPS * 1e3), 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "kernel": "k_stats (fused E-step)" if fused else "k_logz + k_stats (two-sweep E-step)",
                      "kernel_ms_per_iteration": round(kern_ms, 3),
                      "avg_launch_ms": round(avg_ms, 3), "launches": stats_n + logz_n},
