@@ -187,8 +187,9 @@ gmm_status gmm_create(gmm_ctx** out, int32_t K, int32_t D, void* hip_stream) {
   c->bytes = gmm::workspace_bytes(c->plan);
   e = hipMalloc(&c->base, c->bytes);
   if (e != hipSuccess) {
+    const size_t bytes = c->bytes;
     delete c;
-    return fail(nullptr, GMM_ERR_OOM, "workspace hipMalloc(%zu): %s", (size_t)0, hipGetErrorString(e));
+    return fail(nullptr, GMM_ERR_OOM, "workspace hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
   }
   const gmm::Plan& p = c->plan;
   char* q = (char*)c->base;

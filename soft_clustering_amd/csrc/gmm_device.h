@@ -160,13 +160,14 @@ struct Stage {
 // i -> LDS address M0 + 16 i, M0 = the row segment's start); rows past `rows`
 // repeat the last valid row (finite, never used).  Completion is tracked by
 // vmcnt: dma_wait() before the barrier that precedes reading the tile.
+// The SH::NT / 64 waves that share the load pass their index w.
 template <class SH>
 __device__ __forceinline__ void stage_dma(float* __restrict__ xt, const float* __restrict__ X, int64_t ldx,
-                                          int64_t r0, int rows) {
+                                          int64_t r0, int rows, int w = (int)(threadIdx.x >> 6)) {
   constexpr int BN = SH::TILE / SH::RS;
   constexpr int IPR = (SH::CPR + 63) / 64;  // instructions per row
   constexpr int NW = SH::NT / kWave;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = w; i < BN * IPR; i += NW) {
     const int pt = i / IPR, part = i - pt * IPR;
