@@ -44,7 +44,7 @@ namespace gmm {
 // round rd of tile j only after it has gathered round rd of tile j-1 from
 // every peer, and each peer publishes that word only after it has read its
 // round rd words of tile j-2, so no member overwrites a word a slower member
-// has not read yet (in both the plain and the pipelined statistics sweep).
+// has not read yet.
 template <int BN>
 __device__ __forceinline__ void xpost(const EArgs& a, int rg, int p, int j, int rd, float v) {
   const int tid = threadIdx.x;  // < BN: row
@@ -116,9 +116,10 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   constexpr bool REFINE = MODE == MODE_REFINE, F64 = MODE == MODE_FP64;
   constexpr int NPB = SH::NPB, NFB = SH::NFB;
   constexpr int FLUSH = (BN >= 64) ? 32 : 128;  // tiles between fp64 flushes (2048 rows)
-  // workgroups flush at staggered tiles, so the float64 atomics of the grid
-  // do not all reach L2 at once
-  const int fphase = (int)(blockIdx.x % FLUSH);
+  // row groups flush at staggered tiles, so the float64 atomics of the grid
+  // do not all reach L2 at once; the members of a row group flush together
+  // (a flush delays the member's next exchange word, so staggering within a
+  // row group would hold the whole group up once per member)
   constexpr int QP = (SH::NT / BN) > 0 ? (SH::NT / BN) : 1;
 
   __shared__ __attribute__((aligned(16))) float xt[SH::NBUF][SH::TILE];
@@ -140,6 +141,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   const int G = a.R * a.P;
   int rg, p;
   rg_member(G, a.P, rg, p);
+  const int fphase = rg % FLUSH;  // flush stagger, by row group
   const int compbase = p * 32 * WC + wc * 32;  // first component of this wave
   const int cb16 = compbase >> 4;
   const float* w0 = wop_block(a.wop, cb16, WD, wd, DPW);
@@ -394,270 +396,6 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
       }
       if (tid == 0) a.llslots[rg] = a.slot_acc ? a.llslots[rg] + llred[0] : llred[0];
     }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Fused E-step with the statistics of each row tile deferred by one tile.
-// Same arithmetic and the same order of every floating-point operation as the
-// fused k_stats (so the results are bit-identical), but the two exchanges of
-// a tile are no longer waited for right after they are published:
-//
-//   iteration j:  logits(j) on MFMA, publish round 1 (j)        [X tile j]
-//                 gather round 2 (j-1), statistics(j-1) on MFMA  [X tile j-1,
-//                                                                 logits(j-1) from LDS]
-//                 start loading X tile j+1 into tile j-1's buffer
-//                 gather round 1 (j), float64 refinement(j), per-row
-//                 log-sum-exp partial, publish round 2 (j), logits(j) -> LDS
-//
-// Between publishing and gathering each round there is a whole MFMA phase, so
-// the exchange latency and the skew between the P members are covered by
-// matrix work.  The deferred tile's logits wait in LDS in a lane-private
-// layout (each lane writes and reads back its own 32 values).
-template <int WC, int DPW, int BN, int MODE>
-__global__ void __launch_bounds__(kWave* WC) k_stats_pipe(EArgs a) {
-  using SH = Shape<WC, 1, DPW, BN>;
-  static_assert(MODE != MODE_FP64, "float64 logits run the two-sweep path");
-  constexpr bool REFINE = MODE == MODE_REFINE;
-  constexpr int NPB = SH::NPB, NFB = SH::NFB;
-  constexpr int FLUSH = (BN >= 64) ? 32 : 128;  // tiles between fp64 flushes
-  const int fphase = (int)(blockIdx.x % FLUSH);  // staggered as in k_stats
-  constexpr int QP = (SH::NT / BN) > 0 ? (SH::NT / BN) : 1;
-
-  __shared__ __attribute__((aligned(16))) float xt[2][SH::TILE];
-  __shared__ f4 lbuf[WC][NPB * 2][kWave];  // deferred tile's logits
-  __shared__ __attribute__((aligned(16))) float lzt[BN];
-  __shared__ float lpart[WC][BN];
-  __shared__ float exm[QP][BN], exs[QP][BN];
-  __shared__ double llred[BN];
-  __shared__ float2 nrm[BN];
-  __shared__ __attribute__((aligned(16))) float thrs[BN];
-  __shared__ float rlist[WC][kRefineCap];
-  __shared__ unsigned short elist[WC][kRefineCap];
-
-  const int tid = threadIdx.x, lane = tid & 63, wc = tid >> 6;
-  const int g = lane >> 4, r16 = lane & 15;
-  const int G = a.R * a.P;
-  int rg, p;
-  rg_member(G, a.P, rg, p);
-  const int compbase = p * 32 * WC + wc * 32;
-  const int cb16 = compbase >> 4;
-  const float* w0 = wop_block(a.wop, cb16, 1, 0, DPW);
-  const float* w1 = wop_block(a.wop, cb16 + 1, 1, 0, DPW);
-  const float c0 = a.cvec[compbase + r16];
-  const float c1 = a.cvec[compbase + 16 + r16];
-  const double C = *a.cshift;
-  float co[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if constexpr (REFINE) lane_coefs(a, compbase, r16, co);
-  unsigned nsel = 0;
-
-  const int nt = (int)((a.nrows + BN - 1) / BN);
-  const int nj = (rg < nt) ? (nt - rg + a.R - 1) / a.R : 0;  // tiles of this row group
-  f4 sacc[2][NFB];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) sacc[cb][fb] = f4{0.f, 0.f, 0.f, 0.f};
-  float nk0 = 0.f, nk1 = 0.f;
-  double ll = 0.0;
-  bool fresh = (a.slot_acc == 0);
-  double* sbase = a.slots + ((size_t)rg * a.Kpad + compbase) * (2 * a.Dp + 1);
-  const int SR = 2 * a.Dp + 1;
-
-  auto put = [&](double* ptr, double val) {
-    if (fresh)
-      __hip_atomic_store(ptr, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-      __hip_atomic_fetch_add(ptr, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  auto flush = [&]() {
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-#pragma unroll
-      for (int fb = 0; fb < NFB; ++fb) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          put(sbase + (size_t)(cb * 16 + 4 * g + v) * SR + fb * 16 + r16, (double)sacc[cb][fb][v]);
-        sacc[cb][fb] = f4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-    float t0 = nk0 + __shfl_xor(nk0, 16);
-    t0 += __shfl_xor(t0, 32);
-    float t1 = nk1 + __shfl_xor(nk1, 16);
-    t1 += __shfl_xor(t1, 32);
-    if (g == 0) {
-      put(sbase + (size_t)r16 * SR + 2 * a.Dp, (double)t0);
-      put(sbase + (size_t)(16 + r16) * SR + 2 * a.Dp, (double)t1);
-    }
-    nk0 = nk1 = 0.f;
-    fresh = false;
-  };
-  auto tile_rows = [&](int jj) { return (int)min((int64_t)BN, a.nrows - (int64_t)(rg + jj * a.R) * BN); };
-  auto stage = [&](float* buf, int jj, bool wait) {
-    const int64_t r0 = (int64_t)(rg + jj * a.R) * BN;
-    if (a.dma) {
-      stage_dma<SH>(buf, a.X, a.ldx, a.row0 + r0, tile_rows(jj));
-      if (wait) dma_wait();
-    } else {
-      Stage<SH, DPW> stg;
-      stg.load(a.X, a.ldx, a.row0 + r0, tile_rows(jj), a.D);
-      stg.store(buf);
-    }
-  };
-
-  if (nj > 0) stage(xt[0], 0, true);
-  __syncthreads();
-  for (int j = 0; j <= nj; ++j) {
-    const bool cur_ok = j < nj;
-    const int cur = j & 1;
-    const int rows = cur_ok ? tile_rows(j) : 0;
-    f4 acc[NPB][2];
-    // ---- logits of tile j, round 1 published
-    if (cur_ok) {
-#pragma unroll
-      for (int pb = 0; pb < NPB; ++pb) {
-        acc[pb][0] = f4{c0, c0, c0, c0};
-        acc[pb][1] = f4{c1, c1, c1, c1};
-      }
-      logit_tile<SH, DPW>(xt[cur], w0, w1, acc, lane, 0);
-      if constexpr (REFINE) {
-        row_norms2<SH, DPW>(xt[cur], nrm, a.Dp);
-        __syncthreads();
-#pragma unroll
-        for (int pb = 0; pb < NPB; ++pb)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float2 nn = nrm[pb * 16 + 4 * g + v];
-            const float lb = fmaxf(acc[pb][0][v] - err_bound(a.kappa, co[0], co[1], co[2], nn),
-                                   acc[pb][1][v] - err_bound(a.kappa, co[3], co[4], co[5], nn));
-            const float m = row16_max(lb);
-            if (r16 == 0) lpart[wc][pb * 16 + 4 * g + v] = m;
-            if (v == 3) __builtin_amdgcn_sched_barrier(0);
-          }
-        __syncthreads();
-        if (tid < BN) {
-          float m = kNegInf;
-#pragma unroll
-          for (int k = 0; k < WC; ++k) m = fmaxf(m, lpart[k][tid]);
-          xpost<BN>(a, rg, p, j, 0, m);
-        }
-      }
-    }
-    // ---- statistics of tile j-1 (its logits from LDS, log Z from round 2)
-    if (j > 0) {
-      const int jp = j - 1;
-      const int prow = tile_rows(jp);
-      xgather<BN, QP, true>(a, rg, jp, 1, exm, exs, lzt);
-      if (tid < BN) {
-        const float lz = lzt[tid];
-        if (p == 0 && tid < prow) ll += (double)lz;
-        if (tid >= prow) lzt[tid] = kPosInf;
-      }
-      __syncthreads();
-      constexpr bool NARROW = SH::HALF < 16;
-      const float* xs = xt[cur ^ 1] + (NARROW ? (r16 & 7) : r16) + 4 * g * SH::RS;
-      auto fdim = [&](int fb) {
-        if constexpr (NARROW) return fb * 8;
-        else return ((fb * 16 / SH::HALF) >> 1) * SH::HALF + (fb * 16) % SH::HALF;
-      };
-      auto fsq = [&](int fb) {
-        if constexpr (NARROW) return r16 < 8;
-        else return ((fb * 16 / SH::HALF) & 1) == 0;
-      };
-      auto bload = [&](int fb, int pt) {
-        const float x = xs[pt * SH::RS + fdim(fb)];
-        return fsq(fb) ? x * x : x;
-      };
-      // responsibilities of one point block: exp(L - log Z) of the block's
-      // 2 x 4 logits of this lane
-      auto resp = [&](int pb, f4& q0, f4& q1) {
-        const f4 lz = *reinterpret_cast<const f4*>(lzt + pb * 16 + 4 * g);
-        const f4 l0 = lbuf[wc][pb * 2][lane], l1 = lbuf[wc][pb * 2 + 1][lane];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          q0[v] = __expf(l0[v] - lz[v]);
-          q1[v] = __expf(l1[v] - lz[v]);
-          nk0 += q0[v];
-          nk1 += q1[v];
-        }
-      };
-      f4 q0, q1;
-      resp(0, q0, q1);
-      float bx[NFB];
-#pragma unroll
-      for (int fb = 0; fb < NFB; ++fb) bx[fb] = bload(fb, 0);
-#pragma unroll
-      for (int pb = 0; pb < NPB; ++pb) {
-        f4 n0, n1;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int step = pb * 4 + v;
-          const int np = (step + 1) >> 2, nv = (step + 1) & 3;
-          const int ptn = np * 16 + nv;
-          const float r0 = q0[v], r1 = q1[v];
-#pragma unroll
-          for (int fb = 0; fb < NFB; ++fb) {
-            sacc[0][fb] = mfma(r0, bx[fb], sacc[0][fb]);
-            sacc[1][fb] = mfma(r1, bx[fb], sacc[1][fb]);
-            if (step + 1 < NPB * 4) bx[fb] = bload(fb, ptn);
-          }
-          if (v == 1 && pb + 1 < NPB) resp(pb + 1, n0, n1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (pb + 1 < NPB) {
-          q0 = n0;
-          q1 = n1;
-        }
-      }
-      if ((j + fphase) % FLUSH == 0) flush();
-    }
-    __syncthreads();  // tile j-1's buffer and logits are free
-    if (j + 1 < nj) stage(xt[cur ^ 1], j + 1, false);
-    // ---- float64 refinement of tile j, per-row log Z partial published
-    if (cur_ok) {
-      if constexpr (REFINE) {
-        xgather<BN, QP, false>(a, rg, j, 0, exm, exs, thrs);
-        if (tid < BN) thrs[tid] = (tid < rows) ? thrs[tid] - kDelta : kPosInf;
-        __syncthreads();
-        refine_tile<SH, 1, DPW>(acc, thrs, nrm, co, xt[cur], rows, a, C, compbase, rlist[wc], elist[wc], lane, 0,
-                                nsel);
-      }
-#pragma unroll
-      for (int pb = 0; pb < NPB; ++pb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float m = row16_max(fmaxf(acc[pb][0][v], acc[pb][1][v]));
-          const float ms = (m == kNegInf) ? 0.f : m;
-          float e = __expf(acc[pb][0][v] - ms) + __expf(acc[pb][1][v] - ms);
-          e = row16_sum(e);
-          if (r16 == 0) lpart[wc][pb * 16 + 4 * g + v] = (e > 0.f) ? ms + __logf(e) : kNegInf;
-        }
-#pragma unroll
-      for (int pb = 0; pb < NPB; ++pb) {
-        lbuf[wc][pb * 2][lane] = acc[pb][0];
-        lbuf[wc][pb * 2 + 1][lane] = acc[pb][1];
-      }
-      __syncthreads();
-      if (tid < BN) {
-        float M = kNegInf, S = 0.f;
-#pragma unroll
-        for (int k = 0; k < WC; ++k) lse_merge(M, S, lpart[k][tid], 1.f);
-        xpost<BN>(a, rg, p, j, 1, lse_of(M, S));
-      }
-    }
-    if (a.dma && j + 1 < nj) dma_wait();
-    __syncthreads();
-  }
-  if (nj == 0 || ((nj + fphase) % FLUSH) != 0) flush();
-  if constexpr (REFINE) count_refined(a, nsel);
-  if (p == 0) {
-    if (tid < BN) llred[tid] = ll;
-    __syncthreads();
-    for (int s = BN / 2; s > 0; s >>= 1) {
-      if (tid < s) llred[tid] += llred[tid + s];
-      __syncthreads();
-    }
-    if (tid == 0) a.llslots[rg] = a.slot_acc ? a.llslots[rg] + llred[0] : llred[0];
   }
 }
 
@@ -1088,20 +826,12 @@ struct Kern {
   static void* stats_two() { return (void*)&k_stats<WC, WD, DPW, BN, false, M>; }
   template <int M>
   static void* logz() { return (void*)&k_logz<WC, WD, DPW, BN, M>; }
-  // the deferred-statistics variant needs the LDS of a whole CU for the
-  // waiting logits, so it is built for the one-workgroup-per-CU shape only
-  template <int M>
-  static void* stats_pipe() {
-    if constexpr (WD == 1 && WC == 8) return (void*)&k_stats_pipe<WC, DPW, BN, M>;
-    else return nullptr;
-  }
 };
 
 // Kernel variants of one shape, indexed by logit precision mode (the fused
 // kernel has no float64-logit variant: that mode runs the two-sweep path).
 struct KTab {
   void* fused[2];
-  void* pipe[2];  // nullptr where not built
   void* two[3];
   void* logz[3];
 };
@@ -1111,7 +841,6 @@ static bool lookup(int WC, int WD, int DPW, KTab& t) {
   if (WC == wc && WD == wd && DPW == dpw) {                                                           \
     using KK = Kern<wc, wd, dpw>;                                                                     \
     t = KTab{{KK::stats_fused<0>(), KK::stats_fused<1>()},                                             \
-             {KK::stats_pipe<0>(), KK::stats_pipe<1>()},                                               \
              {KK::stats_two<0>(), KK::stats_two<1>(), KK::stats_two<2>()},                                \
              {KK::logz<0>(), KK::logz<1>(), KK::logz<2>()}};                                              \
     return true;                                                                                      \
@@ -1223,13 +952,6 @@ hipError_t occupancy(const Plan& p, int* occStats, int* occLogz) {
   int o1b = 0, o2b = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1, (const void*)t.fused[0], nt, 0);
   if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1b, (const void*)t.fused[1], nt, 0);
-  for (int m = 0; m < 2 && e == hipSuccess; ++m) {
-    void* k = t.pipe[m];
-    if (!k) continue;
-    int op = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&op, (const void*)k, nt, 0);
-    if (op < o1b) o1b = op;
-  }
   if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o2, (const void*)t.logz[0], nt, 0);
   if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o2b, (const void*)t.logz[1], nt, 0);
   if (e != hipSuccess) return e;
@@ -1323,11 +1045,7 @@ hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64
     hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(nx, 256)), dim3(256), 0, s, w.xbuf, nx);
     void* args[] = {&a};
     pre(0);
-    // deferred-statistics kernel where built; FLASHGMM_PIPE=0 selects the
-    // plain one (a knob for measurements; both give identical results)
-    const char* env = getenv("FLASHGMM_PIPE");
-    const bool pipe = t.pipe[mode] && !(env && atoi(env) == 0);
-    hipError_t e = hipLaunchCooperativeKernel(pipe ? t.pipe[mode] : t.fused[mode], dim3(p.G), dim3(nt), args, 0, s);
+    hipError_t e = hipLaunchCooperativeKernel(t.fused[mode], dim3(p.G), dim3(nt), args, 0, s);
     if (e != hipSuccess) return e;
     post(0);
     *nslots = R;

@@ -65,18 +65,15 @@ def gpu_params(params):
     return tuple(torch.as_tensor(a).to(DEV) for a in params)
 
 
-@pytest.mark.parametrize("path", ["fused", "fused_plain", "fused_wc4", "two_sweep", "two_sweep_fp64"])
+@pytest.mark.parametrize("path", ["fused", "fused_wc4", "two_sweep", "two_sweep_fp64"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_estep_parity(name, path, monkeypatch):
-    """fused: the default fused kernel (8-wave workgroups with the statistics
-    deferred by one tile where K allows); fused_plain: 8-wave workgroups
-    without the deferral; fused_wc4: 4-wave workgroups, two per CU;
-    two_sweep_fp64: float64 MFMA logits (GMM_PREC_FP64)."""
+    """fused: the default fused kernel (8-wave workgroups where K allows);
+    fused_wc4: 4-wave workgroups, two per CU; two_sweep_fp64: float64 MFMA
+    logits (GMM_PREC_FP64)."""
     from soft_clustering_amd import GMM, PATH_FUSED, PATH_TWO_SWEEP, PREC_FP64
     if path == "fused_wc4":
         monkeypatch.setenv("FLASHGMM_WC", "4")
-    if path == "fused_plain":
-        monkeypatch.setenv("FLASHGMM_PIPE", "0")
     Xn, Xg, params, _, _ = case_data(name)
     N, D = Xn.shape
     K = params[1].shape[0]
@@ -191,32 +188,6 @@ def test_bit_identical_reruns_and_paths_agree(name):
         errs = check_stats((y[0], y[1], y[2], y[3][0]), (x[0], x[1], x[2], x[3][0]), ms, rms,
                            np.sqrt(params[2].astype(np.float64)), 5e-5)
         assert not errs, "\n".join(errs)
-
-
-@pytest.mark.parametrize("rows", [100, 64 * 64 * 3 + 17, 20_037])
-@pytest.mark.parametrize("precision", ["refined", "fp32"])
-def test_deferred_statistics_bit_identical(rows, precision, monkeypatch):
-    """The fused kernel that defers each tile's statistics by one tile does
-    every floating-point operation of the plain fused kernel in the same
-    order: outputs are bit-identical.  Row counts cover row groups with no
-    tile, with one tile (only the drain step), and several tiles with a
-    ragged last one; K=1024 and K=16384 are the shapes that use it."""
-    from soft_clustering_amd import GMM, PATH_FUSED, PREC_FP32, PREC_REFINED
-    for name in ("mid_prefix", "k16384"):
-        Xn, Xg, params, _, _ = case_data(name)
-        X = Xg[:rows]
-        K, D = params[1].shape
-        log(f"[deferred] case={name} rows={rows} precision={precision}")
-        g = GMM(K, D)
-        g.set_path(PATH_FUSED)
-        g.set_precision(PREC_REFINED if precision == "refined" else PREC_FP32)
-        out = {}
-        for pipe in ("1", "0"):
-            monkeypatch.setenv("FLASHGMM_PIPE", pipe)
-            out[pipe] = [t.clone() for t in g.estep_stats(X, *gpu_params(params))]
-            g.check()
-        for x, y, what in zip(out["1"], out["0"], ("Nk", "S1", "S2", "LL")):
-            assert torch.equal(x, y), f"{name} rows={rows}: {what} differs"
 
 
 def test_accumulate_over_row_chunks():
