@@ -239,7 +239,21 @@ def main():
         dt_a = time.perf_counter() - t0
         line["soft_assign"] = {"rows": nb, "ms": round(dt_a * 1e3, 1), "lists_per_row": round(ids.shape[0] / nb, 4),
                                "logit_tflops_two_sweeps": round(2 * 4.0 * nb * K * D / dt_a / 1e12, 2)}
-        del Xb, offsets, ids
+        del offsets, ids
+        # the pages' own rule: argmax plus the second-best component when its
+        # responsibility exceeds tau, tau in {0.5, 1, 2} / K
+        top2 = []
+        for f in (0.5, 1.0, 2.0):
+            tau = f / K
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            offsets, ids = g.soft_assign(Xb, w, mu, var, tau, 1)
+            torch.cuda.synchronize()
+            dt_t = time.perf_counter() - t0
+            top2.append({"tau_times_K": f, "ms": round(dt_t * 1e3, 1), "lists_per_row": round(ids.shape[0] / nb, 4)})
+            del offsets, ids
+        line["soft_assign_top2"] = top2
+        del Xb
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_rows, args.cpu_budget_s)

@@ -31,6 +31,13 @@ CASES = {
     "low_thr_m8": ("tiny", 3_001, 16, 40, None, 1e-3, 8, 2),
     "fp64_logits_d200": ("mid", 2_005, 200, 100, None, 0.1, 3, 2),
     "fp64_logits_embed": ("embed", 2_003, 768, 512, None, 0.01, 8, 1),
+    # the pages' multi-assignment rule (Section 4.3): the argmax plus the
+    # second-best component when its responsibility exceeds tau, with tau a
+    # small multiple of 1/K (r > tau and r >= tau differ only on exact ties,
+    # which the boundary rule excludes)
+    "top2_tau_half_over_k": ("ivf", 20_011, 128, 16_384, None, 0.5 / 16_384, 1, 2),
+    "top2_tau_1_over_k": ("ivf", 20_011, 128, 16_384, None, 1.0 / 16_384, 1, 2),
+    "top2_tau_2_over_k": ("ivf", 20_011, 128, 16_384, None, 2.0 / 16_384, 1, 2),
 }
 
 
