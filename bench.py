@@ -29,14 +29,18 @@ WORKLOAD_TEXT = {
     "mid": "mid EM: N=1,000,000, D=128, K=1024, fp32, diagonal covariance, 30 EM iterations",
     "tiny": "tiny EM: N=10,000, D=8, K=16, fp32, diagonal covariance, 10 EM iterations",
     "embed": "embedding-like EM: N=10,000,000, D=768, K=4096, fp32, diagonal covariance, 20 EM iterations",
+    "iso": "isotropic EM (sigma_k^2 I): N=100,000,000, D=128, K=1024, fp32, 30 EM iterations",
     "ivf": "IVF: EM on a 1,000,000-row sample, D=128, K=16384, integer values 0..255, 10 EM iterations; "
            "then soft assignment (argmax + up to 3 with r >= 0.1) of 10,000,000 base rows into CSR lists",
 }
 
 
-def useful_flops(N, K, D):
-    """[x^2, x] logit contraction (4D per pair) + r^T[1, x, x^2] statistics (2(2D+1))."""
-    return float(N) * K * (8 * D + 2)
+def useful_flops(N, K, D, iso=False):
+    """Diagonal: [x^2, x] logit contraction (4D per pair) + r^T[1, x, x^2]
+    statistics (2(2D+1)).  Isotropic: x.mu/s^2 plus the ||x||^2 term (2D+2)
+    + r^T[1, x, ||x||^2] (2(D+2)); run on the diagonal kernels, which issue
+    the diagonal count."""
+    return float(N) * K * ((4 * D + 6) if iso else (8 * D + 2))
 
 
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -79,8 +83,12 @@ def cpu_baseline(workload, sample_rows, budget_s):
     ms per EM iteration at the full N (EM cost is linear in N)."""
     import torch
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-    import oracle.gmm_oracle as O
     from soft_clustering_amd import datagen
+    iso = workload == "iso"
+    if iso:
+        import oracle.gmm_oracle_iso as O
+    else:
+        import oracle.gmm_oracle as O
     wl = datagen.WORKLOADS[workload]
     mix = datagen.mixture(wl.law, wl.D, wl.K, seed=wl.seed)
     n = min(sample_rows, wl.N)
@@ -91,7 +99,7 @@ def cpu_baseline(workload, sample_rows, budget_s):
     t0 = time.perf_counter()
     iters = 0
     while True:
-        Nk, S1, S2, ll = O.estep_stats(X, w, mu, var, method="gemm")
+        Nk, S1, S2, ll = O.estep_stats(X, w, mu, var, method="gemm")  # S2: Q for the isotropic model
         w, mu, var = O.mstep(Nk, S1, S2, n, wl.var_floor, mu, var)
         iters += 1
         if time.perf_counter() - t0 > budget_s or iters >= 3:
@@ -103,7 +111,7 @@ def cpu_baseline(workload, sample_rows, budget_s):
             "kind": "oracle",
             "sample": f"{iters} EM iteration(s) of the float64 numpy oracle on the first {n} rows of the "
                       f"{workload} workload ({dt:.2f} s each), scaled by {n_full}/{n}",
-            "gflops": useful_flops(n, wl.K, wl.D) / dt / 1e9,
+            "gflops": useful_flops(n, wl.K, wl.D, iso) / dt / 1e9,
             "torch_threads": torch.get_num_threads()}
 
 
@@ -147,6 +155,7 @@ def main():
     if args.precision is None:
         args.precision = "fp64" if args.workload == "embed" else "refined"
     ivf = args.workload == "ivf"
+    iso = args.workload == "iso"
     N = args.rows or (wl.extra["train_rows"] if ivf else wl.N)
     K, D = wl.K, wl.D
     dev = torch.device("cuda", 0)
@@ -161,10 +170,12 @@ def main():
     g = GMM(K, D, dev)
     g.set_path({"auto": PATH_AUTO, "fused": PATH_FUSED, "two_sweep": PATH_TWO_SWEEP}[args.path])
     g.set_precision({"refined": PREC_REFINED, "fp32": PREC_FP32, "fp64": PREC_FP64}[args.precision])
-    w, mu, var = g.init(X, datagen.init_rows(N, K, seed=wl.init_seed), wl.var_floor)
+    init = g.init_iso if iso else g.init
+    fit = g.fit_iso if iso else g.fit
+    w, mu, var = init(X, datagen.init_rows(N, K, seed=wl.init_seed), wl.var_floor)
     hist_w = torch.zeros(max(args.warmup, 1), dtype=torch.float64, device=dev)
     if args.warmup > 0:
-        g.fit(X, w, mu, var, args.warmup, wl.var_floor, hist_w)
+        fit(X, w, mu, var, args.warmup, wl.var_floor, hist_w)
     g.check()
     torch.cuda.synchronize()
 
@@ -174,7 +185,7 @@ def main():
     g.refine_stats()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    g.fit(X, w, mu, var, args.steps, wl.var_floor, hist)
+    fit(X, w, mu, var, args.steps, wl.var_floor, hist)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     stats_ms, stats_n, logz_ms, logz_n = g.profile_read()
@@ -183,7 +194,7 @@ def main():
     g.check()
 
     ms_step = dt * 1e3 / args.steps
-    F = useful_flops(N, K, D)
+    F = useful_flops(N, K, D, iso)
     gflops = F / (dt / args.steps) / 1e9
     fused = logz_n == 0
     # dominant kernel: fused path, the one E-step launch per iteration
@@ -201,14 +212,15 @@ def main():
     line = {
         "metric": "ms per EM iteration and GFLOP/s at N=100M,K=1024,D=128 fp32; % MFMA peak",
         "value": round(gflops, 1),
-        "unit": "GFLOP/s (useful: N*K*(8D+2) per EM iteration)",
+        "unit": "GFLOP/s (useful: N*K*(" + ("4D+6" if iso else "8D+2") + ") per EM iteration)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic (seeded mixture, generated on the GPU)",
         "config": {"workload": WORKLOAD_TEXT[args.workload] if not args.rows else
                    f"{args.workload} law with N={N}", "N": N, "K": K, "D": D,
-                   "path": "fused" if fused else "two_sweep", "logit_precision": args.precision},
+                   "path": "fused" if fused else "two_sweep", "logit_precision": args.precision,
+                   "covariance": "isotropic" if iso else "diagonal"},
         "pct_mfma_peak": round(100 * gflops / (MFMA_FP32_PEAK_TFLOPS * 1e3), 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4),

@@ -145,6 +145,43 @@ gmm_status gmm_fit(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_t ld
                    float var_floor, float *weights, float *means, float *vars /*[dev] in/out*/,
                    double *loglik_hist /*[dev] T*/);
 
+/* Isotropic model: Sigma_k = sigma^2_k I, the covariance of the pages'
+ * Section 2 and Algorithm 1, with Eq. (3) averaged over the D dimensions:
+ *   sigma^2_k = sum_n r_nk ||x_n - mu_k||^2 / (D N_k) = (Q_k / N_k - ||mu_k||^2) / D,
+ *   Q_k = sum_n r_nk ||x_n||^2.
+ * var_iso is a float32 device array of K variances (16-byte aligned); the
+ * other arguments, the floor, the empty-component rule, errors and
+ * determinism are as in the diagonal calls above.  The E-step runs the
+ * diagonal kernels on the variances broadcast over the dimensions (the
+ * logits are identical); the workspace holds the K x D broadcast.
+ *
+ * gmm_init_iso: means are the rows init_rows, every variance is the mean over
+ * the dimensions of the population per-dimension variance of X, floored;
+ * weights 1/K.  Synchronises the stream (init_rows is a host array). */
+gmm_status gmm_init_iso(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_t ldx,
+                        const int64_t *init_rows /*[host]*/, float var_floor,
+                        float *weights /*[dev] K*/, float *means /*[dev] K*D*/, float *var_iso /*[dev] K*/);
+
+/* E-step statistics of the isotropic model: Nk, S1 as gmm_estep_stats, and
+ * Q[k] = sum_n r_nk ||x_n||^2 (float64); accumulate as gmm_estep_stats. */
+gmm_status gmm_estep_stats_iso(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_t ldx,
+                               const float *weights, const float *means, const float *var_iso /*[dev]*/,
+                               double *Nk /*[dev] K*/, double *S1 /*[dev] K*D*/, double *Q /*[dev] K*/,
+                               double *loglik /*[dev] 1*/, int32_t accumulate);
+
+/* M-step of the isotropic model, in place: weights_k = Nk_k / n_total,
+ * means_k = S1_k / Nk_k, var_iso_k = max((Q_k / Nk_k - ||means_k||^2) / D,
+ * var_floor), all in float64 with float32 results; Nk_k < 1e-6 keeps the
+ * component's mean and variance. */
+gmm_status gmm_mstep_iso(gmm_ctx *ctx, const double *Nk, const double *S1, const double *Q /*[dev]*/,
+                         double n_total, float var_floor,
+                         float *weights, float *means, float *var_iso /*[dev], in/out*/);
+
+/* T EM iterations of the isotropic model, as gmm_fit. */
+gmm_status gmm_fit_iso(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_t ldx, int32_t T,
+                       float var_floor, float *weights, float *means, float *var_iso /*[dev] in/out*/,
+                       double *loglik_hist /*[dev] T*/);
+
 /* Inverted lists of a soft assignment (Section 4.2 argmax assignment and the
  * Section 4.3 multi-assignment, with the threshold and count rule below):
  * each row goes to its highest-responsibility component (lowest index on

@@ -24,6 +24,7 @@ PREC_REFINED, PREC_FP32, PREC_FP64 = 0, 1, 2
 
 EXPORTS = ["gmm_create", "gmm_destroy", "gmm_last_error", "gmm_workspace_bytes", "gmm_set_path", "gmm_set_precision",
            "gmm_init", "gmm_estep_stats", "gmm_mstep", "gmm_fit", "gmm_soft_assign", "gmm_check",
+           "gmm_init_iso", "gmm_estep_stats_iso", "gmm_mstep_iso", "gmm_fit_iso",
            "gmm_profile", "gmm_profile_read", "gmm_refine_stats"]
 
 
@@ -49,6 +50,10 @@ def _load():
         "gmm_estep_stats": (i32, [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32]),
         "gmm_mstep": (i32, [vp, vp, vp, vp, f64, f32, vp, vp, vp]),
         "gmm_fit": (i32, [vp, vp, i64, i64, i32, f32, vp, vp, vp, vp]),
+        "gmm_init_iso": (i32, [vp, vp, i64, i64, vp, f32, vp, vp, vp]),
+        "gmm_estep_stats_iso": (i32, [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32]),
+        "gmm_mstep_iso": (i32, [vp, vp, vp, vp, f64, f32, vp, vp, vp]),
+        "gmm_fit_iso": (i32, [vp, vp, i64, i64, i32, f32, vp, vp, vp, vp]),
         "gmm_soft_assign": (i32, [vp, vp, i64, i64, vp, vp, vp, f32, i32, vp, vp, i64, vp]),
         "gmm_check": (i32, [vp]),
         "gmm_profile": (i32, [vp, i32]),
@@ -210,6 +215,65 @@ class GMM:
             self._check(_lib.gmm_fit(self._h, _ptr(X), N, ldx, int(T), float(var_floor), _ptr(w), _ptr(mu),
                                      _ptr(var), _ptr(ll_hist)))
         return w, mu, var, ll_hist
+
+    # ---- isotropic model (var_iso: K variances)
+    def _params_iso(self, w, mu, var_iso):
+        _need(w, torch.float32, (self.K,), "weights", self.device)
+        _need(mu, torch.float32, (self.K, self.D), "means", self.device)
+        _need(var_iso, torch.float32, (self.K,), "var_iso", self.device)
+
+    def init_iso(self, X, rows, var_floor):
+        N, ldx = _rows(X, self.D, self.device)
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        if rows.shape != (self.K,):
+            raise ValueError(f"rows must have shape ({self.K},)")
+        w, mu, _ = self.params()
+        var_iso = torch.empty(self.K, dtype=torch.float32, device=self.device)
+        with torch.cuda.device(self.device):
+            self._check(_lib.gmm_init_iso(self._h, _ptr(X), N, ldx, rows.ctypes.data_as(ctypes.c_void_p),
+                                          float(var_floor), _ptr(w), _ptr(mu), _ptr(var_iso)))
+        return w, mu, var_iso
+
+    def estep_stats_iso(self, X, w, mu, var_iso, out=None, accumulate=False):
+        N, ldx = _rows(X, self.D, self.device)
+        self._params_iso(w, mu, var_iso)
+        K, D = self.K, self.D
+        if out is None:
+            out = (torch.zeros(K, dtype=torch.float64, device=self.device),
+                   torch.zeros(K, D, dtype=torch.float64, device=self.device),
+                   torch.zeros(K, dtype=torch.float64, device=self.device),
+                   torch.zeros(1, dtype=torch.float64, device=self.device))
+        Nk, S1, Q, ll = out
+        _need(Nk, torch.float64, (K,), "Nk", self.device)
+        _need(S1, torch.float64, (K, D), "S1", self.device)
+        _need(Q, torch.float64, (K,), "Q", self.device)
+        _need(ll, torch.float64, (1,), "loglik", self.device)
+        with torch.cuda.device(self.device):
+            self._check(_lib.gmm_estep_stats_iso(self._h, _ptr(X), N, ldx, _ptr(w), _ptr(mu), _ptr(var_iso),
+                                                 _ptr(Nk), _ptr(S1), _ptr(Q), _ptr(ll), int(bool(accumulate))))
+        return Nk, S1, Q, ll
+
+    def mstep_iso(self, Nk, S1, Q, n_total, var_floor, w, mu, var_iso):
+        K, D = self.K, self.D
+        _need(Nk, torch.float64, (K,), "Nk", self.device)
+        _need(S1, torch.float64, (K, D), "S1", self.device)
+        _need(Q, torch.float64, (K,), "Q", self.device)
+        self._params_iso(w, mu, var_iso)
+        with torch.cuda.device(self.device):
+            self._check(_lib.gmm_mstep_iso(self._h, _ptr(Nk), _ptr(S1), _ptr(Q), float(n_total), float(var_floor),
+                                           _ptr(w), _ptr(mu), _ptr(var_iso)))
+        return w, mu, var_iso
+
+    def fit_iso(self, X, w, mu, var_iso, T, var_floor, ll_hist=None):
+        N, ldx = _rows(X, self.D, self.device)
+        self._params_iso(w, mu, var_iso)
+        if ll_hist is None:
+            ll_hist = torch.zeros(int(T), dtype=torch.float64, device=self.device)
+        _need(ll_hist, torch.float64, (int(T),), "loglik_hist", self.device)
+        with torch.cuda.device(self.device):
+            self._check(_lib.gmm_fit_iso(self._h, _ptr(X), N, ldx, int(T), float(var_floor), _ptr(w), _ptr(mu),
+                                         _ptr(var_iso), _ptr(ll_hist)))
+        return w, mu, var_iso, ll_hist
 
     def soft_assign(self, X, w, mu, var, threshold=0.1, max_extra=3, ids_capacity=None):
         """CSR inverted lists: (offsets int64[K+1], ids int32[nnz])."""

@@ -199,6 +199,8 @@ gmm_status gmm_create(gmm_ctx** out, int32_t K, int32_t D, void* hip_stream) {
   c->ws.cpeak = carve<double>(q, p.Kpad);
   c->ws.cshift = carve<double>(q, 1);
   c->ws.w64 = carve<double2>(q, (size_t)p.Kpad * p.Dp);
+  c->ws.vexp = carve<float>(q, (size_t)p.K * p.D);
+  c->ws.qiso = carve<double>(q, p.K);
   c->ws.wop64 = carve<double>(q, (size_t)p.Kpad * 2 * p.Dp);
   c->ws.cvec64 = carve<double>(q, p.Kpad);
   c->ws.f64 = 0;
@@ -378,6 +380,94 @@ gmm_status gmm_fit(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, int32_t
     hipError_t e = gmm::launch_mstep(ctx->plan, ctx->ws, Nk, S1, S2, (double)N, var_floor, weights, means, vars,
                                      ctx->stream);
     if (e != hipSuccess) return hip_fail(ctx, e, "mstep launch");
+  }
+  return GMM_OK;
+}
+
+gmm_status gmm_init_iso(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, const int64_t* init_rows,
+                        float var_floor, float* weights, float* means, float* var_iso) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  gmm_status st = check_x(ctx, X, N, ldx);
+  if (st) return st;
+  st = check_params(ctx, weights, means, var_iso);
+  if (st) return st;
+  if (!init_rows) return fail(ctx, GMM_ERR_INVALID_ARG, "init_rows is NULL");
+  if (!(var_floor > 0.f) || !isfinite(var_floor)) return fail(ctx, GMM_ERR_INVALID_ARG, "var_floor must be > 0");
+  const int K = ctx->plan.K;
+  for (int k = 0; k < K; ++k)
+    if (init_rows[k] < 0 || init_rows[k] >= N)
+      return fail(ctx, GMM_ERR_INVALID_ARG, "init_rows[%d]=%lld out of [0, N)", k, (long long)init_rows[k]);
+  hipError_t e = hipMemcpyAsync(ctx->ws.rows, init_rows, (size_t)K * 8, hipMemcpyHostToDevice, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "init rows copy");
+  e = gmm::launch_init_iso(ctx->plan, ctx->ws, X, N, ldx, var_floor, weights, means, var_iso, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "init launch");
+  e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "init");
+  return GMM_OK;
+}
+
+gmm_status gmm_estep_stats_iso(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, const float* weights,
+                               const float* means, const float* var_iso, double* Nk, double* S1, double* Q,
+                               double* loglik, int32_t accumulate) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  gmm_status st = check_x(ctx, X, N, ldx);
+  if (st) return st;
+  st = check_params(ctx, weights, means, var_iso);
+  if (st) return st;
+  if (!Nk || !S1 || !Q || !loglik) return fail(ctx, GMM_ERR_INVALID_ARG, "statistics outputs must be non-NULL");
+  if (accumulate != 0 && accumulate != 1) return fail(ctx, GMM_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  const gmm::Plan& p = ctx->plan;
+  hipError_t e = gmm::launch_iso_expand(p, ctx->ws, var_iso, ctx->stream);
+  // S2 goes to the statistics scratch; cleared first when the reduction adds
+  double* S2 = ctx->ws.stats + p.K + (size_t)p.K * p.D;
+  if (e == hipSuccess && accumulate) e = gmm::launch_fill_zero(S2, (size_t)p.K * p.D, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "isotropic set-up");
+  st = estep_into(ctx, X, N, ldx, weights, means, ctx->ws.vexp, Nk, S1, S2, loglik, accumulate);
+  if (st) return st;
+  e = gmm::launch_iso_q(p, S2, Q, accumulate, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "isotropic Q");
+  return GMM_OK;
+}
+
+gmm_status gmm_mstep_iso(gmm_ctx* ctx, const double* Nk, const double* S1, const double* Q, double n_total,
+                         float var_floor, float* weights, float* means, float* var_iso) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  if (!Nk || !S1 || !Q) return fail(ctx, GMM_ERR_INVALID_ARG, "statistics inputs must be non-NULL");
+  gmm_status st = check_params(ctx, weights, means, var_iso);
+  if (st) return st;
+  if (!(n_total > 0.0) || !isfinite(n_total)) return fail(ctx, GMM_ERR_INVALID_ARG, "n_total must be > 0");
+  if (!(var_floor > 0.f) || !isfinite(var_floor)) return fail(ctx, GMM_ERR_INVALID_ARG, "var_floor must be > 0");
+  hipError_t e = gmm::launch_mstep_iso(ctx->plan, ctx->ws, Nk, S1, Q, n_total, var_floor, weights, means, var_iso,
+                                       ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "mstep launch");
+  return GMM_OK;
+}
+
+gmm_status gmm_fit_iso(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, int32_t T, float var_floor,
+                       float* weights, float* means, float* var_iso, double* loglik_hist) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  gmm_status st = check_x(ctx, X, N, ldx);
+  if (st) return st;
+  st = check_params(ctx, weights, means, var_iso);
+  if (st) return st;
+  if (T < 1) return fail(ctx, GMM_ERR_INVALID_ARG, "T must be >= 1");
+  if (!loglik_hist) return fail(ctx, GMM_ERR_INVALID_ARG, "loglik_hist is NULL");
+  if (!(var_floor > 0.f) || !isfinite(var_floor)) return fail(ctx, GMM_ERR_INVALID_ARG, "var_floor must be > 0");
+  const gmm::Plan& p = ctx->plan;
+  const int K = p.K, D = p.D;
+  double* Nk = ctx->ws.stats;
+  double* S1 = Nk + K;
+  double* S2 = S1 + (size_t)K * D;
+  for (int t = 0; t < T; ++t) {
+    hipError_t e = gmm::launch_iso_expand(p, ctx->ws, var_iso, ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "isotropic set-up");
+    st = estep_into(ctx, X, N, ldx, weights, means, ctx->ws.vexp, Nk, S1, S2, loglik_hist + t, 0);
+    if (st) return st;
+    e = gmm::launch_iso_q(p, S2, ctx->ws.qiso, 0, ctx->stream);
+    if (e == hipSuccess)
+      e = gmm::launch_mstep_iso(p, ctx->ws, Nk, S1, ctx->ws.qiso, (double)N, var_floor, weights, means, var_iso,
+                                ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "isotropic mstep launch");
   }
   return GMM_OK;
 }

@@ -60,6 +60,8 @@ struct Workspace {
   double* colmean;   // D
   int64_t* rows;     // K  init rows
   int* flags;        // [0] numeric fault, [1] exchange timeout, [2] list overflow
+  float* vexp;       // K * D  isotropic variances broadcast over the dimensions
+  double* qiso;      // K      isotropic Q_k of gmm_fit_iso
   int colG;
   // soft assignment
   int32_t* asel;                 // assignChunk * 9  per-row selections
@@ -92,6 +94,14 @@ hipError_t launch_reduce(const Plan& p, const Workspace& w, double* Nk, double* 
                          double* ll, int accumulate, int nslots, int nllslots, int64_t nrows,
                          hipStream_t s);
 
+hipError_t launch_iso_expand(const Plan& p, const Workspace& w, const float* var_iso, hipStream_t s);
+hipError_t launch_iso_q(const Plan& p, const double* S2, double* Q, int accumulate, hipStream_t s);
+hipError_t launch_mstep_iso(const Plan& p, const Workspace& w, const double* Nk, const double* S1, const double* Q,
+                            double n_total, float var_floor, float* weights, float* means, float* var_iso,
+                            hipStream_t s);
+hipError_t launch_init_iso(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx,
+                           float var_floor, float* weights, float* means, float* var_iso, hipStream_t s);
+hipError_t launch_fill_zero(double* p, size_t n, hipStream_t s);
 hipError_t launch_mstep(const Plan& p, const Workspace& w, const double* Nk, const double* S1,
                         const double* S2, double n_total, float var_floor, float* weights,
                         float* means, float* vars, hipStream_t s);

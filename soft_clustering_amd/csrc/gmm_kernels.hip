@@ -734,6 +734,74 @@ __global__ void k_mstep(const double* __restrict__ Nk, const double* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Isotropic model, Sigma_k = sigma^2_k I ("Flash-GMM", Section 2, the pages'
+// own covariance; Eq. (3) averaged over the D dimensions).  Its E-step is the
+// diagonal one with sigma^2_kd = sigma^2_k for every d, so the E-step kernels
+// above run on the broadcast variances; Q_k = sum_n r_nk ||x_n||^2 is the sum
+// over d of the diagonal S2_kd.  Every reduction over d is a fixed-order
+// float64 tree (one wave per component), so results are deterministic.
+__device__ __forceinline__ double wave_sum64(double v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__global__ void k_iso_expand(const float* __restrict__ var_iso, float* __restrict__ vexp, int K, int D) {
+  const size_t total = (size_t)K * D;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x)
+    vexp[i] = var_iso[i / D];
+}
+
+// Q_k (+)= sum_d S2_kd
+__global__ void k_iso_q(const double* __restrict__ S2, double* Q, int K, int D, int accumulate) {
+  const int k = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x & 63;
+  if (k >= K) return;
+  double t = 0.0;
+  for (int d = lane; d < D; d += kWave) t += S2[(size_t)k * D + d];
+  t = wave_sum64(t);
+  if (lane == 0) Q[k] = accumulate ? Q[k] + t : t;
+}
+
+// pi_k = N_k / N; mu_k = S1_k / N_k; sigma^2_k = max((Q_k / N_k - ||mu_k||^2) / D, floor);
+// components with N_k < 1e-6 keep mean and variance
+__global__ void k_mstep_iso(const double* __restrict__ Nk, const double* __restrict__ S1,
+                            const double* __restrict__ Q, double n_total, float floor_, float* w, float* mu,
+                            float* var_iso, int K, int D, int* flags) {
+  const int k = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x & 63;
+  if (k >= K) return;
+  const double nk = Nk[k];
+  if (lane == 0) {
+    w[k] = (float)(nk / n_total);
+    if (!isfinite(nk)) flags[0] = 1;
+  }
+  if (!(nk >= 1e-6)) return;
+  double mm = 0.0;
+  for (int d = lane; d < D; d += kWave) {
+    const double m = S1[(size_t)k * D + d] / nk;
+    mu[(size_t)k * D + d] = (float)m;
+    mm += m * m;
+  }
+  mm = wave_sum64(mm);
+  if (lane == 0) var_iso[k] = (float)fmax((Q[k] / nk - mm) / D, (double)floor_);
+}
+
+// init: every component's variance is the mean over d of the per-dimension
+// population variances, floored
+__global__ void k_iso_init_var(const double* __restrict__ colvar, int D, float floor_, float* var_iso, int K) {
+  __shared__ double tot;
+  if (threadIdx.x < kWave) {
+    double t = 0.0;
+    for (int d = threadIdx.x; d < D; d += kWave) t += colvar[d];
+    t = wave_sum64(t);
+    if (threadIdx.x == 0) tot = t;
+  }
+  __syncthreads();
+  const float v = (float)fmax(tot / D, (double)floor_);
+  for (int k = threadIdx.x; k < K; k += blockDim.x) var_iso[k] = v;
+}
+
+// ---------------------------------------------------------------------------
 // Initialisation: column sums (pass 0) or squared deviations (pass 1) of row
 // blocks in float64, then a pairwise tree over blocks.
 // Column sums of X over a row range per workgroup (init: the global
@@ -925,6 +993,7 @@ size_t workspace_bytes(const Plan& p) {
   b += 2 * up((size_t)p.Kpad * 8) + up(8);
   b += up((size_t)p.Kpad * p.Dp * 16) + up((size_t)p.Kpad * 8) + up(8);
   b += up((size_t)p.Kpad * 2 * p.Dp * 8) + up((size_t)p.Kpad * 8);  // wop64, cvec64
+  b += up((size_t)p.K * p.D * 4) + up((size_t)p.K * 8);  // isotropic: broadcast variances, Q
   b += up((size_t)p.R * p.Kpad * p.SR * 8);
   b += up((size_t)(p.R > p.Glogz ? p.R : p.Glogz) * 8);
   b += up((size_t)p.chunk * 4);
@@ -1085,6 +1154,41 @@ hipError_t launch_mstep(const Plan& p, const Workspace& w, const double* Nk, con
   const size_t total = (size_t)p.K * p.D;
   hipLaunchKernelGGL(k_mstep, dim3(grid_for(total, 256)), dim3(256), 0, s, Nk, S1, S2, n_total, var_floor,
                      weights, means, vars, p.K, p.D, w.flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_iso_expand(const Plan& p, const Workspace& w, const float* var_iso, hipStream_t s) {
+  const size_t total = (size_t)p.K * p.D;
+  hipLaunchKernelGGL(k_iso_expand, dim3(grid_for(total, 256)), dim3(256), 0, s, var_iso, w.vexp, p.K, p.D);
+  return hipGetLastError();
+}
+
+hipError_t launch_iso_q(const Plan& p, const double* S2, double* Q, int accumulate, hipStream_t s) {
+  hipLaunchKernelGGL(k_iso_q, dim3((p.K + 3) / 4), dim3(256), 0, s, S2, Q, p.K, p.D, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_mstep_iso(const Plan& p, const Workspace& w, const double* Nk, const double* S1, const double* Q,
+                            double n_total, float var_floor, float* weights, float* means, float* var_iso,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(k_mstep_iso, dim3((p.K + 3) / 4), dim3(256), 0, s, Nk, S1, Q, n_total, var_floor, weights,
+                     means, var_iso, p.K, p.D, w.flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_init_iso(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx,
+                           float var_floor, float* weights, float* means, float* var_iso, hipStream_t s) {
+  // the diagonal initialisation leaves the per-dimension variances (before
+  // the floor) in the statistics scratch; its K x D variances go to vexp
+  hipError_t e = launch_init(p, w, X, N, ldx, var_floor, weights, means, w.vexp, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_iso_init_var, dim3(1), dim3(256), 0, s, (const double*)w.stats, p.D, var_floor, var_iso,
+                     p.K);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(double* p, size_t n, hipStream_t s) {
+  hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(n, 256)), dim3(256), 0, s, (unsigned long long*)p, n);
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ Mixture laws (parameters of the *generating* distribution, float64 numpy):
   ivf    N=1e7 base D=128  K=16384  integer values 0..255 stored as fp32: clipped,
                                     rounded Gaussians around 1024 super-centres with
                                     16 sub-centres each
+  iso    N=1e8      D=128  K=1024   the mid law with one std per component (isotropic)
 Parameters are drawn from numpy ``default_rng(seed)`` in the order
 means -> stds -> weights.  Rows are drawn in fixed chunks of ``CHUNK`` rows;
 chunk ``c`` uses a torch generator seeded from ``(seed, stream, c)``, so any
@@ -49,6 +50,8 @@ WORKLOADS = {
     "mid": Workload("mid", 1_000_000, 128, 1024, 30, 1e-6, "mid"),
     "large": Workload("large", 100_000_000, 128, 1024, 30, 1e-6, "mid"),
     "embed": Workload("embed", 10_000_000, 768, 4096, 20, 1e-5, "embed"),
+    # the pages' isotropic model at the large size
+    "iso": Workload("iso", 100_000_000, 128, 1024, 30, 1e-6, "iso"),
     # ivf: EM on a 1e6-row sample, then soft assignment of the 1e7-row base.
     "ivf": Workload("ivf", 10_000_000, 128, 16384, 10, 1.0 / 12.0, "ivf",
                     extra={"train_rows": 1_000_000, "queries": 10_000,
@@ -84,6 +87,12 @@ def mixture(law: str, D: int, K: int, seed: int = 0) -> Mixture:
     elif law == "mid":
         means = rng.normal(0.0, 4.0, (K, D))
         stds = rng.uniform(0.5, 1.5, (K, D))
+        weights = rng.dirichlet(2.0 * np.ones(K))
+    elif law == "iso":
+        # the mid law with one standard deviation per component (the pages'
+        # isotropic model, Sigma_k = sigma_k^2 I)
+        means = rng.normal(0.0, 4.0, (K, D))
+        stds = np.repeat(rng.uniform(0.5, 1.5, (K, 1)), D, axis=1)
         weights = rng.dirichlet(2.0 * np.ones(K))
     elif law == "embed":
         c = rng.normal(size=(K, D))
