@@ -30,6 +30,7 @@ WORKLOAD_TEXT = {
     "tiny": "tiny EM: N=10,000, D=8, K=16, fp32, diagonal covariance, 10 EM iterations",
     "embed": "embedding-like EM: N=10,000,000, D=768, K=4096, fp32, diagonal covariance, 20 EM iterations",
     "iso": "isotropic EM (sigma_k^2 I): N=100,000,000, D=128, K=1024, fp32, 30 EM iterations",
+    "kmeans": "k-means warm start: Lloyd iterations at N=100,000,000, D=128, K=1024 (the large data), fp32",
     "ivf": "IVF: EM on a 1,000,000-row sample, D=128, K=16384, integer values 0..255, 10 EM iterations; "
            "then soft assignment (argmax + up to 3 with r >= 0.1) of 10,000,000 base rows into CSR lists",
 }
@@ -115,6 +116,44 @@ def cpu_baseline(workload, sample_rows, budget_s):
             "torch_threads": torch.get_num_threads()}
 
 
+def bench_kmeans(args):
+    """Lloyd iterations of the k-means warm start on the large data set: each
+    assigns every row to its nearest centre (two logit sweeps of the
+    soft-assignment kernels, counting then placing the CSR lists) and moves
+    the centres (one gather pass over X)."""
+    import torch
+    from soft_clustering_amd import GMM, datagen
+    wl = datagen.WORKLOADS["large"]
+    N = args.rows or wl.N
+    K, D = wl.K, wl.D
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    mix = datagen.mixture(wl.law, D, K, seed=wl.seed)
+    X = torch.empty(N, D, dtype=torch.float32, device=dev)
+    datagen.sample_into(X, mix, 0, seed=wl.seed)
+    rows = torch.as_tensor(datagen.init_rows(N, K, seed=wl.init_seed), device=dev)
+    c = X[rows].contiguous()
+    g = GMM(K, D, dev)
+    if args.warmup > 0:
+        g.kmeans(X, c, args.warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _, counts, _, _ = g.kmeans(X, c, args.steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt * 1e3 / args.steps
+    useful = 2.0 * N * K * D  # the x.c products of the distances
+    line = {"metric": "ms per Lloyd iteration (k-means warm start)", "value": round(ms, 3), "unit": "ms",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+            "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic (seeded mixture, generated on the GPU)",
+            "config": {"workload": WORKLOAD_TEXT["kmeans"], "N": N, "K": K, "D": D},
+            "distance_tflops": round(useful / (dt / args.steps) / 1e12, 2),
+            "issued_logit_tflops": round(2 * 4.0 * N * K * D / (dt / args.steps) / 1e12, 2),
+            "empty_clusters": int((counts == 0).sum().item())}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +179,8 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.workload == "kmeans":
+        return bench_kmeans(args)
     if args.copy_calibration > 0:
         n = int(args.copy_calibration * (1 << 30)) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")

@@ -182,6 +182,31 @@ gmm_status gmm_fit_iso(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_
                        float var_floor, float *weights, float *means, float *var_iso /*[dev] in/out*/,
                        double *loglik_hist /*[dev] T*/);
 
+/* k-means warm start.  The pages seed their mixtures with k-means (the set-up
+ * of the IVF experiments); the algorithm is Lloyd's: every row goes to its
+ * nearest centre in squared Euclidean distance (lowest index on ties, the
+ * comparison exact in float64 near ties), then every centre moves to the
+ * mean of its rows; a centre with no rows keeps its position.  Centres are
+ * float32 [dev] K x D, updated in place over iters iterations; counts [dev]
+ * float64[K] receives the list sizes of the last assignment.  list_offsets
+ * [dev] int64[K+1] and list_ids [dev] int32[N] are caller-owned scratch that
+ * holds the last assignment as CSR lists (row ids ascending in each list).
+ * The sums run in list order: deterministic.  N < 2^31.  Synchronises. */
+gmm_status gmm_kmeans(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_t ldx, int32_t iters,
+                      float *centres /*[dev] K*D in/out*/, double *counts /*[dev] K*/,
+                      int64_t *list_offsets /*[dev] K+1*/, int32_t *list_ids /*[dev] N*/);
+
+/* Mixture seeded from a clustering: one assignment of the rows to the given
+ * centres, then weights_k = n_k / N, means_k = centres_k and the variances of
+ * each cluster's rows about its centre, per dimension (vars K x D) or
+ * averaged over the dimensions when isotropic = 1 (vars K); an empty cluster
+ * gets the variance of all rows; variances floored by var_floor.  Scratch and
+ * synchronisation as gmm_kmeans. */
+gmm_status gmm_init_kmeans(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_t ldx,
+                           const float *centres /*[dev] K*D*/, float var_floor, int32_t isotropic,
+                           float *weights /*[dev] K*/, float *means /*[dev] K*D*/, float *vars /*[dev]*/,
+                           int64_t *list_offsets /*[dev] K+1*/, int32_t *list_ids /*[dev] N*/);
+
 /* Inverted lists of a soft assignment (Section 4.2 argmax assignment and the
  * Section 4.3 multi-assignment, with the threshold and count rule below):
  * each row goes to its highest-responsibility component (lowest index on

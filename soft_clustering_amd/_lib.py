@@ -24,7 +24,7 @@ PREC_REFINED, PREC_FP32, PREC_FP64 = 0, 1, 2
 
 EXPORTS = ["gmm_create", "gmm_destroy", "gmm_last_error", "gmm_workspace_bytes", "gmm_set_path", "gmm_set_precision",
            "gmm_init", "gmm_estep_stats", "gmm_mstep", "gmm_fit", "gmm_soft_assign", "gmm_check",
-           "gmm_init_iso", "gmm_estep_stats_iso", "gmm_mstep_iso", "gmm_fit_iso",
+           "gmm_init_iso", "gmm_estep_stats_iso", "gmm_mstep_iso", "gmm_fit_iso", "gmm_kmeans", "gmm_init_kmeans",
            "gmm_profile", "gmm_profile_read", "gmm_refine_stats"]
 
 
@@ -54,6 +54,8 @@ def _load():
         "gmm_estep_stats_iso": (i32, [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32]),
         "gmm_mstep_iso": (i32, [vp, vp, vp, vp, f64, f32, vp, vp, vp]),
         "gmm_fit_iso": (i32, [vp, vp, i64, i64, i32, f32, vp, vp, vp, vp]),
+        "gmm_kmeans": (i32, [vp, vp, i64, i64, i32, vp, vp, vp, vp]),
+        "gmm_init_kmeans": (i32, [vp, vp, i64, i64, vp, f32, i32, vp, vp, vp, vp, vp]),
         "gmm_soft_assign": (i32, [vp, vp, i64, i64, vp, vp, vp, f32, i32, vp, vp, i64, vp]),
         "gmm_check": (i32, [vp]),
         "gmm_profile": (i32, [vp, i32]),
@@ -274,6 +276,37 @@ class GMM:
             self._check(_lib.gmm_fit_iso(self._h, _ptr(X), N, ldx, int(T), float(var_floor), _ptr(w), _ptr(mu),
                                          _ptr(var_iso), _ptr(ll_hist)))
         return w, mu, var_iso, ll_hist
+
+    # ---- k-means warm start
+    def _list_scratch(self, N):
+        return (torch.empty(self.K + 1, dtype=torch.int64, device=self.device),
+                torch.empty(max(N, 1), dtype=torch.int32, device=self.device))
+
+    def kmeans(self, X, centres, iters):
+        """Lloyd iterations in place on centres (K x D float32); returns
+        (centres, counts float64[K], offsets, ids) of the last assignment."""
+        N, ldx = _rows(X, self.D, self.device)
+        _need(centres, torch.float32, (self.K, self.D), "centres", self.device)
+        counts = torch.zeros(self.K, dtype=torch.float64, device=self.device)
+        offsets, ids = self._list_scratch(N)
+        with torch.cuda.device(self.device):
+            self._check(_lib.gmm_kmeans(self._h, _ptr(X), N, ldx, int(iters), _ptr(centres), _ptr(counts),
+                                        _ptr(offsets), _ptr(ids)))
+        return centres, counts, offsets, ids[:N]
+
+    def init_kmeans(self, X, centres, var_floor, isotropic=False):
+        """(weights, means, vars) of the mixture seeded from the clustering."""
+        N, ldx = _rows(X, self.D, self.device)
+        _need(centres, torch.float32, (self.K, self.D), "centres", self.device)
+        w, mu, var = self.params()
+        if isotropic:
+            var = torch.empty(self.K, dtype=torch.float32, device=self.device)
+        offsets, ids = self._list_scratch(N)
+        with torch.cuda.device(self.device):
+            self._check(_lib.gmm_init_kmeans(self._h, _ptr(X), N, ldx, _ptr(centres), float(var_floor),
+                                             int(bool(isotropic)), _ptr(w), _ptr(mu), _ptr(var), _ptr(offsets),
+                                             _ptr(ids)))
+        return w, mu, var
 
     def soft_assign(self, X, w, mu, var, threshold=0.1, max_extra=3, ids_capacity=None):
         """CSR inverted lists: (offsets int64[K+1], ids int32[nnz])."""

@@ -135,6 +135,10 @@ gmm_status estep_into(gmm_ctx* c, const float* X, int64_t N, int64_t ldx, const 
   return GMM_OK;
 }
 
+gmm_status soft_assign_run(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, const float* weights,
+                           const float* means, const float* vars, float threshold, int32_t max_extra,
+                           int64_t* list_offsets, int32_t* list_ids, int64_t ids_capacity, int64_t* nnz);
+
 }  // namespace
 
 extern "C" {
@@ -201,6 +205,7 @@ gmm_status gmm_create(gmm_ctx** out, int32_t K, int32_t D, void* hip_stream) {
   c->ws.w64 = carve<double2>(q, (size_t)p.Kpad * p.Dp);
   c->ws.vexp = carve<float>(q, (size_t)p.K * p.D);
   c->ws.qiso = carve<double>(q, p.K);
+  c->ws.wuni = carve<float>(q, p.K);
   c->ws.wop64 = carve<double>(q, (size_t)p.Kpad * 2 * p.Dp);
   c->ws.cvec64 = carve<double>(q, p.Kpad);
   c->ws.f64 = 0;
@@ -486,6 +491,18 @@ gmm_status gmm_soft_assign(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx,
   if (ids_capacity < 0) return fail(ctx, GMM_ERR_INVALID_ARG, "ids_capacity must be >= 0");
   if (ids_capacity > 0 && !list_ids) return fail(ctx, GMM_ERR_INVALID_ARG, "list_ids is NULL");
   if (N >= ((int64_t)1 << 31)) return fail(ctx, GMM_ERR_INVALID_ARG, "N must be < 2^31 for int32 ids");
+  return soft_assign_run(ctx, X, N, ldx, weights, means, vars, threshold, max_extra, list_offsets, list_ids,
+                         ids_capacity, nnz);
+}
+
+}  // extern "C"
+
+namespace {
+
+// the soft assignment after argument checks (also the k-means assignment)
+gmm_status soft_assign_run(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, const float* weights,
+                           const float* means, const float* vars, float threshold, int32_t max_extra,
+                           int64_t* list_offsets, int32_t* list_ids, int64_t ids_capacity, int64_t* nnz) {
   const gmm::Plan& p = ctx->plan;
   if (p.occAssign < 1) return fail(ctx, GMM_ERR_UNSUPPORTED, "no soft-assignment kernel for this context's shape");
   hipStream_t s = ctx->stream;
@@ -523,6 +540,70 @@ gmm_status gmm_soft_assign(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx,
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(ctx, e, "soft assignment");
   return gmm_check(ctx);
+}
+
+// k-means helpers: assignment of every row to its nearest centre (CSR)
+gmm_status kmeans_assign(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, const float* centres,
+                         int64_t* offsets, int32_t* ids) {
+  hipError_t e = gmm::launch_kmeans_params(ctx->plan, ctx->ws, centres, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "k-means set-up");
+  int64_t nnz = 0;
+  return soft_assign_run(ctx, X, N, ldx, ctx->ws.wuni, centres, ctx->ws.vexp, 1.0f, 0, offsets, ids, N, &nnz);
+}
+
+gmm_status kmeans_check(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, const float* centres,
+                        const int64_t* offsets, const int32_t* ids) {
+  gmm_status st = check_x(ctx, X, N, ldx);
+  if (st) return st;
+  if (!centres || !aligned16(centres)) return fail(ctx, GMM_ERR_INVALID_ARG, "centres must be non-NULL, 16-byte aligned");
+  if (!offsets || !ids) return fail(ctx, GMM_ERR_INVALID_ARG, "list scratch must be non-NULL");
+  if (N >= ((int64_t)1 << 31)) return fail(ctx, GMM_ERR_INVALID_ARG, "N must be < 2^31 for int32 ids");
+  return GMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gmm_status gmm_kmeans(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, int32_t iters, float* centres,
+                      double* counts, int64_t* list_offsets, int32_t* list_ids) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  gmm_status st = kmeans_check(ctx, X, N, ldx, centres, list_offsets, list_ids);
+  if (st) return st;
+  if (iters < 1) return fail(ctx, GMM_ERR_INVALID_ARG, "iters must be >= 1");
+  if (!counts) return fail(ctx, GMM_ERR_INVALID_ARG, "counts is NULL");
+  for (int it = 0; it < iters; ++it) {
+    st = kmeans_assign(ctx, X, N, ldx, centres, list_offsets, list_ids);
+    if (st) return st;
+    hipError_t e = gmm::launch_centroids(ctx->plan, ctx->ws, X, N, ldx, list_offsets, list_ids, centres, counts, 0,
+                                         1.f, 0, nullptr, nullptr, nullptr, ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "centroid update");
+  }
+  hipError_t e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "k-means");
+  return GMM_OK;
+}
+
+gmm_status gmm_init_kmeans(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, const float* centres,
+                           float var_floor, int32_t isotropic, float* weights, float* means, float* vars,
+                           int64_t* list_offsets, int32_t* list_ids) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  gmm_status st = kmeans_check(ctx, X, N, ldx, centres, list_offsets, list_ids);
+  if (st) return st;
+  st = check_params(ctx, weights, means, vars);
+  if (st) return st;
+  if (isotropic != 0 && isotropic != 1) return fail(ctx, GMM_ERR_INVALID_ARG, "isotropic must be 0 or 1");
+  if (!(var_floor > 0.f) || !isfinite(var_floor)) return fail(ctx, GMM_ERR_INVALID_ARG, "var_floor must be > 0");
+  hipError_t e = gmm::launch_colvar(ctx->plan, ctx->ws, X, N, ldx, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "column variances");
+  st = kmeans_assign(ctx, X, N, ldx, centres, list_offsets, list_ids);
+  if (st) return st;
+  e = gmm::launch_centroids(ctx->plan, ctx->ws, X, N, ldx, list_offsets, list_ids, const_cast<float*>(centres),
+                            nullptr, 1, var_floor, isotropic, weights, means, vars, ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "mixture from clusters");
+  e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) return hip_fail(ctx, e, "init from k-means");
+  return GMM_OK;
 }
 
 gmm_status gmm_refine_stats(gmm_ctx* ctx, int64_t* refined, double* logits) {

@@ -62,6 +62,7 @@ struct Workspace {
   int* flags;        // [0] numeric fault, [1] exchange timeout, [2] list overflow
   float* vexp;       // K * D  isotropic variances broadcast over the dimensions
   double* qiso;      // K      isotropic Q_k of gmm_fit_iso
+  float* wuni;       // K      k-means: equal weights
   int colG;
   // soft assignment
   int32_t* asel;                 // assignChunk * 9  per-row selections
@@ -102,6 +103,11 @@ hipError_t launch_mstep_iso(const Plan& p, const Workspace& w, const double* Nk,
 hipError_t launch_init_iso(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx,
                            float var_floor, float* weights, float* means, float* var_iso, hipStream_t s);
 hipError_t launch_fill_zero(double* p, size_t n, hipStream_t s);
+hipError_t launch_kmeans_params(const Plan& p, const Workspace& w, const float* centres, hipStream_t s);
+hipError_t launch_centroids(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx,
+                            const int64_t* offsets, const int32_t* ids, float* centres, double* counts, int mode,
+                            float var_floor, int iso, float* weights, float* means, float* vars, hipStream_t s);
+hipError_t launch_colvar(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx, hipStream_t s);
 hipError_t launch_mstep(const Plan& p, const Workspace& w, const double* Nk, const double* S1,
                         const double* S2, double n_total, float var_floor, float* weights,
                         float* means, float* vars, hipStream_t s);

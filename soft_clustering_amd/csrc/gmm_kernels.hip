@@ -802,6 +802,78 @@ __global__ void k_iso_init_var(const double* __restrict__ colvar, int D, float f
 }
 
 // ---------------------------------------------------------------------------
+// k-means warm start (Lloyd's algorithm; the pages seed their mixtures with
+// k-means).  Rows are assigned to their nearest centre by the soft-assignment
+// kernels (argmax of the logits with equal weights and variances 1/2, which
+// is the argmin of the squared distance, float64-exact near ties, lowest
+// index on ties) into CSR lists; one workgroup per centre then sums its
+// list's rows in list order (row ids ascending), so the result is
+// deterministic.
+//   mode 0: centres_k = mean of its rows (an empty list keeps its centre),
+//           counts_k = its size;
+//   mode 1: the mixture seeded from the clustering: weights_k = n_k / N,
+//           means_k = centres_k, vars = population variance of the rows
+//           about the centre (colvar, the variance of all rows, for an empty
+//           list), averaged over the dimensions when iso, floored.
+__global__ void k_fill_f32(float* __restrict__ p, size_t n, float v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+__global__ void __launch_bounds__(256) k_centroids(const float* __restrict__ X, int64_t ldx,
+                                                   const int64_t* __restrict__ offsets,
+                                                   const int32_t* __restrict__ ids, int D, float* centres,
+                                                   double* counts, int mode, const double* __restrict__ colvar,
+                                                   float floor_, int64_t N, int iso, float* weights, float* means,
+                                                   float* vars) {
+  __shared__ double red[256];
+  const int k = blockIdx.x;
+  const int64_t b = offsets[k], e = offsets[k + 1];
+  const int64_t n = e - b;
+  double tsum = 0.0;  // iso: this thread's dims' variances
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    const double c = (double)centres[(size_t)k * D + d];
+    double acc = 0.0;
+    int64_t i = b;
+    // eight rows' loads in flight, added in list order
+    for (; i + 8 <= e; i += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = X[(int64_t)ids[i + u] * ldx + d];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const double x = (double)v[u];
+        acc += (mode == 0) ? x : (x - c) * (x - c);
+      }
+    }
+    for (; i < e; ++i) {
+      const double x = (double)X[(int64_t)ids[i] * ldx + d];
+      acc += (mode == 0) ? x : (x - c) * (x - c);
+    }
+    if (mode == 0) {
+      if (n > 0) centres[(size_t)k * D + d] = (float)(acc / (double)n);
+    } else {
+      const double var = (n > 0) ? acc / (double)n : colvar[d];
+      means[(size_t)k * D + d] = (float)c;
+      if (!iso) vars[(size_t)k * D + d] = (float)fmax(var, (double)floor_);
+      tsum += var;
+    }
+  }
+  if (threadIdx.x == 0) {
+    if (mode == 0) counts[k] = (double)n;
+    else weights[k] = (float)((double)n / (double)N);
+  }
+  if (mode == 1 && iso) {
+    red[threadIdx.x] = tsum;
+    __syncthreads();
+    for (int st = blockDim.x / 2; st > 0; st >>= 1) {
+      if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) vars[k] = (float)fmax(red[0] / D, (double)floor_);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Initialisation: column sums (pass 0) or squared deviations (pass 1) of row
 // blocks in float64, then a pairwise tree over blocks.
 // Column sums of X over a row range per workgroup (init: the global
@@ -994,6 +1066,7 @@ size_t workspace_bytes(const Plan& p) {
   b += up((size_t)p.Kpad * p.Dp * 16) + up((size_t)p.Kpad * 8) + up(8);
   b += up((size_t)p.Kpad * 2 * p.Dp * 8) + up((size_t)p.Kpad * 8);  // wop64, cvec64
   b += up((size_t)p.K * p.D * 4) + up((size_t)p.K * 8);  // isotropic: broadcast variances, Q
+  b += up((size_t)p.K * 4);  // k-means: equal weights
   b += up((size_t)p.R * p.Kpad * p.SR * 8);
   b += up((size_t)(p.R > p.Glogz ? p.R : p.Glogz) * 8);
   b += up((size_t)p.chunk * 4);
@@ -1189,6 +1262,36 @@ hipError_t launch_init_iso(const Plan& p, const Workspace& w, const float* X, in
 
 hipError_t launch_fill_zero(double* p, size_t n, hipStream_t s) {
   hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(n, 256)), dim3(256), 0, s, (unsigned long long*)p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_kmeans_params(const Plan& p, const Workspace& w, const float* centres, hipStream_t s) {
+  // equal weights and variances 1/2: the logit of centre k is a constant
+  // minus the squared distance to it
+  hipLaunchKernelGGL(k_fill_f32, dim3(grid_for((size_t)p.K, 256)), dim3(256), 0, s, w.wuni, (size_t)p.K,
+                     1.0f / (float)p.K);
+  hipLaunchKernelGGL(k_fill_f32, dim3(grid_for((size_t)p.K * p.D, 256)), dim3(256), 0, s, w.vexp,
+                     (size_t)p.K * p.D, 0.5f);
+  return hipGetLastError();
+}
+
+hipError_t launch_centroids(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx,
+                            const int64_t* offsets, const int32_t* ids, float* centres, double* counts, int mode,
+                            float var_floor, int iso, float* weights, float* means, float* vars, hipStream_t s) {
+  hipLaunchKernelGGL(k_centroids, dim3(p.K), dim3(256), 0, s, X, ldx, offsets, ids, p.D, centres, counts, mode,
+                     (const double*)w.stats, var_floor, N, iso, weights, means, vars);
+  return hipGetLastError();
+}
+
+hipError_t launch_colvar(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx, hipStream_t s) {
+  const int nb = (int)((N < (int64_t)w.colG) ? N : (int64_t)w.colG);
+  hipLaunchKernelGGL(k_colpart, dim3(nb), dim3(256), 0, s, X, N, ldx, p.D, (const double*)nullptr, w.colpart, 0);
+  hipLaunchKernelGGL(k_colfinal, dim3((p.D + 255) / 256), dim3(256), 0, s, w.colpart, nb, p.D, (double)N,
+                     w.colmean);
+  hipLaunchKernelGGL(k_colpart, dim3(nb), dim3(256), 0, s, X, N, ldx, p.D, (const double*)w.colmean, w.colpart,
+                     1);
+  hipLaunchKernelGGL(k_colfinal, dim3((p.D + 255) / 256), dim3(256), 0, s, w.colpart, nb, p.D, (double)N,
+                     w.stats);
   return hipGetLastError();
 }
 

@@ -1,0 +1,112 @@
+"""k-means warm start on the HIP path against the float64 Lloyd oracle
+through the C ABI: one Lloyd iteration at a time from the same centres (the
+CSR assignment must match the oracle's argmin on every row that is not a
+near-tie, the centres to float32 rounding), the mixture seeded from the
+clustering, determinism, and ten iterations end to end."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.kmeans_oracle as KM
+from soft_clustering_amd import datagen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+# name: (law, N, D, K, ldx)
+CASES = {
+    "tiny": ("tiny", 10_000, 8, 16, None),
+    "odd_d5_k7": ("tiny", 1_003, 5, 7, 8),
+    "mid_prefix": ("mid", 20_037, 128, 1024, None),
+}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def data(name):
+    law, N, D, K, ldx = CASES[name]
+    mix = datagen.mixture(law, D, K, seed=0)
+    Xc = datagen.sample(mix, N, seed=0, ldx=ldx)
+    Xn = Xc.contiguous().numpy()
+    rows = datagen.init_rows(N, K, seed=1)
+    c0 = Xn[rows].astype(np.float32)
+    if ldx is not None:
+        buf = torch.full((N, ldx), float("nan"), dtype=torch.float32)
+        buf[:, :D] = Xc
+        Xg = buf.to(DEV)[:, :D]
+    else:
+        Xg = Xc.to(DEV)
+    return Xn, Xg, c0
+
+
+def csr_assignment(offsets, ids, N):
+    off = offsets.cpu().numpy()
+    ids = ids.cpu().numpy()
+    a = np.full(N, -1, np.int64)
+    for k in range(off.shape[0] - 1):
+        seg = ids[off[k]:off[k + 1]]
+        assert np.all(np.diff(seg) > 0), "ids ascending within a list"
+        a[seg] = k
+    assert np.all(a >= 0), "every row in exactly one list"
+    return a
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_kmeans_lloyd_step_parity(name):
+    from soft_clustering_amd import GMM
+    Xn, Xg, c0 = data(name)
+    N, D = Xn.shape
+    K = c0.shape[0]
+    log(f"[kmeans] case={name} N={N} D={D} K={K}")
+    g = GMM(K, D)
+    c = torch.as_tensor(c0).to(DEV)
+    for it in range(3):
+        cin = c.cpu().numpy().copy()
+        _, counts, offsets, ids = g.kmeans(Xg, c, 1)
+        a_gpu = csr_assignment(offsets, ids, N)
+        a_ref, two = KM.assign(Xn, cin)
+        tie = (two[:, 1] - two[:, 0]) <= 1e-9 * np.maximum(np.abs(two[:, 0]), 1.0)
+        bad = (a_gpu != a_ref) & ~tie
+        assert not np.any(bad), f"iteration {it}: {int(bad.sum())} rows assigned differently, e.g. row {np.argmax(bad)}"
+        cnt, want = KM.update(Xn, a_gpu, cin)  # the oracle's update of the GPU's own assignment
+        np.testing.assert_array_equal(counts.cpu().numpy(), cnt)
+        np.testing.assert_allclose(c.cpu().numpy(), want.astype(np.float32), rtol=2e-7, atol=1e-6)
+
+
+def test_kmeans_end_to_end_and_deterministic():
+    from soft_clustering_amd import GMM
+    Xn, Xg, c0 = data("tiny")
+    K, D = c0.shape
+    g = GMM(K, D)
+    out = []
+    for _ in range(2):
+        c = torch.as_tensor(c0).to(DEV)
+        _, counts, _, _ = g.kmeans(Xg, c, 10)
+        out.append((c.clone(), counts.clone()))
+    assert torch.equal(out[0][0], out[1][0]) and torch.equal(out[0][1], out[1][1])
+    cref, cnt, _ = KM.lloyd(Xn, c0, 10)
+    np.testing.assert_allclose(out[0][0].cpu().numpy(), cref, rtol=1e-5, atol=1e-5)
+    np.testing.assert_array_equal(out[0][1].cpu().numpy(), cnt)
+
+
+@pytest.mark.parametrize("isotropic", [False, True])
+@pytest.mark.parametrize("name", ["tiny", "mid_prefix"])
+def test_init_from_kmeans(name, isotropic):
+    from soft_clustering_amd import GMM
+    Xn, Xg, c0 = data(name)
+    N = Xn.shape[0]
+    K, D = c0.shape
+    g = GMM(K, D)
+    c = torch.as_tensor(c0).to(DEV)
+    g.kmeans(Xg, c, 3)
+    cen = c.cpu().numpy()
+    w, mu, v = g.init_kmeans(Xg, c, 1e-6, isotropic=isotropic)
+    rw, rmu, rv = KM.mixture_from_clusters(Xn, cen, 1e-6, isotropic=isotropic)
+    np.testing.assert_array_equal(w.cpu().numpy(), rw.astype(np.float32))
+    np.testing.assert_array_equal(mu.cpu().numpy(), cen)
+    np.testing.assert_allclose(v.cpu().numpy(), rv.astype(np.float32), rtol=2e-6)
