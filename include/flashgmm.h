@@ -182,6 +182,26 @@ gmm_status gmm_fit_iso(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_
                        float var_floor, float *weights, float *means, float *var_iso /*[dev] in/out*/,
                        double *loglik_hist /*[dev] T*/);
 
+/* Out-of-core E-step and fit: X_host is a HOST array of N rows (row stride
+ * ldx floats), pinned (hipHostMalloc) for the copies to overlap the compute,
+ * pageable also accepted.  Rows go to the device in chunks of chunk_rows
+ * through two device staging buffers that the context allocates on first use
+ * (2 x chunk_rows x D floats, kept until gmm_destroy): the copy of chunk i+1
+ * runs on a copy stream of the context while the E-step of chunk i runs on
+ * the context's stream.  The statistics are those of gmm_estep_stats with
+ * accumulate = 1 over the same row ranges (bit-identical), and gmm_fit_host
+ * is gmm_fit on them.  Everything else (outputs, errors, no host
+ * synchronisation) as gmm_estep_stats / gmm_fit; X_host must stay valid until
+ * the context's stream has synchronised.  This is the pages' route to data
+ * sets larger than device memory (N >= 1e9). */
+gmm_status gmm_estep_stats_host(gmm_ctx *ctx, const float *X_host /*[host]*/, int64_t N, int64_t ldx,
+                                const float *weights, const float *means, const float *vars /*[dev]*/,
+                                double *Nk /*[dev] K*/, double *S1 /*[dev] K*D*/, double *S2 /*[dev] K*D*/,
+                                double *loglik /*[dev] 1*/, int32_t accumulate, int64_t chunk_rows);
+gmm_status gmm_fit_host(gmm_ctx *ctx, const float *X_host /*[host]*/, int64_t N, int64_t ldx, int32_t T,
+                        float var_floor, float *weights, float *means, float *vars /*[dev] in/out*/,
+                        double *loglik_hist /*[dev] T*/, int64_t chunk_rows);
+
 /* k-means warm start.  The pages seed their mixtures with k-means (the set-up
  * of the IVF experiments); the algorithm is Lloyd's: every row goes to its
  * nearest centre in squared Euclidean distance (lowest index on ties, the

@@ -25,6 +25,7 @@ PREC_REFINED, PREC_FP32, PREC_FP64 = 0, 1, 2
 EXPORTS = ["gmm_create", "gmm_destroy", "gmm_last_error", "gmm_workspace_bytes", "gmm_set_path", "gmm_set_precision",
            "gmm_init", "gmm_estep_stats", "gmm_mstep", "gmm_fit", "gmm_soft_assign", "gmm_check",
            "gmm_init_iso", "gmm_estep_stats_iso", "gmm_mstep_iso", "gmm_fit_iso", "gmm_kmeans", "gmm_init_kmeans",
+           "gmm_estep_stats_host", "gmm_fit_host",
            "gmm_profile", "gmm_profile_read", "gmm_refine_stats"]
 
 
@@ -55,6 +56,8 @@ def _load():
         "gmm_mstep_iso": (i32, [vp, vp, vp, vp, f64, f32, vp, vp, vp]),
         "gmm_fit_iso": (i32, [vp, vp, i64, i64, i32, f32, vp, vp, vp, vp]),
         "gmm_kmeans": (i32, [vp, vp, i64, i64, i32, vp, vp, vp, vp]),
+        "gmm_estep_stats_host": (i32, [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, i64]),
+        "gmm_fit_host": (i32, [vp, vp, i64, i64, i32, f32, vp, vp, vp, vp, i64]),
         "gmm_init_kmeans": (i32, [vp, vp, i64, i64, vp, f32, i32, vp, vp, vp, vp, vp]),
         "gmm_soft_assign": (i32, [vp, vp, i64, i64, vp, vp, vp, f32, i32, vp, vp, i64, vp]),
         "gmm_check": (i32, [vp]),
@@ -276,6 +279,40 @@ class GMM:
             self._check(_lib.gmm_fit_iso(self._h, _ptr(X), N, ldx, int(T), float(var_floor), _ptr(w), _ptr(mu),
                                          _ptr(var_iso), _ptr(ll_hist)))
         return w, mu, var_iso, ll_hist
+
+    # ---- out-of-core: X in host memory (a CPU tensor, pinned for overlap)
+    def _host_rows(self, X):
+        if not isinstance(X, torch.Tensor) or X.device.type != "cpu" or X.dtype != torch.float32:
+            raise TypeError("X must be a float32 CPU tensor")
+        if X.dim() != 2 or X.shape[1] != self.D or X.stride(1) != 1:
+            raise ValueError(f"X must be N x {self.D} with unit column stride")
+        return X.shape[0], X.stride(0)
+
+    def estep_stats_host(self, X, w, mu, var, chunk_rows, out=None, accumulate=False):
+        N, ldx = self._host_rows(X)
+        self._params(w, mu, var)
+        K, D = self.K, self.D
+        if out is None:
+            out = (torch.zeros(K, dtype=torch.float64, device=self.device),
+                   torch.zeros(K, D, dtype=torch.float64, device=self.device),
+                   torch.zeros(K, D, dtype=torch.float64, device=self.device),
+                   torch.zeros(1, dtype=torch.float64, device=self.device))
+        Nk, S1, S2, ll = out
+        with torch.cuda.device(self.device):
+            self._check(_lib.gmm_estep_stats_host(self._h, ctypes.c_void_p(X.data_ptr()), N, ldx, _ptr(w), _ptr(mu),
+                                                  _ptr(var), _ptr(Nk), _ptr(S1), _ptr(S2), _ptr(ll),
+                                                  int(bool(accumulate)), int(chunk_rows)))
+        return Nk, S1, S2, ll
+
+    def fit_host(self, X, w, mu, var, T, var_floor, chunk_rows, ll_hist=None):
+        N, ldx = self._host_rows(X)
+        self._params(w, mu, var)
+        if ll_hist is None:
+            ll_hist = torch.zeros(int(T), dtype=torch.float64, device=self.device)
+        with torch.cuda.device(self.device):
+            self._check(_lib.gmm_fit_host(self._h, ctypes.c_void_p(X.data_ptr()), N, ldx, int(T), float(var_floor),
+                                          _ptr(w), _ptr(mu), _ptr(var), _ptr(ll_hist), int(chunk_rows)))
+        return w, mu, var, ll_hist
 
     # ---- k-means warm start
     def _list_scratch(self, N):

@@ -29,6 +29,13 @@ struct gmm_ctx {
   std::vector<hipEvent_t> ev_free;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_pending[2];
   hipEvent_t ev_open[2] = {nullptr, nullptr};
+  // out-of-core E-step: a copy stream, two device staging buffers of
+  // stage_rows x D floats (grown on demand) and their events
+  hipStream_t copy_stream = nullptr;
+  float* stage[2] = {nullptr, nullptr};
+  int64_t stage_rows = 0;
+  hipEvent_t ev_copied[2] = {nullptr, nullptr};
+  hipEvent_t ev_used[2] = {nullptr, nullptr};
 };
 
 namespace {
@@ -256,6 +263,12 @@ void gmm_destroy(gmm_ctx* ctx) {
   drop_events(ctx);
   for (hipEvent_t e : ctx->ev_free) hipEventDestroy(e);
   if (ctx->base) hipFree(ctx->base);
+  for (int b = 0; b < 2; ++b) {
+    if (ctx->stage[b]) hipFree(ctx->stage[b]);
+    if (ctx->ev_copied[b]) hipEventDestroy(ctx->ev_copied[b]);
+    if (ctx->ev_used[b]) hipEventDestroy(ctx->ev_used[b]);
+  }
+  if (ctx->copy_stream) hipStreamDestroy(ctx->copy_stream);
   delete ctx;
 }
 
@@ -551,6 +564,76 @@ gmm_status kmeans_assign(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, c
   return soft_assign_run(ctx, X, N, ldx, ctx->ws.wuni, centres, ctx->ws.vexp, 1.0f, 0, offsets, ids, N, &nnz);
 }
 
+// Out-of-core E-step: rows [r0, r0 + rows) of a host X are copied into
+// alternating device staging buffers on the copy stream while the E-step of
+// the previous chunk runs on the context's stream; an event per buffer keeps
+// a copy from overwriting a chunk whose E-step has not finished.  The
+// statistics accumulate over the chunks exactly as gmm_estep_stats with
+// accumulate = 1 on the same row ranges.  Staging rows have a stride of D
+// rounded up to 4 floats; the padding floats are never read as data.
+gmm_status stage_setup(gmm_ctx* c, int64_t chunk) {
+  if (!c->copy_stream) {
+    hipError_t e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking);
+    for (int b = 0; b < 2 && e == hipSuccess; ++b) {
+      e = hipEventCreateWithFlags(&c->ev_copied[b], hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_used[b], hipEventDisableTiming);
+    }
+    if (e != hipSuccess) return hip_fail(c, e, "copy stream set-up");
+  }
+  if (chunk > c->stage_rows) {
+    hipError_t e = hipStreamSynchronize(c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->copy_stream);
+    if (e != hipSuccess) return hip_fail(c, e, "stream synchronize");
+    for (int b = 0; b < 2; ++b) {
+      if (c->stage[b]) hipFree(c->stage[b]);
+      c->stage[b] = nullptr;
+    }
+    c->stage_rows = 0;
+    const size_t bytes = (size_t)chunk * ((c->plan.D + 3) & ~3) * sizeof(float);
+    for (int b = 0; b < 2; ++b) {
+      e = hipMalloc(&c->stage[b], bytes);
+      if (e != hipSuccess) return fail(c, GMM_ERR_OOM, "staging hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+    }
+    c->stage_rows = chunk;
+  }
+  return GMM_OK;
+}
+
+gmm_status estep_host(gmm_ctx* c, const float* Xh, int64_t N, int64_t ldx, const float* w, const float* mu,
+                      const float* var, double* Nk, double* S1, double* S2, double* ll, int accumulate,
+                      int64_t chunk) {
+  gmm_status st = stage_setup(c, chunk);
+  if (st) return st;
+  const int D = c->plan.D;
+  const int ld = (D + 3) & ~3;  // staging row stride (the kernels' float4 rows)
+  int i = 0;
+  for (int64_t r0 = 0; r0 < N; r0 += chunk, ++i) {
+    const int64_t rows = (N - r0 < chunk) ? N - r0 : chunk;
+    const int b = i & 1;
+    hipError_t e = hipSuccess;
+    if (i >= 2) e = hipStreamWaitEvent(c->copy_stream, c->ev_used[b], 0);
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync(c->stage[b], (size_t)ld * sizeof(float), Xh + r0 * ldx, (size_t)ldx * sizeof(float),
+                           (size_t)D * sizeof(float), (size_t)rows, hipMemcpyHostToDevice, c->copy_stream);
+    if (e == hipSuccess) e = hipEventRecord(c->ev_copied[b], c->copy_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(c->stream, c->ev_copied[b], 0);
+    if (e != hipSuccess) return hip_fail(c, e, "chunk copy");
+    st = estep_into(c, c->stage[b], rows, ld, w, mu, var, Nk, S1, S2, ll, (i > 0) ? 1 : accumulate);
+    if (st) return st;
+    e = hipEventRecord(c->ev_used[b], c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "chunk event");
+  }
+  return GMM_OK;
+}
+
+gmm_status check_host_x(gmm_ctx* c, const float* Xh, int64_t N, int64_t ldx, int64_t chunk) {
+  if (!Xh) return fail(c, GMM_ERR_INVALID_ARG, "X is NULL");
+  if (N < 1) return fail(c, GMM_ERR_INVALID_ARG, "N must be >= 1 (got %lld)", (long long)N);
+  if (ldx < c->plan.D) return fail(c, GMM_ERR_INVALID_ARG, "ldx must be >= D (got %lld, D=%d)", (long long)ldx, c->plan.D);
+  if (chunk < 1 || chunk > ((int64_t)1 << 30)) return fail(c, GMM_ERR_INVALID_ARG, "chunk_rows must be in [1, 2^30]");
+  return GMM_OK;
+}
+
 gmm_status kmeans_check(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, const float* centres,
                         const int64_t* offsets, const int32_t* ids) {
   gmm_status st = check_x(ctx, X, N, ldx);
@@ -564,6 +647,43 @@ gmm_status kmeans_check(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, co
 }  // namespace
 
 extern "C" {
+
+gmm_status gmm_estep_stats_host(gmm_ctx* ctx, const float* X_host, int64_t N, int64_t ldx, const float* weights,
+                                const float* means, const float* vars, double* Nk, double* S1, double* S2,
+                                double* loglik, int32_t accumulate, int64_t chunk_rows) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  gmm_status st = check_host_x(ctx, X_host, N, ldx, chunk_rows);
+  if (st) return st;
+  st = check_params(ctx, weights, means, vars);
+  if (st) return st;
+  if (!Nk || !S1 || !S2 || !loglik) return fail(ctx, GMM_ERR_INVALID_ARG, "statistics outputs must be non-NULL");
+  if (accumulate != 0 && accumulate != 1) return fail(ctx, GMM_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  return estep_host(ctx, X_host, N, ldx, weights, means, vars, Nk, S1, S2, loglik, accumulate, chunk_rows);
+}
+
+gmm_status gmm_fit_host(gmm_ctx* ctx, const float* X_host, int64_t N, int64_t ldx, int32_t T, float var_floor,
+                        float* weights, float* means, float* vars, double* loglik_hist, int64_t chunk_rows) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  gmm_status st = check_host_x(ctx, X_host, N, ldx, chunk_rows);
+  if (st) return st;
+  st = check_params(ctx, weights, means, vars);
+  if (st) return st;
+  if (T < 1) return fail(ctx, GMM_ERR_INVALID_ARG, "T must be >= 1");
+  if (!loglik_hist) return fail(ctx, GMM_ERR_INVALID_ARG, "loglik_hist is NULL");
+  if (!(var_floor > 0.f) || !isfinite(var_floor)) return fail(ctx, GMM_ERR_INVALID_ARG, "var_floor must be > 0");
+  const int K = ctx->plan.K, D = ctx->plan.D;
+  double* Nk = ctx->ws.stats;
+  double* S1 = Nk + K;
+  double* S2 = S1 + (size_t)K * D;
+  for (int t = 0; t < T; ++t) {
+    st = estep_host(ctx, X_host, N, ldx, weights, means, vars, Nk, S1, S2, loglik_hist + t, 0, chunk_rows);
+    if (st) return st;
+    hipError_t e = gmm::launch_mstep(ctx->plan, ctx->ws, Nk, S1, S2, (double)N, var_floor, weights, means, vars,
+                                     ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "mstep launch");
+  }
+  return GMM_OK;
+}
 
 gmm_status gmm_kmeans(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, int32_t iters, float* centres,
                       double* counts, int64_t* list_offsets, int32_t* list_ids) {

@@ -1,0 +1,82 @@
+"""Out-of-core E-step and fit (X in host memory, chunks copied through two
+device staging buffers on a copy stream while the E-step of the previous
+chunk runs): bit-identical to the device E-step over the same row ranges
+with accumulate, pinned and pageable host memory, a row stride above D, and
+fit parity against the float64 oracle per iteration."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.gmm_oracle as O
+from soft_clustering_amd import datagen
+from tests.tolerance import check_params
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def case(law, N, D, K, ldx=None, pinned=True):
+    mix = datagen.mixture(law, D, K, seed=0)
+    Xc = datagen.sample(mix, N, seed=0)
+    if ldx is not None:
+        buf = torch.full((N, ldx), float("nan"), dtype=torch.float32)
+        buf[:, :D] = Xc
+        Xh = buf[:, :D]
+    else:
+        Xh = Xc.clone()
+    if pinned:
+        Xh = Xh.pin_memory() if ldx is None else buf.pin_memory()[:, :D]
+    Xn = Xc.numpy()
+    params = tuple(torch.as_tensor(a.astype(np.float32)).to(DEV)
+                   for a in O.init(Xn, datagen.init_rows(N, K, seed=1), 1e-6))
+    return Xn, Xh, params
+
+
+@pytest.mark.parametrize("pinned", [True, False])
+@pytest.mark.parametrize("name,law,N,D,K,ldx,chunk", [
+    ("mid_prefix", "mid", 20_037, 128, 1024, None, 7_000),
+    ("odd_d5_k7", "tiny", 1_003, 5, 7, 8, 300),
+    ("one_chunk", "tiny", 4_001, 8, 16, None, 10_000),
+])
+def test_host_estep_bit_identical_to_device_chunks(name, law, N, D, K, ldx, chunk, pinned):
+    from soft_clustering_amd import GMM
+    Xn, Xh, params = case(law, N, D, K, ldx, pinned)
+    g = GMM(K, D)
+    host = [t.clone() for t in g.estep_stats_host(Xh, *params, chunk)]
+    g.check()
+    ld = (D + 3) // 4 * 4
+    Xd = torch.zeros(N, ld, dtype=torch.float32, device=DEV)
+    Xd[:, :D] = torch.as_tensor(Xn).to(DEV)
+    Xd = Xd[:, :D]
+    out = None
+    for r0 in range(0, N, chunk):
+        out = g.estep_stats(Xd[r0:r0 + chunk], *params, out=out, accumulate=r0 > 0)
+    g.check()
+    for a, b, what in zip(host, out, ("Nk", "S1", "S2", "LL")):
+        assert torch.equal(a, b), f"{name}: {what} differs"
+
+
+def test_fit_host_per_iteration_and_single_chunk():
+    from soft_clustering_amd import GMM
+    Xn, Xh, params = case("tiny", 10_000, 8, 16)
+    N = Xn.shape[0]
+    K = 16
+    g = GMM(K, 8)
+    w, mu, var = (t.clone() for t in params)
+    for t in range(3):
+        th = tuple(a.cpu().numpy().copy() for a in (w, mu, var))
+        Nk, S1, S2, ll = O.estep_stats(Xn, *th, method="direct")
+        want = O.mstep(Nk, S1, S2, N, 1e-6, th[1], th[2])
+        hist = torch.zeros(1, dtype=torch.float64, device=DEV)
+        g.fit_host(Xh, w, mu, var, 1, 1e-6, 3_333, hist)
+        g.check()
+        assert abs(hist.item() - ll) <= 1e-4 * abs(ll)
+        errs = check_params((w.cpu(), mu.cpu(), var.cpu()), want, Nk, N, 1e-4)
+        assert not errs, errs
+    # one chunk holding every row: the same launches as gmm_fit on device data
+    a = [t.clone() for t in params]
+    b = [t.clone() for t in params]
+    ha = g.fit_host(Xh, *a, 4, 1e-6, N)[3]
+    hb = g.fit(torch.as_tensor(Xn).to(DEV), *b, 4, 1e-6)[3]
+    g.check()
+    assert torch.equal(ha, hb) and all(torch.equal(x, y) for x, y in zip(a, b))
