@@ -48,16 +48,18 @@ def useful_flops(N, K, D, iso=False):
 
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                "k_stats_fused_large_traffic.md")
-KERNEL_SOURCES = ("gmm_kernels.hip", "gmm_device.h", "gmm_internal.h")
-
-
-def kernel_source_hash():
+def kernel_source_hash(root=None):
+    """sha256 prefix of the fused E-step's source: the text of k_stats (from its
+    heading comment to the next kernel's) and the device code it includes."""
     import hashlib
+    base = os.path.join(root or os.path.dirname(os.path.abspath(__file__)), "soft_clustering_amd", "csrc")
+    src = open(os.path.join(base, "gmm_kernels.hip")).read()
+    i = src.index("// E-step statistics sweep.")
+    j = src.index("// First sweep of the two-sweep path", i)
     h = hashlib.sha256()
-    base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "soft_clustering_amd", "csrc")
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(base, f), "rb") as fh:
-            h.update(fh.read())
+    h.update(src[i:j].encode())
+    with open(os.path.join(base, "gmm_device.h"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 
