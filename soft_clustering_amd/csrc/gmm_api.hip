@@ -122,18 +122,27 @@ bool want_fused(const gmm_ctx* c) {
   return c->plan.fusedOK != 0 && c->plan.P <= 64;
 }
 
+// var_iso (isotropic model): var is its broadcast, and the fused isotropic
+// kernel runs where it applies (else the diagonal kernels on the broadcast)
 gmm_status estep_into(gmm_ctx* c, const float* X, int64_t N, int64_t ldx, const float* w, const float* mu,
-                      const float* var, double* Nk, double* S1, double* S2, double* ll, int accumulate) {
+                      const float* var, double* Nk, double* S1, double* S2, double* ll, int accumulate,
+                      const float* var_iso = nullptr) {
   hipStream_t s = c->stream;
   hipError_t e = gmm::launch_precompute(c->plan, c->ws, w, mu, var, s);
   if (e != hipSuccess) return hip_fail(c, e, "precompute launch");
   const bool fused = want_fused(c);
+  const char* envi = getenv("FLASHGMM_ISO_KERNEL");  // 0: diagonal kernels on the broadcast (measurements)
+  const bool iso = var_iso && fused && gmm::iso_kernel_ok(c->plan, c->ws) && !(envi && atoi(envi) == 0);
+  if (iso) {
+    e = gmm::launch_precompute_iso(c->plan, c->ws, mu, var_iso, s);
+    if (e != hipSuccess) return hip_fail(c, e, "precompute launch");
+  }
   gmm::LaunchHooks hk;
   hk.before = hook_before;
   hk.after = hook_after;
   hk.user = c;
   int nslots = 0;
-  e = gmm::launch_estep(c->plan, c->ws, X, N, ldx, fused, s, c->prof ? &hk : nullptr, &nslots);
+  e = gmm::launch_estep(c->plan, c->ws, X, N, ldx, fused, s, c->prof ? &hk : nullptr, &nslots, iso);
   if (e != hipSuccess) return hip_fail(c, e, fused ? "fused E-step launch" : "two-sweep E-step launch");
   e = gmm::launch_reduce(c->plan, c->ws, Nk, S1, S2, ll, accumulate, nslots, fused ? nslots : c->plan.Glogz, N,
                          s);
@@ -213,6 +222,8 @@ gmm_status gmm_create(gmm_ctx** out, int32_t K, int32_t D, void* hip_stream) {
   c->ws.vexp = carve<float>(q, (size_t)p.K * p.D);
   c->ws.qiso = carve<double>(q, p.K);
   c->ws.wuni = carve<float>(q, p.K);
+  c->ws.wiso = carve<float>(q, (size_t)p.Kpad * p.Dp);
+  c->ws.ivec = carve<float>(q, p.Kpad);
   c->ws.wop64 = carve<double>(q, (size_t)p.Kpad * 2 * p.Dp);
   c->ws.cvec64 = carve<double>(q, p.Kpad);
   c->ws.f64 = 0;
@@ -440,7 +451,7 @@ gmm_status gmm_estep_stats_iso(gmm_ctx* ctx, const float* X, int64_t N, int64_t 
   double* S2 = ctx->ws.stats + p.K + (size_t)p.K * p.D;
   if (e == hipSuccess && accumulate) e = gmm::launch_fill_zero(S2, (size_t)p.K * p.D, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, "isotropic set-up");
-  st = estep_into(ctx, X, N, ldx, weights, means, ctx->ws.vexp, Nk, S1, S2, loglik, accumulate);
+  st = estep_into(ctx, X, N, ldx, weights, means, ctx->ws.vexp, Nk, S1, S2, loglik, accumulate, var_iso);
   if (st) return st;
   e = gmm::launch_iso_q(p, S2, Q, accumulate, ctx->stream);
   if (e != hipSuccess) return hip_fail(ctx, e, "isotropic Q");
@@ -479,7 +490,7 @@ gmm_status gmm_fit_iso(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, int
   for (int t = 0; t < T; ++t) {
     hipError_t e = gmm::launch_iso_expand(p, ctx->ws, var_iso, ctx->stream);
     if (e != hipSuccess) return hip_fail(ctx, e, "isotropic set-up");
-    st = estep_into(ctx, X, N, ldx, weights, means, ctx->ws.vexp, Nk, S1, S2, loglik_hist + t, 0);
+    st = estep_into(ctx, X, N, ldx, weights, means, ctx->ws.vexp, Nk, S1, S2, loglik_hist + t, 0, var_iso);
     if (st) return st;
     e = gmm::launch_iso_q(p, S2, ctx->ws.qiso, 0, ctx->stream);
     if (e == hipSuccess)

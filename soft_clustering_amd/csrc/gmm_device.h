@@ -86,6 +86,9 @@ struct EArgs {
   int dma;               // 1: X tiles by LDS DMA (D == Dp)
   const double* wop64;   // Kpad x 2 Dp  [a | b] in float64, MFMA-operand order (as wop)
   const double* cvec64;  // Kpad  c_k - C in float64 (-inf: padding)
+  // isotropic kernel: W = mu / s^2 in its MFMA-operand order, 1 / (2 s^2)
+  const float* wiso;     // Kpad x Dp
+  const float* ivec;     // Kpad  (0: padding)
 };
 
 // ---------------------------------------------------------------------------
@@ -185,6 +188,70 @@ __device__ __forceinline__ void stage_dma(float* __restrict__ xt, const float* _
 // Wait for this wave's outstanding global memory operations (LDS DMA
 // included): s_waitcnt vmcnt(0).
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Isotropic logits x . (mu_k / s_k^2) of one wave (WD = 1): A = x of 16
+// points, lane (g, r16) giving row r16's dims g*Q + 4 s4 .. +3 (Q = DPW / 4),
+// B = the matching W values of 16 components, DPW/16 groups of four k-steps;
+// W fetched one group ahead.  acc must hold the starting value.
+template <class SH, int DPW>
+__device__ __forceinline__ void logit_tile_iso(const float* __restrict__ xt, const float* __restrict__ w0,
+                                               const float* __restrict__ w1, f4 (&acc)[SH::NPB][2], int lane) {
+  const int g = lane >> 4, r16 = lane & 15;
+  constexpr int Q = DPW / 4, S4 = DPW / 16;
+  const float* arow = xt + r16 * SH::RS + g * Q;
+  f4 b0 = *reinterpret_cast<const f4*>(w0 + lane * 4);
+  f4 b1 = *reinterpret_cast<const f4*>(w1 + lane * 4);
+#pragma unroll 2
+  for (int s4 = 0; s4 < S4; ++s4) {
+    const int nx = (s4 + 1 < S4) ? s4 + 1 : s4;
+    const f4 b0n = *reinterpret_cast<const f4*>(w0 + (nx * kWave + lane) * 4);
+    const f4 b1n = *reinterpret_cast<const f4*>(w1 + (nx * kWave + lane) * 4);
+    auto ld = [&](int pb) { return *reinterpret_cast<const f4*>(arow + pb * 16 * SH::RS + s4 * 4); };
+    f4 an = ld(0);
+#pragma unroll
+    for (int pb = 0; pb < SH::NPB; ++pb) {
+      const f4 a = an;
+      if (pb + 1 < SH::NPB) an = ld(pb + 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[pb][0] = mfma(a[i], b0[i], acc[pb][0]);
+        acc[pb][1] = mfma(a[i], b1[i], acc[pb][1]);
+      }
+    }
+    b0 = b0n;
+    b1 = b1n;
+  }
+}
+
+// Row norms for the isotropic kernel: nrm as row_norms2 (rounded up, for the
+// error bound) and xn2[pt] = ||x||^2 in float32 (fixed order) for the logits
+// and Q.
+template <class SH, int DPW>
+__device__ __forceinline__ void row_norms_iso(const float* __restrict__ xt, float2* __restrict__ nrm,
+                                              float* __restrict__ xn2) {
+  constexpr int BN = SH::TILE / SH::RS;
+  constexpr int TPR = SH::NT / BN;
+  const int pt = threadIdx.x / TPR, sub = threadIdx.x % TPR;
+  float n2 = 0.f, n1 = 0.f;
+  if (pt < BN) {
+    const float* xrow = xt + pt * SH::RS;
+#pragma unroll
+    for (int q = sub; q < SH::CPR; q += TPR) {
+      const f4 xv = *reinterpret_cast<const f4*>(xrow + q * 4);
+      n2 += (xv[0] * xv[0] + xv[1] * xv[1]) + (xv[2] * xv[2] + xv[3] * xv[3]);
+      n1 += (fabsf(xv[0]) + fabsf(xv[1])) + (fabsf(xv[2]) + fabsf(xv[3]));
+    }
+  }
+#pragma unroll
+  for (int o = TPR / 2; o > 0; o >>= 1) {
+    n2 += __shfl_xor(n2, o);
+    n1 += __shfl_xor(n1, o);
+  }
+  if (pt < BN && sub == 0) {
+    nrm[pt] = make_float2(n2 * (1.f + 1e-6f), n1 * (1.f + 1e-6f));
+    xn2[pt] = n2;
+  }
+}
 
 // Partial logits of one wave: its 2 component blocks x NPB point blocks over
 // its dim segment.  acc must hold the starting value (c or 0).  Per group of

@@ -63,6 +63,8 @@ struct Workspace {
   float* vexp;       // K * D  isotropic variances broadcast over the dimensions
   double* qiso;      // K      isotropic Q_k of gmm_fit_iso
   float* wuni;       // K      k-means: equal weights
+  float* wiso;       // Kpad * Dp  isotropic kernel: mu / s^2 in MFMA-operand order
+  float* ivec;       // Kpad       isotropic kernel: 1 / (2 s^2)
   int colG;
   // soft assignment
   int32_t* asel;                 // assignChunk * 9  per-row selections
@@ -89,8 +91,12 @@ struct LaunchHooks {
   void* user = nullptr;
 };
 // *nslots receives the number of statistics slots (row groups) written.
+// iso: the fused isotropic kernel (iso_kernel_ok; launch_precompute_iso first)
 hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx,
-                        bool fused, hipStream_t s, const LaunchHooks* hooks, int* nslots);
+                        bool fused, hipStream_t s, const LaunchHooks* hooks, int* nslots, bool iso = false);
+bool iso_kernel_ok(const Plan& p, const Workspace& w);
+hipError_t launch_precompute_iso(const Plan& p, const Workspace& w, const float* means, const float* var_iso,
+                                 hipStream_t s);
 hipError_t launch_reduce(const Plan& p, const Workspace& w, double* Nk, double* S1, double* S2,
                          double* ll, int accumulate, int nslots, int nllslots, int64_t nrows,
                          hipStream_t s);

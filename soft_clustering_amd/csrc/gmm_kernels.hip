@@ -110,11 +110,19 @@ __device__ __forceinline__ void row_exchange(const EArgs& a, int rg, int p, int 
 
 // ---------------------------------------------------------------------------
 // E-step statistics sweep.  FUSED: per-row log Z by exchange; else from a.logz.
-template <int WC, int WD, int DPW, int BN, bool FUSED, int MODE>
+// ISO: the isotropic model (Sigma_k = s_k^2 I) with its own contractions:
+// logits x . mu_k / s_k^2 over D features (minus ||x||^2 / (2 s_k^2) added per
+// row and component), statistics r^T x over D features, Q_k = sum r ||x||^2
+// accumulated like N_k; S1 lands in the slots' x positions, Q in the x^2
+// position of dim 0 and zeros in the other x^2 positions, so the diagonal
+// reduction yields N_k, S1 and Q = sum_d S2_kd.
+template <int WC, int WD, int DPW, int BN, bool FUSED, int MODE, bool ISO = false>
 __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats(EArgs a) {
   using SH = Shape<WC, WD, DPW, BN>;
   constexpr bool REFINE = MODE == MODE_REFINE, F64 = MODE == MODE_FP64;
-  constexpr int NPB = SH::NPB, NFB = SH::NFB;
+  static_assert(!ISO || (FUSED && WD == 1 && !F64), "isotropic kernel: fused path, WD = 1, float32 logits");
+  constexpr int NPB = SH::NPB;
+  constexpr int NFB = ISO ? DPW / 16 : SH::NFB;  // statistics feature blocks
   constexpr int FLUSH = (BN >= 64) ? 32 : 128;  // tiles between fp64 flushes (2048 rows)
   // row groups flush at staggered tiles, so the float64 atomics of the grid
   // do not all reach L2 at once; the members of a row group flush together
@@ -134,6 +142,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   __shared__ float vtmp[BN];
   __shared__ float rlist[SH::COOP ? WC : WC * WD][kRefineCap];  // refinement lists (per group or wave)
   __shared__ unsigned short elist[SH::COOP ? WC : WC * WD][kRefineCap];
+  __shared__ __attribute__((aligned(16))) float xn2[ISO ? BN : 4];  // ISO: ||x||^2 of the tile's rows
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wc = w % WC, wd = w / WC;
@@ -144,8 +153,11 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   const int fphase = rg % FLUSH;  // flush stagger, by row group
   const int compbase = p * 32 * WC + wc * 32;  // first component of this wave
   const int cb16 = compbase >> 4;
-  const float* w0 = wop_block(a.wop, cb16, WD, wd, DPW);
-  const float* w1 = wop_block(a.wop, cb16 + 1, WD, wd, DPW);
+  const float* w0 = ISO ? a.wiso + (size_t)cb16 * DPW * 16 : wop_block(a.wop, cb16, WD, wd, DPW);
+  const float* w1 = ISO ? a.wiso + (size_t)(cb16 + 1) * DPW * 16 : wop_block(a.wop, cb16 + 1, WD, wd, DPW);
+  const float iv0 = ISO ? a.ivec[compbase + r16] : 0.f;  // 1 / (2 s^2) of the lane's components
+  const float iv1 = ISO ? a.ivec[compbase + 16 + r16] : 0.f;
+  float q0 = 0.f, q1 = 0.f;                              // ISO: Q partials
   const float c0 = (wd == 0) ? a.cvec[compbase + r16] : 0.f;
   const float c1 = (wd == 0) ? a.cvec[compbase + 16 + r16] : 0.f;
   const double C = *a.cshift;
@@ -179,13 +191,24 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
       __hip_atomic_fetch_add(ptr, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   auto flush = [&]() {
+    // slot feature index of x (sq = false) or x^2 (sq = true) of dim d of the
+    // wave's segment: quarters of HALF dims alternate x^2, x
+    auto fpos = [&](int d, bool sq) { return (2 * (d / SH::HALF) + (sq ? 0 : 1)) * SH::HALF + d % SH::HALF; };
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
       for (int fb = 0; fb < NFB; ++fb) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          put(sbase + (size_t)(cb * 16 + 4 * g + v) * SR + wd * 2 * DPW + fb * 16 + r16, (double)sacc[cb][fb][v]);
+        for (int v = 0; v < 4; ++v) {
+          double* row = sbase + (size_t)(cb * 16 + 4 * g + v) * SR + wd * 2 * DPW;
+          if constexpr (ISO) {
+            const int d = fb * 16 + r16;
+            put(row + fpos(d, false), (double)sacc[cb][fb][v]);
+            if (fresh && d > 0) put(row + fpos(d, true), 0.0);
+          } else {
+            put(row + fb * 16 + r16, (double)sacc[cb][fb][v]);
+          }
+        }
         sacc[cb][fb] = f4{0.f, 0.f, 0.f, 0.f};
       }
     }
@@ -196,6 +219,17 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
     if (wd == 0 && g == 0) {
       put(sbase + (size_t)r16 * SR + 2 * a.Dp, (double)t0);
       put(sbase + (size_t)(16 + r16) * SR + 2 * a.Dp, (double)t1);
+    }
+    if constexpr (ISO) {
+      float u0 = q0 + __shfl_xor(q0, 16);
+      u0 += __shfl_xor(u0, 32);
+      float u1 = q1 + __shfl_xor(q1, 16);
+      u1 += __shfl_xor(u1, 32);
+      if (g == 0) {
+        put(sbase + (size_t)r16 * SR + fpos(0, true), (double)u0);
+        put(sbase + (size_t)(16 + r16) * SR + fpos(0, true), (double)u1);
+      }
+      q0 = q1 = 0.f;
     }
     nk0 = nk1 = 0.f;
     fresh = false;
@@ -240,14 +274,31 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
         acc[pb][0] = f4{c0, c0, c0, c0};
         acc[pb][1] = f4{c1, c1, c1, c1};
       }
-      logit_tile<SH, DPW>(xt[cur], w0, w1, acc, lane, wd);
-      reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
+      if constexpr (ISO) {
+        row_norms_iso<SH, DPW>(xt[cur], nrm, xn2);
+        logit_tile_iso<SH, DPW>(xt[cur], w0, w1, acc, lane);
+        __syncthreads();  // xn2
+#pragma unroll
+        for (int pb = 0; pb < NPB; ++pb) {
+          const f4 n4 = *reinterpret_cast<const f4*>(xn2 + pb * 16 + 4 * g);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            acc[pb][0][v] = fmaf(-iv0, n4[v], acc[pb][0][v]);
+            acc[pb][1][v] = fmaf(-iv1, n4[v], acc[pb][1][v]);
+          }
+        }
+      } else {
+        logit_tile<SH, DPW>(xt[cur], w0, w1, acc, lane, wd);
+        reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
+      }
     }
 
     // ---- float64 refinement of the logits that can matter
     if constexpr (REFINE) {
-      row_norms2<SH, DPW>(xt[cur], nrm, a.Dp);
-      __syncthreads();
+      if constexpr (!ISO) {
+        row_norms2<SH, DPW>(xt[cur], nrm, a.Dp);
+        __syncthreads();
+      }
       if constexpr (FUSED) {
         // round 1 of the exchange: each workgroup's largest lower bound
         // L - E of the row's logits; their maximum bounds the row's largest
@@ -322,14 +373,16 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
     // lane (g, r16) feeds feature f = fb * 16 + r16 of its segment for point
     // 4g + v of each 16-point block: offsets from xs are compile-time except
     // for DPW = 16, whose 8-dim halves split a 16-lane block
-    constexpr bool NARROW = SH::HALF < 16;
+    constexpr bool NARROW = !ISO && SH::HALF < 16;
     const float* xs = xt[cur] + wd * DPW + (NARROW ? (r16 & 7) : r16) + 4 * g * SH::RS;
     auto fdim = [&](int fb) {  // dim offset of feature block fb (minus the lane part)
-      if constexpr (NARROW) return fb * 8;
+      if constexpr (ISO) return fb * 16;
+      else if constexpr (NARROW) return fb * 8;
       else return ((fb * 16 / SH::HALF) >> 1) * SH::HALF + (fb * 16) % SH::HALF;
     };
     auto fsq = [&](int fb) {  // x^2 feature?
-      if constexpr (NARROW) return r16 < 8;
+      if constexpr (ISO) return false;
+      else if constexpr (NARROW) return r16 < 8;
       else return ((fb * 16 / SH::HALF) & 1) == 0;
     };
     auto bload = [&](int fb, int pt) {
@@ -347,6 +400,14 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
         acc[pb][1][v] = __expf(acc[pb][1][v] - lz[v]);
         nk0 += acc[pb][0][v];
         nk1 += acc[pb][1][v];
+      }
+      if constexpr (ISO) {
+        const f4 n4 = *reinterpret_cast<const f4*>(xn2 + pb * 16 + 4 * g);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          q0 = fmaf(acc[pb][0][v], n4[v], q0);
+          q1 = fmaf(acc[pb][1][v], n4[v], q1);
+        }
       }
     }
     // one B operand per feature block: each is reloaded for the next point
@@ -597,6 +658,29 @@ __global__ void k_precompute_c(const float* __restrict__ w, const float* __restr
     // log-density of the component at its own mean, and the full constant
     cpeak[comp] = lw - 0.5 * ld - 0.5 * D * kLog2Pi;
     cfull[comp] = cpeak[comp] - 0.5 * q;
+  }
+}
+
+// Isotropic kernel operands: W = mu_k / s_k^2 in the order logit_tile_iso
+// reads it ([comp block][group of four k-steps][lane][4]: lane (g, r16) holds
+// component r16's dims g*Q + 4 s4 .. +3, Q = DPW / 4) and 1 / (2 s_k^2).
+__global__ void k_precompute_wiso(const float* __restrict__ mu, const float* __restrict__ var_iso, float* wiso,
+                                  float* ivec, int K, int D, int Kpad, int DPW) {
+  const int S4 = DPW / 16, Q = DPW / 4;
+  const size_t total = (size_t)Kpad * DPW;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int i = (int)(idx & 3);
+    const int lane = (int)((idx >> 2) & 63);
+    const size_t rest = idx >> 8;
+    const int s4 = (int)(rest % S4);
+    const int cb16 = (int)(rest / S4);
+    const int comp = cb16 * 16 + (lane & 15);
+    const int d = (lane >> 4) * Q + s4 * 4 + i;
+    float val = 0.f;
+    if (comp < K && d < D) val = (float)((double)mu[(size_t)comp * D + d] / (double)var_iso[comp]);
+    wiso[idx] = val;
+    if (idx < (size_t)Kpad) ivec[idx] = (idx < (size_t)K) ? (float)(0.5 / (double)var_iso[idx]) : 0.f;
   }
 }
 
@@ -966,12 +1050,18 @@ struct Kern {
   static void* stats_two() { return (void*)&k_stats<WC, WD, DPW, BN, false, M>; }
   template <int M>
   static void* logz() { return (void*)&k_logz<WC, WD, DPW, BN, M>; }
+  template <int M>
+  static void* stats_iso() {
+    if constexpr (WD == 1) return (void*)&k_stats<WC, WD, DPW, BN, true, M, true>;
+    else return nullptr;
+  }
 };
 
 // Kernel variants of one shape, indexed by logit precision mode (the fused
 // kernel has no float64-logit variant: that mode runs the two-sweep path).
 struct KTab {
   void* fused[2];
+  void* iso[2];  // fused isotropic kernels (nullptr where not built)
   void* two[3];
   void* logz[3];
 };
@@ -981,6 +1071,7 @@ static bool lookup(int WC, int WD, int DPW, KTab& t) {
   if (WC == wc && WD == wd && DPW == dpw) {                                                           \
     using KK = Kern<wc, wd, dpw>;                                                                     \
     t = KTab{{KK::stats_fused<0>(), KK::stats_fused<1>()},                                             \
+             {KK::stats_iso<0>(), KK::stats_iso<1>()},                                                 \
              {KK::stats_two<0>(), KK::stats_two<1>(), KK::stats_two<2>()},                                \
              {KK::logz<0>(), KK::logz<1>(), KK::logz<2>()}};                                              \
     return true;                                                                                      \
@@ -1067,6 +1158,7 @@ size_t workspace_bytes(const Plan& p) {
   b += up((size_t)p.Kpad * 2 * p.Dp * 8) + up((size_t)p.Kpad * 8);  // wop64, cvec64
   b += up((size_t)p.K * p.D * 4) + up((size_t)p.K * 8);  // isotropic: broadcast variances, Q
   b += up((size_t)p.K * 4);  // k-means: equal weights
+  b += up((size_t)p.Kpad * p.Dp * 4) + up((size_t)p.Kpad * 4);  // isotropic kernel: W, 1/(2 s^2)
   b += up((size_t)p.R * p.Kpad * p.SR * 8);
   b += up((size_t)(p.R > p.Glogz ? p.R : p.Glogz) * 8);
   b += up((size_t)p.chunk * 4);
@@ -1094,6 +1186,12 @@ hipError_t occupancy(const Plan& p, int* occStats, int* occLogz) {
   int o1b = 0, o2b = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1, (const void*)t.fused[0], nt, 0);
   if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1b, (const void*)t.fused[1], nt, 0);
+  for (int m = 0; m < 2 && e == hipSuccess; ++m) {
+    if (!t.iso[m]) continue;
+    int oi = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&oi, (const void*)t.iso[m], nt, 0);
+    if (oi < o1b) o1b = oi;
+  }
   if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o2, (const void*)t.logz[0], nt, 0);
   if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o2b, (const void*)t.logz[1], nt, 0);
   if (e != hipSuccess) return e;
@@ -1156,6 +1254,8 @@ static EArgs make_args(const Plan& p, const Workspace& w, const float* X, int64_
   a.dma = (p.D == p.Dp && !(env && atoi(env) == 0)) ? 1 : 0;
   a.wop64 = w.wop64;
   a.cvec64 = w.cvec64;
+  a.wiso = w.wiso;
+  a.ivec = w.ivec;
   return a;
 }
 
@@ -1164,8 +1264,21 @@ __global__ void k_fill_u64(unsigned long long* p, size_t n) {
     p[i] = 0ull;
 }
 
+bool iso_kernel_ok(const Plan& p, const Workspace& w) {
+  KTab t;
+  return !w.f64 && lookup(p.WC, p.WD, p.DPW, t) && t.iso[w.refine ? 1 : 0] != nullptr;
+}
+
+hipError_t launch_precompute_iso(const Plan& p, const Workspace& w, const float* means, const float* var_iso,
+                                 hipStream_t s) {
+  const size_t total = (size_t)p.Kpad * p.DPW;
+  hipLaunchKernelGGL(k_precompute_wiso, dim3(grid_for(total, 256)), dim3(256), 0, s, means, var_iso, w.wiso,
+                     w.ivec, p.K, p.D, p.Kpad, p.DPW);
+  return hipGetLastError();
+}
+
 hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx, bool fused,
-                        hipStream_t s, const LaunchHooks* hk, int* nslots) {
+                        hipStream_t s, const LaunchHooks* hk, int* nslots, bool iso) {
   auto pre = [&](int which) {
     if (hk && hk->before) hk->before(hk->user, which, s);
   };
@@ -1187,7 +1300,9 @@ hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64
     hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(nx, 256)), dim3(256), 0, s, w.xbuf, nx);
     void* args[] = {&a};
     pre(0);
-    hipError_t e = hipLaunchCooperativeKernel(t.fused[mode], dim3(p.G), dim3(nt), args, 0, s);
+    void* kern = (iso && t.iso[mode]) ? t.iso[mode] : t.fused[mode];
+    if (iso && !t.iso[mode]) return hipErrorInvalidValue;
+    hipError_t e = hipLaunchCooperativeKernel(kern, dim3(p.G), dim3(nt), args, 0, s);
     if (e != hipSuccess) return e;
     post(0);
     *nslots = R;

@@ -208,3 +208,26 @@ def test_fit_iso_mid_1e6_rows_one_iteration():
     ref = OI.mstep(*want[:3], N, wl.var_floor, th[1], th[2])
     errs = check_params_iso((w.cpu(), mu.cpu(), v.cpu()), ref, want[0], N, 1e-4)
     assert not errs, errs
+
+
+@pytest.mark.parametrize("precision", ["refined", "fp32"])
+@pytest.mark.parametrize("name", ["tiny", "odd_d5_k7", "iso_prefix"])
+def test_iso_kernel_matches_broadcast_path(name, precision, monkeypatch):
+    """The fused isotropic kernel (D-wide contractions) against the diagonal
+    kernels run on the broadcast variances: the same statistics up to
+    float32 rounding of the logits (refined logits agree to float64)."""
+    from soft_clustering_amd import GMM, PATH_FUSED, PREC_FP32, PREC_REFINED
+    Xn, Xg, params, _ = data(name)
+    K, D = params[1].shape
+    g = GMM(K, D)
+    g.set_path(PATH_FUSED)
+    g.set_precision(PREC_REFINED if precision == "refined" else PREC_FP32)
+    out = {}
+    for flag in ("1", "0"):
+        monkeypatch.setenv("FLASHGMM_ISO_KERNEL", flag)
+        out[flag] = [t.cpu().numpy() for t in g.estep_stats_iso(Xg, *gpu(params))]
+        g.check()
+    a, b = out["1"], out["0"]
+    tol = 1e-5 if precision == "refined" else 1e-3
+    errs = check_stats_iso((a[0], a[1], a[2], a[3][0]), (b[0], b[1], b[2], b[3][0]), Xn, params[2], tol)
+    assert not errs, errs
