@@ -171,10 +171,12 @@ def bench_stream(args):
 
 
 def bench_kmeans(args):
-    """Lloyd iterations of the k-means warm start on the large data set: each
-    assigns every row to its nearest centre (two logit sweeps of the
-    soft-assignment kernels, counting then placing the CSR lists) and moves
-    the centres (one gather pass over X)."""
+    """Lloyd iterations of the k-means warm start on the large data set.  Each
+    is one sweep of the fused isotropic E-step kernel in its hard mode
+    (nearest centre per row, one-hot statistics) and a centre update from the
+    sums; FLASHGMM_KMEANS_FUSED=0 selects the list path instead (two logit
+    sweeps of the soft-assignment kernels into CSR lists, then a gather pass
+    over X), which needs the lists as scratch."""
     import torch
     from soft_clustering_amd import GMM, datagen
     wl = datagen.WORKLOADS["large"]
@@ -188,11 +190,12 @@ def bench_kmeans(args):
     rows = torch.as_tensor(datagen.init_rows(N, K, seed=wl.init_seed), device=dev)
     c = X[rows].contiguous()
     g = GMM(K, D, dev)
+    lists = os.environ.get("FLASHGMM_KMEANS_FUSED", "1").strip() == "0"
     if args.warmup > 0:
-        g.kmeans(X, c, args.warmup)
+        g.kmeans(X, c, args.warmup, lists=lists)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    _, counts, _, _ = g.kmeans(X, c, args.steps)
+    _, counts, _, _ = g.kmeans(X, c, args.steps, lists=lists)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms = dt * 1e3 / args.steps
@@ -201,9 +204,13 @@ def bench_kmeans(args):
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
             "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "data": "synthetic (seeded mixture, generated on the GPU)",
-            "config": {"workload": WORKLOAD_TEXT["kmeans"], "N": N, "K": K, "D": D},
+            "config": {"workload": WORKLOAD_TEXT["kmeans"], "N": N, "K": K, "D": D,
+                       "path": "lists" if lists else "fused"},
             "distance_tflops": round(useful / (dt / args.steps) / 1e12, 2),
-            "issued_logit_tflops": round(2 * 4.0 * N * K * D / (dt / args.steps) / 1e12, 2),
+            # MFMA work issued per iteration: the list path runs two logit sweeps
+            # over the 2D expanded features; the fused sweep runs the logits over
+            # D features and the (one-hot) statistics product over D
+            "issued_mfma_tflops": round((8.0 if lists else 4.0) * N * K * D / (dt / args.steps) / 1e12, 2),
             "empty_clusters": int((counts == 0).sum().item())}
     print(json.dumps(line), flush=True)
 

@@ -208,10 +208,16 @@ gmm_status gmm_fit_host(gmm_ctx *ctx, const float *X_host /*[host]*/, int64_t N,
  * comparison exact in float64 near ties), then every centre moves to the
  * mean of its rows; a centre with no rows keeps its position.  Centres are
  * float32 [dev] K x D, updated in place over iters iterations; counts [dev]
- * float64[K] receives the list sizes of the last assignment.  list_offsets
- * [dev] int64[K+1] and list_ids [dev] int32[N] are caller-owned scratch that
- * holds the last assignment as CSR lists (row ids ascending in each list).
- * The sums run in list order: deterministic.  N < 2^31.  Synchronises. */
+ * float64[K] receives the cluster sizes of the last assignment.
+ * Where the fused path applies (D <= 128, float32 or refined logits) an
+ * iteration is one sweep of the fused isotropic E-step kernel with one-hot
+ * responsibilities (the row's argmax exchanged like the log-sum-exp) and the
+ * centre sums accumulate like the E-step statistics (float32 within 2048-row
+ * windows, float64 across); list_offsets [dev] int64[K+1] and list_ids [dev]
+ * int32[N] may then be NULL, and if given receive the CSR lists of the rows'
+ * nearest returned centres (row ids ascending).  Elsewhere the iterations run
+ * through those lists (required then) with float64 sums in list order.
+ * Deterministic either way.  N < 2^31.  Synchronises. */
 gmm_status gmm_kmeans(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_t ldx, int32_t iters,
                       float *centres /*[dev] K*D in/out*/, double *counts /*[dev] K*/,
                       int64_t *list_offsets /*[dev] K+1*/, int32_t *list_ids /*[dev] N*/);

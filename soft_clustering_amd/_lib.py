@@ -319,17 +319,20 @@ class GMM:
         return (torch.empty(self.K + 1, dtype=torch.int64, device=self.device),
                 torch.empty(max(N, 1), dtype=torch.int32, device=self.device))
 
-    def kmeans(self, X, centres, iters):
+    def kmeans(self, X, centres, iters, lists=True):
         """Lloyd iterations in place on centres (K x D float32); returns
-        (centres, counts float64[K], offsets, ids) of the last assignment."""
+        (centres, counts float64[K], offsets, ids).  With lists the CSR lists
+        of the rows' nearest returned centres come back (one more assignment
+        sweep); without them offsets and ids are None, which only the fused
+        path accepts."""
         N, ldx = _rows(X, self.D, self.device)
         _need(centres, torch.float32, (self.K, self.D), "centres", self.device)
         counts = torch.zeros(self.K, dtype=torch.float64, device=self.device)
-        offsets, ids = self._list_scratch(N)
+        offsets, ids = self._list_scratch(N) if lists else (None, None)
         with torch.cuda.device(self.device):
             self._check(_lib.gmm_kmeans(self._h, _ptr(X), N, ldx, int(iters), _ptr(centres), _ptr(counts),
                                         _ptr(offsets), _ptr(ids)))
-        return centres, counts, offsets, ids[:N]
+        return centres, counts, offsets, (ids[:N] if lists else None)
 
     def init_kmeans(self, X, centres, var_floor, isotropic=False):
         """(weights, means, vars) of the mixture seeded from the clustering."""

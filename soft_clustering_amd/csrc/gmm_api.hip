@@ -126,13 +126,14 @@ bool want_fused(const gmm_ctx* c) {
 // kernel runs where it applies (else the diagonal kernels on the broadcast)
 gmm_status estep_into(gmm_ctx* c, const float* X, int64_t N, int64_t ldx, const float* w, const float* mu,
                       const float* var, double* Nk, double* S1, double* S2, double* ll, int accumulate,
-                      const float* var_iso = nullptr) {
+                      const float* var_iso = nullptr, bool hard = false) {
   hipStream_t s = c->stream;
   hipError_t e = gmm::launch_precompute(c->plan, c->ws, w, mu, var, s);
   if (e != hipSuccess) return hip_fail(c, e, "precompute launch");
   const bool fused = want_fused(c);
   const char* envi = getenv("FLASHGMM_ISO_KERNEL");  // 0: diagonal kernels on the broadcast (measurements)
-  const bool iso = var_iso && fused && gmm::iso_kernel_ok(c->plan, c->ws) && !(envi && atoi(envi) == 0);
+  const bool iso = var_iso && fused && gmm::iso_kernel_ok(c->plan, c->ws, hard) && !(envi && atoi(envi) == 0);
+  if (hard && !iso) return fail(c, GMM_ERR_UNSUPPORTED, "no fused k-means kernel for this shape");
   if (iso) {
     e = gmm::launch_precompute_iso(c->plan, c->ws, mu, var_iso, s);
     if (e != hipSuccess) return hip_fail(c, e, "precompute launch");
@@ -142,7 +143,8 @@ gmm_status estep_into(gmm_ctx* c, const float* X, int64_t N, int64_t ldx, const 
   hk.after = hook_after;
   hk.user = c;
   int nslots = 0;
-  e = gmm::launch_estep(c->plan, c->ws, X, N, ldx, fused, s, c->prof ? &hk : nullptr, &nslots, iso);
+  e = gmm::launch_estep(c->plan, c->ws, X, N, ldx, fused, s, c->prof ? &hk : nullptr, &nslots,
+                        iso ? (hard ? 2 : 1) : 0);
   if (e != hipSuccess) return hip_fail(c, e, fused ? "fused E-step launch" : "two-sweep E-step launch");
   e = gmm::launch_reduce(c->plan, c->ws, Nk, S1, S2, ll, accumulate, nslots, fused ? nslots : c->plan.Glogz, N,
                          s);
@@ -222,6 +224,7 @@ gmm_status gmm_create(gmm_ctx** out, int32_t K, int32_t D, void* hip_stream) {
   c->ws.vexp = carve<float>(q, (size_t)p.K * p.D);
   c->ws.qiso = carve<double>(q, p.K);
   c->ws.wuni = carve<float>(q, p.K);
+  c->ws.vhalf = carve<float>(q, p.K);
   c->ws.wiso = carve<float>(q, (size_t)p.Kpad * p.Dp);
   c->ws.ivec = carve<float>(q, p.Kpad);
   c->ws.wop64 = carve<double>(q, (size_t)p.Kpad * 2 * p.Dp);
@@ -646,11 +649,11 @@ gmm_status check_host_x(gmm_ctx* c, const float* Xh, int64_t N, int64_t ldx, int
 }
 
 gmm_status kmeans_check(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, const float* centres,
-                        const int64_t* offsets, const int32_t* ids) {
+                        const int64_t* offsets, const int32_t* ids, bool lists_required = true) {
   gmm_status st = check_x(ctx, X, N, ldx);
   if (st) return st;
   if (!centres || !aligned16(centres)) return fail(ctx, GMM_ERR_INVALID_ARG, "centres must be non-NULL, 16-byte aligned");
-  if (!offsets || !ids) return fail(ctx, GMM_ERR_INVALID_ARG, "list scratch must be non-NULL");
+  if (lists_required && (!offsets || !ids)) return fail(ctx, GMM_ERR_INVALID_ARG, "list scratch must be non-NULL");
   if (N >= ((int64_t)1 << 31)) return fail(ctx, GMM_ERR_INVALID_ARG, "N must be < 2^31 for int32 ids");
   return GMM_OK;
 }
@@ -699,10 +702,37 @@ gmm_status gmm_fit_host(gmm_ctx* ctx, const float* X_host, int64_t N, int64_t ld
 gmm_status gmm_kmeans(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, int32_t iters, float* centres,
                       double* counts, int64_t* list_offsets, int32_t* list_ids) {
   if (!ctx) return GMM_ERR_INVALID_ARG;
-  gmm_status st = kmeans_check(ctx, X, N, ldx, centres, list_offsets, list_ids);
+  gmm_status st = kmeans_check(ctx, X, N, ldx, centres, list_offsets, list_ids, false);
   if (st) return st;
   if (iters < 1) return fail(ctx, GMM_ERR_INVALID_ARG, "iters must be >= 1");
   if (!counts) return fail(ctx, GMM_ERR_INVALID_ARG, "counts is NULL");
+  const gmm::Plan& p = ctx->plan;
+  const char* envk = getenv("FLASHGMM_KMEANS_FUSED");  // 0: the list path (measurements)
+  if (want_fused(ctx) && gmm::iso_kernel_ok(p, ctx->ws, true) && !(envk && atoi(envk) == 0)) {
+    // one fused sweep per iteration: nearest centre (exchanged argmax),
+    // one-hot statistics, then centres = S1 / n
+    double* Nk = ctx->ws.stats;
+    double* S1 = Nk + p.K;
+    double* S2 = S1 + (size_t)p.K * p.D;
+    double* ll = S2 + (size_t)p.K * p.D;
+    for (int it = 0; it < iters; ++it) {
+      hipError_t e = gmm::launch_kmeans_params(p, ctx->ws, centres, ctx->stream);
+      if (e != hipSuccess) return hip_fail(ctx, e, "k-means set-up");
+      st = estep_into(ctx, X, N, ldx, ctx->ws.wuni, centres, ctx->ws.vexp, Nk, S1, S2, ll, 0, ctx->ws.vhalf, true);
+      if (st) return st;
+      e = gmm::launch_kmeans_update(p, Nk, S1, centres, counts, ctx->stream);
+      if (e != hipSuccess) return hip_fail(ctx, e, "centroid update");
+    }
+    if (list_offsets && list_ids) {  // the rows' lists for the returned centres
+      st = kmeans_assign(ctx, X, N, ldx, centres, list_offsets, list_ids);
+      if (st) return st;
+    }
+    hipError_t e = hipStreamSynchronize(ctx->stream);
+    if (e != hipSuccess) return hip_fail(ctx, e, "k-means");
+    return gmm_check(ctx);
+  }
+  if (!list_offsets || !list_ids)
+    return fail(ctx, GMM_ERR_INVALID_ARG, "this shape runs k-means through the lists: list scratch is required");
   for (int it = 0; it < iters; ++it) {
     st = kmeans_assign(ctx, X, N, ldx, centres, list_offsets, list_ids);
     if (st) return st;

@@ -42,6 +42,13 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp<0xB1>(v));
   return v;
 }
+__device__ __forceinline__ float row16_min(float v) {
+  v = fminf(v, dpp<0x140>(v));
+  v = fminf(v, dpp<0x141>(v));
+  v = fminf(v, dpp<0x4E>(v));
+  v = fminf(v, dpp<0xB1>(v));
+  return v;
+}
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp<0x140>(v);
   v += dpp<0x141>(v);

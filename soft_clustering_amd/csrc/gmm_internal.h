@@ -63,6 +63,7 @@ struct Workspace {
   float* vexp;       // K * D  isotropic variances broadcast over the dimensions
   double* qiso;      // K      isotropic Q_k of gmm_fit_iso
   float* wuni;       // K      k-means: equal weights
+  float* vhalf;      // K      k-means: isotropic variances 1/2
   float* wiso;       // Kpad * Dp  isotropic kernel: mu / s^2 in MFMA-operand order
   float* ivec;       // Kpad       isotropic kernel: 1 / (2 s^2)
   int colG;
@@ -91,10 +92,13 @@ struct LaunchHooks {
   void* user = nullptr;
 };
 // *nslots receives the number of statistics slots (row groups) written.
-// iso: the fused isotropic kernel (iso_kernel_ok; launch_precompute_iso first)
+// variant (fused path): 0 diagonal, 1 isotropic, 2 isotropic with hard
+// (k-means) assignment; 1 and 2 need iso_kernel_ok and launch_precompute_iso
 hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx,
-                        bool fused, hipStream_t s, const LaunchHooks* hooks, int* nslots, bool iso = false);
-bool iso_kernel_ok(const Plan& p, const Workspace& w);
+                        bool fused, hipStream_t s, const LaunchHooks* hooks, int* nslots, int variant = 0);
+bool iso_kernel_ok(const Plan& p, const Workspace& w, bool hard);
+hipError_t launch_kmeans_update(const Plan& p, const double* Nk, const double* S1, float* centres, double* counts,
+                                hipStream_t s);
 hipError_t launch_precompute_iso(const Plan& p, const Workspace& w, const float* means, const float* var_iso,
                                  hipStream_t s);
 hipError_t launch_reduce(const Plan& p, const Workspace& w, double* Nk, double* S1, double* S2,

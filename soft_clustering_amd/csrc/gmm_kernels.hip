@@ -101,6 +101,64 @@ __device__ __forceinline__ void xgather(const EArgs& a, int rg, int j, int rd, f
   }
 }
 
+// Exchange of one (value, component) pair per row for the hard (argmax)
+// mode: the word holds a 16-bit tile tag (tiles mod 65535, plus 1, so the
+// tile two back on the same slot differs), the 16-bit component and the
+// float; the gather keeps the largest value, the lowest component on ties.
+template <int BN, int QP>
+__device__ __forceinline__ void row_exchange_arg(const EArgs& a, int rg, int p, int j, const float* vin,
+                                                 const int* kin, float (*exm)[BN], int (*exk)[BN], float* vout,
+                                                 int* kout) {
+  const int tid = threadIdx.x;
+  const unsigned long long tag = (unsigned long long)((unsigned)j % 65535u + 1u);
+  unsigned long long* xb = a.xbuf + ((size_t)((rg * 2 + 1) * 2 + (j & 1)) * a.P) * BN;
+  if (tid < BN) {
+    const unsigned long long word = (tag << 48) | ((unsigned long long)(kin[tid] & 0xFFFF) << 32) |
+                                    (unsigned long long)__float_as_uint(vin[tid]);
+    __hip_atomic_store(xb + (size_t)p * BN + tid, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (tid < QP * BN) {
+    const int pt = tid % BN, qp = tid / BN;
+    float M = kNegInf;
+    int Kb = 0x7fffffff;
+    for (int q = qp; q < a.P; q += QP) {
+      const unsigned long long* src = xb + (size_t)q * BN + pt;
+      unsigned long long word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int spins = 0; (word >> 48) != tag; ++spins) {  // bounded wait, as in xgather
+        if ((spins & 255) == 0 && __hip_atomic_load(&a.flags[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+          break;
+        if (spins > (1 << 20)) {
+          __hip_atomic_store(&a.flags[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      const float val = __uint_as_float((unsigned)(word & 0xffffffffu));
+      const int kk = (int)((word >> 32) & 0xFFFF);
+      if (val > M || (val == M && kk < Kb)) {
+        M = val;
+        Kb = kk;
+      }
+    }
+    exm[qp][pt] = M;
+    exk[qp][pt] = Kb;
+  }
+  __syncthreads();
+  if (tid < BN) {
+    float M = kNegInf;
+    int Kb = 0x7fffffff;
+#pragma unroll
+    for (int k = 0; k < QP; ++k)
+      if (exm[k][tid] > M || (exm[k][tid] == M && exk[k][tid] < Kb)) {
+        M = exm[k][tid];
+        Kb = exk[k][tid];
+      }
+    vout[tid] = M;
+    kout[tid] = Kb;
+  }
+}
+
 template <int BN, int QP, bool LSE>
 __device__ __forceinline__ void row_exchange(const EArgs& a, int rg, int p, int j, int rd, const float* vin,
                                              float (*exm)[BN], float (*exs)[BN], float* vout) {
@@ -116,11 +174,20 @@ __device__ __forceinline__ void row_exchange(const EArgs& a, int rg, int p, int 
 // accumulated like N_k; S1 lands in the slots' x positions, Q in the x^2
 // position of dim 0 and zeros in the other x^2 positions, so the diagonal
 // reduction yields N_k, S1 and Q = sum_d S2_kd.
-template <int WC, int WD, int DPW, int BN, bool FUSED, int MODE, bool ISO = false>
+//
+// HARD (with ISO): the k-means step.  Responsibilities are one-hot at the
+// row's largest logit (lowest component on ties) instead of the softmax: the
+// refinement threshold is the row's largest lower bound itself (every
+// component that can be the argmax is recomputed in float64), the second
+// exchange round carries (max, argmax) pairs, and no log-likelihood is
+// accumulated.  With equal weights and variances 1/2 the largest logit is the
+// nearest centre.
+template <int WC, int WD, int DPW, int BN, bool FUSED, int MODE, bool ISO = false, bool HARD = false>
 __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats(EArgs a) {
   using SH = Shape<WC, WD, DPW, BN>;
   constexpr bool REFINE = MODE == MODE_REFINE, F64 = MODE == MODE_FP64;
   static_assert(!ISO || (FUSED && WD == 1 && !F64), "isotropic kernel: fused path, WD = 1, float32 logits");
+  static_assert(!HARD || ISO, "hard assignment: isotropic kernel");
   constexpr int NPB = SH::NPB;
   constexpr int NFB = ISO ? DPW / 16 : SH::NFB;  // statistics feature blocks
   constexpr int FLUSH = (BN >= 64) ? 32 : 128;  // tiles between fp64 flushes (2048 rows)
@@ -143,6 +210,9 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   __shared__ float rlist[SH::COOP ? WC : WC * WD][kRefineCap];  // refinement lists (per group or wave)
   __shared__ unsigned short elist[SH::COOP ? WC : WC * WD][kRefineCap];
   __shared__ __attribute__((aligned(16))) float xn2[ISO ? BN : 4];  // ISO: ||x||^2 of the tile's rows
+  __shared__ int lidx[HARD ? WC : 1][BN];                             // HARD: per-wave argmax
+  __shared__ int exk[HARD ? QP : 1][BN];
+  __shared__ int garg[HARD ? BN : 1];                                 // HARD: the row's argmax
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wc = w % WC, wd = w / WC;
@@ -324,7 +394,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
           vtmp[tid] = m;
         }
         row_exchange<BN, QP, false>(a, rg, p, j, 0, vtmp, exm, exs, thrs);
-        if (tid < BN) thrs[tid] = (tid < rows) ? thrs[tid] - kDelta : kPosInf;
+        if (tid < BN) thrs[tid] = (tid < rows) ? thrs[tid] - (HARD ? 0.f : kDelta) : kPosInf;
       } else {
         // reference: the row's final log Z from the first sweep
         if (tid < BN) thrs[tid] = ((tid < rows) ? a.logz[trow + tid] : kPosInf) - kDelta;
@@ -333,8 +403,37 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
       refine_tile<SH, WD, DPW>(acc, thrs, nrm, co, xt[cur], rows, a, C, compbase, rlist[SH::COOP ? wc : w], elist[SH::COOP ? wc : w], lane, wd, nsel);
     }
 
-    // ---- per-row log Z
-    if constexpr (FUSED) {
+    // ---- per-row log Z (HARD: the row's argmax)
+    if constexpr (HARD) {
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float m = row16_max(fmaxf(acc[pb][0][v], acc[pb][1][v]));
+          // lowest lane of the DPP row holding m, block 0 before block 1
+          const float i0 = row16_min((acc[pb][0][v] == m) ? (float)r16 : 64.f);
+          const float i1 = row16_min((acc[pb][1][v] == m) ? (float)r16 : 64.f);
+          if (r16 == 0) {
+            lpart[wc][pb * 16 + 4 * g + v] = m;
+            lidx[wc][pb * 16 + 4 * g + v] = compbase + (i0 < 16.f ? (int)i0 : (i1 < 16.f ? 16 + (int)i1 : 0));
+          }
+        }
+      __syncthreads();
+      if (tid < BN) {
+        float M = lpart[0][tid];
+        int Kb = lidx[0][tid];
+#pragma unroll
+        for (int k = 1; k < WC; ++k)
+          if (lpart[k][tid] > M) {
+            M = lpart[k][tid];
+            Kb = lidx[k][tid];
+          }
+        vtmp[tid] = M;
+        garg[tid] = Kb;
+      }
+      row_exchange_arg<BN, QP>(a, rg, p, j, vtmp, garg, exm, exk, lzt, garg);
+      if (tid < BN && tid >= rows) garg[tid] = -1;
+    } else if constexpr (FUSED) {
       if (wd == 0) {
 #pragma unroll
         for (int pb = 0; pb < NPB; ++pb)
@@ -396,8 +495,14 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
       const f4 lz = *reinterpret_cast<const f4*>(lzt + pb * 16 + 4 * g);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        acc[pb][0][v] = __expf(acc[pb][0][v] - lz[v]);
-        acc[pb][1][v] = __expf(acc[pb][1][v] - lz[v]);
+        if constexpr (HARD) {
+          const int k = garg[pb * 16 + 4 * g + v];
+          acc[pb][0][v] = (compbase + r16 == k) ? 1.f : 0.f;
+          acc[pb][1][v] = (compbase + 16 + r16 == k) ? 1.f : 0.f;
+        } else {
+          acc[pb][0][v] = __expf(acc[pb][0][v] - lz[v]);
+          acc[pb][1][v] = __expf(acc[pb][1][v] - lz[v]);
+        }
         nk0 += acc[pb][0][v];
         nk1 += acc[pb][1][v];
       }
@@ -899,6 +1004,19 @@ __global__ void k_iso_init_var(const double* __restrict__ colvar, int D, float f
 //           means_k = centres_k, vars = population variance of the rows
 //           about the centre (colvar, the variance of all rows, for an empty
 //           list), averaged over the dimensions when iso, floored.
+// centres_k = S1_k / n_k (n_k, exact counts of the one-hot responsibilities)
+// for every centre with rows; the others keep their position
+__global__ void k_kmeans_update(const double* __restrict__ Nk, const double* __restrict__ S1, float* centres,
+                                double* counts, int K, int D) {
+  const size_t total = (size_t)K * D;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int k = (int)(i / D);
+    const double n = Nk[k];
+    if (n >= 0.5) centres[i] = (float)(S1[i] / n);
+    if (i - (size_t)k * D == 0) counts[k] = n;
+  }
+}
+
 __global__ void k_fill_f32(float* __restrict__ p, size_t n, float v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
@@ -1055,13 +1173,19 @@ struct Kern {
     if constexpr (WD == 1) return (void*)&k_stats<WC, WD, DPW, BN, true, M, true>;
     else return nullptr;
   }
+  template <int M>
+  static void* stats_hard() {
+    if constexpr (WD == 1) return (void*)&k_stats<WC, WD, DPW, BN, true, M, true, true>;
+    else return nullptr;
+  }
 };
 
 // Kernel variants of one shape, indexed by logit precision mode (the fused
 // kernel has no float64-logit variant: that mode runs the two-sweep path).
 struct KTab {
   void* fused[2];
-  void* iso[2];  // fused isotropic kernels (nullptr where not built)
+  void* iso[2];   // fused isotropic kernels (nullptr where not built)
+  void* hard[2];  // fused k-means (hard assignment) kernels
   void* two[3];
   void* logz[3];
 };
@@ -1072,6 +1196,7 @@ static bool lookup(int WC, int WD, int DPW, KTab& t) {
     using KK = Kern<wc, wd, dpw>;                                                                     \
     t = KTab{{KK::stats_fused<0>(), KK::stats_fused<1>()},                                             \
              {KK::stats_iso<0>(), KK::stats_iso<1>()},                                                 \
+             {KK::stats_hard<0>(), KK::stats_hard<1>()},                                               \
              {KK::stats_two<0>(), KK::stats_two<1>(), KK::stats_two<2>()},                                \
              {KK::logz<0>(), KK::logz<1>(), KK::logz<2>()}};                                              \
     return true;                                                                                      \
@@ -1157,7 +1282,7 @@ size_t workspace_bytes(const Plan& p) {
   b += up((size_t)p.Kpad * p.Dp * 16) + up((size_t)p.Kpad * 8) + up(8);
   b += up((size_t)p.Kpad * 2 * p.Dp * 8) + up((size_t)p.Kpad * 8);  // wop64, cvec64
   b += up((size_t)p.K * p.D * 4) + up((size_t)p.K * 8);  // isotropic: broadcast variances, Q
-  b += up((size_t)p.K * 4);  // k-means: equal weights
+  b += 2 * up((size_t)p.K * 4);  // k-means: equal weights, variances 1/2
   b += up((size_t)p.Kpad * p.Dp * 4) + up((size_t)p.Kpad * 4);  // isotropic kernel: W, 1/(2 s^2)
   b += up((size_t)p.R * p.Kpad * p.SR * 8);
   b += up((size_t)(p.R > p.Glogz ? p.R : p.Glogz) * 8);
@@ -1186,10 +1311,11 @@ hipError_t occupancy(const Plan& p, int* occStats, int* occLogz) {
   int o1b = 0, o2b = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1, (const void*)t.fused[0], nt, 0);
   if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1b, (const void*)t.fused[1], nt, 0);
-  for (int m = 0; m < 2 && e == hipSuccess; ++m) {
-    if (!t.iso[m]) continue;
+  for (int m = 0; m < 4 && e == hipSuccess; ++m) {
+    void* kk = (m < 2) ? t.iso[m] : t.hard[m - 2];
+    if (!kk) continue;
     int oi = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&oi, (const void*)t.iso[m], nt, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&oi, (const void*)kk, nt, 0);
     if (oi < o1b) o1b = oi;
   }
   if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o2, (const void*)t.logz[0], nt, 0);
@@ -1264,9 +1390,10 @@ __global__ void k_fill_u64(unsigned long long* p, size_t n) {
     p[i] = 0ull;
 }
 
-bool iso_kernel_ok(const Plan& p, const Workspace& w) {
+bool iso_kernel_ok(const Plan& p, const Workspace& w, bool hard) {
   KTab t;
-  return !w.f64 && lookup(p.WC, p.WD, p.DPW, t) && t.iso[w.refine ? 1 : 0] != nullptr;
+  if (w.f64 || !lookup(p.WC, p.WD, p.DPW, t)) return false;
+  return (hard ? t.hard[w.refine ? 1 : 0] : t.iso[w.refine ? 1 : 0]) != nullptr;
 }
 
 hipError_t launch_precompute_iso(const Plan& p, const Workspace& w, const float* means, const float* var_iso,
@@ -1278,7 +1405,7 @@ hipError_t launch_precompute_iso(const Plan& p, const Workspace& w, const float*
 }
 
 hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx, bool fused,
-                        hipStream_t s, const LaunchHooks* hk, int* nslots, bool iso) {
+                        hipStream_t s, const LaunchHooks* hk, int* nslots, int variant) {
   auto pre = [&](int which) {
     if (hk && hk->before) hk->before(hk->user, which, s);
   };
@@ -1300,8 +1427,8 @@ hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64
     hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(nx, 256)), dim3(256), 0, s, w.xbuf, nx);
     void* args[] = {&a};
     pre(0);
-    void* kern = (iso && t.iso[mode]) ? t.iso[mode] : t.fused[mode];
-    if (iso && !t.iso[mode]) return hipErrorInvalidValue;
+    void* kern = (variant == 2) ? t.hard[mode] : (variant == 1) ? t.iso[mode] : t.fused[mode];
+    if (!kern) return hipErrorInvalidValue;
     hipError_t e = hipLaunchCooperativeKernel(kern, dim3(p.G), dim3(nt), args, 0, s);
     if (e != hipSuccess) return e;
     post(0);
@@ -1380,6 +1507,13 @@ hipError_t launch_fill_zero(double* p, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_kmeans_update(const Plan& p, const double* Nk, const double* S1, float* centres, double* counts,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(k_kmeans_update, dim3(grid_for((size_t)p.K * p.D, 256)), dim3(256), 0, s, Nk, S1, centres,
+                     counts, p.K, p.D);
+  return hipGetLastError();
+}
+
 hipError_t launch_kmeans_params(const Plan& p, const Workspace& w, const float* centres, hipStream_t s) {
   // equal weights and variances 1/2: the logit of centre k is a constant
   // minus the squared distance to it
@@ -1387,6 +1521,7 @@ hipError_t launch_kmeans_params(const Plan& p, const Workspace& w, const float* 
                      1.0f / (float)p.K);
   hipLaunchKernelGGL(k_fill_f32, dim3(grid_for((size_t)p.K * p.D, 256)), dim3(256), 0, s, w.vexp,
                      (size_t)p.K * p.D, 0.5f);
+  hipLaunchKernelGGL(k_fill_f32, dim3(grid_for((size_t)p.K, 256)), dim3(256), 0, s, w.vhalf, (size_t)p.K, 0.5f);
   return hipGetLastError();
 }
 
