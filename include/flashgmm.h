@@ -204,8 +204,10 @@ gmm_status gmm_fit_host(gmm_ctx *ctx, const float *X_host /*[host]*/, int64_t N,
 
 /* k-means warm start.  The pages seed their mixtures with k-means (the set-up
  * of the IVF experiments); the algorithm is Lloyd's: every row goes to its
- * nearest centre in squared Euclidean distance (lowest index on ties, the
- * comparison exact in float64 near ties), then every centre moves to the
+ * nearest centre in squared Euclidean distance (lowest index on ties; every
+ * candidate that can be nearest is recomputed in float64 and compared after
+ * rounding to float32, so the float64 order holds except between distances
+ * within about one float32 ulp), then every centre moves to the
  * mean of its rows; a centre with no rows keeps its position.  Centres are
  * float32 [dev] K x D, updated in place over iters iterations; counts [dev]
  * float64[K] receives the cluster sizes of the last assignment.

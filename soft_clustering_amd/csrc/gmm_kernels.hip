@@ -178,7 +178,8 @@ __device__ __forceinline__ void row_exchange(const EArgs& a, int rg, int p, int 
 // HARD (with ISO): the k-means step.  Responsibilities are one-hot at the
 // row's largest logit (lowest component on ties) instead of the softmax: the
 // refinement threshold is the row's largest lower bound itself (every
-// component that can be the argmax is recomputed in float64), the second
+// component that can be the argmax is recomputed in float64, then compared
+// as float32: the float64 order except within one float32 ulp), the second
 // exchange round carries (max, argmax) pairs, and no log-likelihood is
 // accumulated.  With equal weights and variances 1/2 the largest logit is the
 // nearest centre.
