@@ -83,6 +83,21 @@ typedef enum {
     GMM_PREC_FP64 = 2
 } gmm_precision;
 
+/* Matrix instructions of the first-pass logits under REFINED precision
+ * (gmm_set_logit_mfma); they decide which logits are recomputed in float64,
+ * never the values of those that matter.
+ * SPLIT_BF16 (default): every float of the contraction is split into two
+ *   bfloat16 (x = x_hi + x_lo, within 2^-16 |x|) and the contraction is
+ *   three bfloat16 MFMA passes (hi.hi + hi.lo + lo.hi), about 5x the fp32
+ *   MFMA throughput; the refinement's error bound includes the split error.
+ *   Used by the fused E-steps for D <= 128 (diagonal; isotropic and the
+ *   k-means hard assignment for D > 16); elsewhere FP32 runs.
+ * FP32: one fp32 MFMA pass. */
+typedef enum {
+    GMM_LOGIT_MFMA_SPLIT_BF16 = 0,
+    GMM_LOGIT_MFMA_FP32 = 1
+} gmm_logit_mfma;
+
 /* Create a context for K components of dimension D on the current HIP device.
  * hip_stream is a hipStream_t (NULL = the null stream).  Allocates the
  * workspace, whose size depends on K, D and the device but not on N (see
@@ -106,6 +121,16 @@ gmm_status gmm_set_path(gmm_ctx *ctx, int32_t path);
 
 /* Select the logit precision (gmm_precision) of later E-steps. */
 gmm_status gmm_set_precision(gmm_ctx *ctx, int32_t mode);
+
+/* Select the first-pass logit instructions (gmm_logit_mfma) of later
+ * E-steps. */
+gmm_status gmm_set_logit_mfma(gmm_ctx *ctx, int32_t kind);
+
+/* 1 if the E-step of ctx for model (0 diagonal, 1 isotropic, 2 the k-means
+ * hard assignment), with the context's current path, precision and logit
+ * setting, runs split-bfloat16 logits; 0 if not; -1 for NULL or an unknown
+ * model. */
+int32_t gmm_split_logits_active(const gmm_ctx *ctx, int32_t model);
 
 /* Initialisation (not on the pages, which warm-start from k-means):
  * means_k = X[init_rows[k]] for K distinct rows; every component gets the

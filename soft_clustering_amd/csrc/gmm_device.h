@@ -96,6 +96,9 @@ struct EArgs {
   // isotropic kernel: W = mu / s^2 in its MFMA-operand order, 1 / (2 s^2)
   const float* wiso;     // Kpad x Dp
   const float* ivec;     // Kpad  (0: padding)
+  // split-bf16 logits: W = W_hi + W_lo in bfloat16, in the operand order of
+  // v_mfma_f32_16x16x32_bf16 (see logit_tile_split)
+  const __bf16* wsp;     // Kpad x 2 Dp x 2
 };
 
 // ---------------------------------------------------------------------------
@@ -298,6 +301,137 @@ __device__ __forceinline__ void logit_tile(const float* __restrict__ xt, const f
     }
     b0 = b0n;
     b1 = b1n;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-bfloat16 logits.  A float x is carried as x_hi + x_lo with
+// x_hi = bf16(x) and x_lo = bf16(x - x_hi) (x - x_hi is exact in float32), so
+// |x - x_hi - x_lo| <= 2^-16 |x|; W likewise.  The logit contraction
+// sum_f x_f w_f is then three bfloat16 MFMA passes, x_hi w_hi + x_hi w_lo +
+// x_lo w_hi (products exact in float32, sums in float32), leaving out
+// x_lo w_lo: at most about 3 * 2^-16 |x_f w_f| per feature on top of the
+// float32 summation error of the 6 Dp partial products.  Each bfloat16 MFMA
+// covers 32 features at 16x the float32 MFMA rate, so the three passes cost
+// under a fifth of the float32 contraction.  The error bound of the float64
+// refinement is widened to match, so the refined results are unchanged.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f4 mfma_bf16(bf16x8 a, bf16x8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS layout of one split row (WD = 1): hi operands then lo operands, each
+// S MFMA steps x 4 lane groups x 8 features, plus 8 pad values (consecutive
+// rows 4 banks apart).  Diagonal model (S = DPW / 16): step s, lane group g
+// holds features x^2 (g even) or x (g odd) of dims (g / 2) * DPW / 2 + 8 s
+// .. + 7.  Isotropic model (x only, S = DPW / 32): lane group g holds dims
+// g * DPW / 4 + 8 s .. + 7.  Both keep the float32 kernels' assignment of
+// dims to lane groups, so W needs only regrouping.
+template <int DPW, bool ISO = false>
+struct SplitRow {
+  static constexpr int S = ISO ? DPW / 32 : DPW / 16;
+  static constexpr int LO = ISO ? DPW : 2 * DPW;  // bf16 offset of the lo operands
+  static constexpr int XSR = 2 * LO + 8;          // bf16 per row
+  static constexpr int WBLK = S * 2 * 512;        // bf16 of split W per 16-component block
+};
+
+// Convert the rows this wave staged (rows w, w + NW, ... of the tile: the
+// LDS-DMA row assignment with one instruction per row) from float32 in xt
+// to split bfloat16 operands in xsb.  Called after this wave's dma_wait, so
+// the rows it reads are its own DMA's; the next barrier publishes xsb.
+template <class SH, int DPW, bool ISO>
+__device__ __forceinline__ void split_rows(const float* __restrict__ xt, __bf16* __restrict__ xsb, int w) {
+  using SR = SplitRow<DPW, ISO>;
+  constexpr int BN = SH::TILE / SH::RS;
+  constexpr int NW = SH::NT / kWave;
+  constexpr int CH = DPW / 8;                 // 8-dim chunks per row
+  constexpr int RPW = (BN + NW - 1) / NW;     // rows per wave
+  constexpr int HS = DPW / 16;                // chunks per half (= S)
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int it = lane; it < RPW * CH; it += kWave) {
+    const int rl = it / CH, c = it - rl * CH;
+    const int pt = w + rl * NW;
+    if (pt < BN) {
+      const float* src = xt + pt * SH::RS + c * 8;
+      const f4 u0 = *reinterpret_cast<const f4*>(src);
+      const f4 u1 = *reinterpret_cast<const f4*>(src + 4);
+      __bf16* row = xsb + pt * SR::XSR;
+      bf16x8 xh, xl;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = (i < 4) ? u0[i] : u1[i - 4];
+        const __bf16 hx = (__bf16)x;
+        xh[i] = hx;
+        xl[i] = (__bf16)(x - (float)hx);
+      }
+      if constexpr (ISO) {
+        const int st = c % SR::S, gg = c / SR::S;  // step, lane group
+        *reinterpret_cast<bf16x8*>(row + (st * 4 + gg) * 8) = xh;
+        *reinterpret_cast<bf16x8*>(row + SR::LO + (st * 4 + gg) * 8) = xl;
+      } else {
+        bf16x8 qh, ql;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x = (i < 4) ? u0[i] : u1[i - 4];
+          const float q = x * x;
+          const __bf16 hq = (__bf16)q;
+          qh[i] = hq;
+          ql[i] = (__bf16)(q - (float)hq);
+        }
+        const int st = c % HS, gq = c / HS;  // step, half
+        *reinterpret_cast<bf16x8*>(row + (st * 4 + 2 * gq) * 8) = qh;
+        *reinterpret_cast<bf16x8*>(row + (st * 4 + 2 * gq + 1) * 8) = xh;
+        *reinterpret_cast<bf16x8*>(row + SR::LO + (st * 4 + 2 * gq) * 8) = ql;
+        *reinterpret_cast<bf16x8*>(row + SR::LO + (st * 4 + 2 * gq + 1) * 8) = xl;
+      }
+    }
+  }
+}
+
+// Logits of one wave (WD = 1) from the split operands: per step the W hi/lo
+// of both component blocks (fetched one step ahead from L2), per point block
+// the x hi/lo of 16 rows (one ds_read_b128 each), three MFMAs per block.
+// ws0/ws1: the two component blocks' split W, [step][hi, lo][lane][8].
+// acc must hold the starting value.
+template <class SH, int DPW, bool ISO>
+__device__ __forceinline__ void logit_tile_split(const __bf16* __restrict__ xsb, const __bf16* __restrict__ ws0,
+                                                 const __bf16* __restrict__ ws1, f4 (&acc)[SH::NPB][2], int lane) {
+  using SR = SplitRow<DPW, ISO>;
+  const int g = lane >> 4, r16 = lane & 15;
+  const __bf16* arow = xsb + r16 * SR::XSR + g * 8;
+  auto wl = [&](const __bf16* wb, int st, int hl) {
+    return *reinterpret_cast<const bf16x8*>(wb + ((st * 2 + hl) * kWave + lane) * 8);
+  };
+  bf16x8 h0 = wl(ws0, 0, 0), l0 = wl(ws0, 0, 1), h1 = wl(ws1, 0, 0), l1 = wl(ws1, 0, 1);
+#pragma unroll 2
+  for (int st = 0; st < SR::S; ++st) {
+    const int nx = (st + 1 < SR::S) ? st + 1 : st;
+    const bf16x8 h0n = wl(ws0, nx, 0), l0n = wl(ws0, nx, 1), h1n = wl(ws1, nx, 0), l1n = wl(ws1, nx, 1);
+    auto ld = [&](int pb, int off) {
+      return *reinterpret_cast<const bf16x8*>(arow + pb * 16 * SR::XSR + off + st * 32);
+    };
+    bf16x8 ahn = ld(0, 0), aln = ld(0, SR::LO);
+#pragma unroll
+    for (int pb = 0; pb < SH::NPB; ++pb) {
+      const bf16x8 ah = ahn, al = aln;
+      if (pb + 1 < SH::NPB) {
+        ahn = ld(pb + 1, 0);
+        aln = ld(pb + 1, SR::LO);
+      }
+      // small terms first
+      acc[pb][0] = mfma_bf16(al, h0, acc[pb][0]);
+      acc[pb][1] = mfma_bf16(al, h1, acc[pb][1]);
+      acc[pb][0] = mfma_bf16(ah, l0, acc[pb][0]);
+      acc[pb][1] = mfma_bf16(ah, l1, acc[pb][1]);
+      acc[pb][0] = mfma_bf16(ah, h0, acc[pb][0]);
+      acc[pb][1] = mfma_bf16(ah, h1, acc[pb][1]);
+    }
+    h0 = h0n;
+    l0 = l0n;
+    h1 = h1n;
+    l1 = l1n;
   }
 }
 

@@ -183,12 +183,17 @@ __device__ __forceinline__ void row_exchange(const EArgs& a, int rg, int p, int 
 // exchange round carries (max, argmax) pairs, and no log-likelihood is
 // accumulated.  With equal weights and variances 1/2 the largest logit is the
 // nearest centre.
-template <int WC, int WD, int DPW, int BN, bool FUSED, int MODE, bool ISO = false, bool HARD = false>
+template <int WC, int WD, int DPW, int BN, bool FUSED, int MODE, bool ISO = false, bool HARD = false,
+          bool SPLIT = false>
 __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats(EArgs a) {
   using SH = Shape<WC, WD, DPW, BN>;
   constexpr bool REFINE = MODE == MODE_REFINE, F64 = MODE == MODE_FP64;
   static_assert(!ISO || (FUSED && WD == 1 && !F64), "isotropic kernel: fused path, WD = 1, float32 logits");
   static_assert(!HARD || ISO, "hard assignment: isotropic kernel");
+  static_assert(!SPLIT || (FUSED && REFINE && WD == 1), "split-bf16 logits: fused refined kernels, WD = 1");
+  static_assert(!SPLIT || !ISO || DPW >= 32, "isotropic split logits: 8 dims per lane group and step");
+  using SPR = SplitRow<DPW, ISO>;
+  static_assert(!SPLIT || SH::CPR <= kWave, "split rows follow the one-instruction-per-row DMA assignment");
   constexpr int NPB = SH::NPB;
   constexpr int NFB = ISO ? DPW / 16 : SH::NFB;  // statistics feature blocks
   constexpr int FLUSH = (BN >= 64) ? 32 : 128;  // tiles between fp64 flushes (2048 rows)
@@ -214,6 +219,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   __shared__ int lidx[HARD ? WC : 1][BN];                             // HARD: per-wave argmax
   __shared__ int exk[HARD ? QP : 1][BN];
   __shared__ int garg[HARD ? BN : 1];                                 // HARD: the row's argmax
+  __shared__ __attribute__((aligned(16))) __bf16 xsb[SPLIT ? BN * SPR::XSR : 8];  // split operands
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wc = w % WC, wd = w / WC;
@@ -226,6 +232,8 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   const int cb16 = compbase >> 4;
   const float* w0 = ISO ? a.wiso + (size_t)cb16 * DPW * 16 : wop_block(a.wop, cb16, WD, wd, DPW);
   const float* w1 = ISO ? a.wiso + (size_t)(cb16 + 1) * DPW * 16 : wop_block(a.wop, cb16 + 1, WD, wd, DPW);
+  const __bf16* ws0 = SPLIT ? a.wsp + (size_t)cb16 * SPR::WBLK : nullptr;
+  const __bf16* ws1 = SPLIT ? a.wsp + (size_t)(cb16 + 1) * SPR::WBLK : nullptr;
   const float iv0 = ISO ? a.ivec[compbase + r16] : 0.f;  // 1 / (2 s^2) of the lane's components
   const float iv1 = ISO ? a.ivec[compbase + 16 + r16] : 0.f;
   float q0 = 0.f, q1 = 0.f;                              // ISO: Q partials
@@ -321,9 +329,20 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
       stg.store(buf);
     }
   };
+  // split operands of a freshly staged tile: each wave converts the rows its
+  // own DMA brought in (register staging: after a barrier, the same rows)
+  auto split_now = [&](const float* buf) {
+    if constexpr (SPLIT) {
+      if (!a.dma) __syncthreads();
+      split_rows<SH, DPW, ISO>(buf, xsb, w);
+    }
+  };
   int j = 0;
   int t = rg;
-  if (t < nt) stage_now(xt[0], t);
+  if (t < nt) {
+    stage_now(xt[0], t);
+    split_now(xt[0]);
+  }
   __syncthreads();
   for (; t < nt; t += a.R, ++j) {
     const int cur = (SH::NBUF == 2) ? (j & 1) : 0;
@@ -347,7 +366,8 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
       }
       if constexpr (ISO) {
         row_norms_iso<SH, DPW>(xt[cur], nrm, xn2);
-        logit_tile_iso<SH, DPW>(xt[cur], w0, w1, acc, lane);
+        if constexpr (SPLIT) logit_tile_split<SH, DPW, true>(xsb, ws0, ws1, acc, lane);
+        else logit_tile_iso<SH, DPW>(xt[cur], w0, w1, acc, lane);
         __syncthreads();  // xn2
 #pragma unroll
         for (int pb = 0; pb < NPB; ++pb) {
@@ -358,6 +378,8 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
             acc[pb][1][v] = fmaf(-iv1, n4[v], acc[pb][1][v]);
           }
         }
+      } else if constexpr (SPLIT) {
+        logit_tile_split<SH, DPW, false>(xsb, ws0, ws1, acc, lane);
       } else {
         logit_tile<SH, DPW>(xt[cur], w0, w1, acc, lane, wd);
         reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
@@ -546,6 +568,9 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
         if constexpr (SH::NBUF == 1) __syncthreads();  // every wave is done with the buffer
         stage_now(xt[(SH::NBUF == 2) ? (cur ^ 1) : 0], tn);
       }
+      // every wave finished this tile's logits (barriers since), so the
+      // split operands can be overwritten
+      split_now(xt[(SH::NBUF == 2) ? (cur ^ 1) : 0]);
     }
     if ((j + 1 + fphase) % FLUSH == 0) flush();
     __syncthreads();
@@ -731,6 +756,64 @@ __global__ void k_precompute_w(const float* __restrict__ mu, const float* __rest
       val = (gg & 1) ? (double)mu[(size_t)comp * D + dim] / s2 : -0.5 / s2;
     }
     wop[idx] = (T)val;
+  }
+}
+
+// The same [a | b] as split bfloat16 pairs (WD = 1) for logit_tile_split:
+// per 16-component block, [step][hi, lo][lane][8]; lane (g, r16) of step st
+// holds component r16's a (g even) or b (g odd) of dims
+// (g / 2) * DPW / 2 + 8 st .. + 7.  hi = bf16(w), lo = bf16(w - hi) of the
+// float32 value w.
+__global__ void k_precompute_wsplit(const float* __restrict__ mu, const float* __restrict__ var, __bf16* wsp,
+                                    int K, int D, int Kpad, int DPW) {
+  const int S = DPW / 16;
+  const size_t total = (size_t)Kpad * 2 * DPW;  // (hi, lo) pairs
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int cb = (int)(idx / ((size_t)S * 512));
+    int rem = (int)(idx - (size_t)cb * S * 512);
+    const int st = rem / 512;
+    rem -= st * 512;
+    const int lane = rem >> 3, jj = rem & 7;
+    const int gg = lane >> 4;
+    const int comp = cb * 16 + (lane & 15);
+    const int dim = (gg >> 1) * (DPW / 2) + st * 8 + jj;
+    double val = 0.0;
+    if (comp < K && dim < D) {
+      const double s2 = (double)var[(size_t)comp * D + dim];
+      val = (gg & 1) ? (double)mu[(size_t)comp * D + dim] / s2 : -0.5 / s2;
+    }
+    const float vf = (float)val;
+    const __bf16 hi = (__bf16)vf;
+    const size_t base = ((size_t)(cb * S + st) * 2) * 512 + (size_t)lane * 8 + jj;
+    wsp[base] = hi;
+    wsp[base + 512] = (__bf16)(vf - (float)hi);
+  }
+}
+
+// The isotropic W = mu / s^2 as split bfloat16 pairs for the isotropic kernel
+// with split logits: per 16-component block, [step][hi, lo][lane][8]; lane
+// (g, r16) of step st holds component r16's value for dims
+// g * DPW / 4 + 8 st .. + 7.
+__global__ void k_precompute_wsplit_iso(const float* __restrict__ mu, const float* __restrict__ var_iso,
+                                        __bf16* wsp, int K, int D, int Kpad, int DPW) {
+  const int S = DPW / 32, Q = DPW / 4;
+  const size_t total = (size_t)Kpad * DPW;  // (hi, lo) pairs
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int cb = (int)(idx / ((size_t)S * 512));
+    int rem = (int)(idx - (size_t)cb * S * 512);
+    const int st = rem / 512;
+    rem -= st * 512;
+    const int lane = rem >> 3, jj = rem & 7;
+    const int comp = cb * 16 + (lane & 15);
+    const int d = (lane >> 4) * Q + st * 8 + jj;
+    float vf = 0.f;
+    if (comp < K && d < D) vf = (float)((double)mu[(size_t)comp * D + d] / (double)var_iso[comp]);
+    const __bf16 hi = (__bf16)vf;
+    const size_t base = ((size_t)(cb * S + st) * 2) * 512 + (size_t)lane * 8 + jj;
+    wsp[base] = hi;
+    wsp[base + 512] = (__bf16)(vf - (float)hi);
   }
 }
 
@@ -1179,6 +1262,18 @@ struct Kern {
     if constexpr (WD == 1) return (void*)&k_stats<WC, WD, DPW, BN, true, M, true, true>;
     else return nullptr;
   }
+  static void* stats_split() {
+    if constexpr (WD == 1) return (void*)&k_stats<WC, WD, DPW, BN, true, MODE_REFINE, false, false, true>;
+    else return nullptr;
+  }
+  static void* stats_iso_split() {
+    if constexpr (WD == 1 && DPW >= 32) return (void*)&k_stats<WC, WD, DPW, BN, true, MODE_REFINE, true, false, true>;
+    else return nullptr;
+  }
+  static void* stats_hard_split() {
+    if constexpr (WD == 1 && DPW >= 32) return (void*)&k_stats<WC, WD, DPW, BN, true, MODE_REFINE, true, true, true>;
+    else return nullptr;
+  }
 };
 
 // Kernel variants of one shape, indexed by logit precision mode (the fused
@@ -1187,6 +1282,9 @@ struct KTab {
   void* fused[2];
   void* iso[2];   // fused isotropic kernels (nullptr where not built)
   void* hard[2];  // fused k-means (hard assignment) kernels
+  void* split;    // fused diagonal refined kernel with split-bf16 logits (nullptr where not built)
+  void* iso_split;   // the same for the isotropic kernel
+  void* hard_split;  // and its hard-assignment mode
   void* two[3];
   void* logz[3];
 };
@@ -1198,6 +1296,7 @@ static bool lookup(int WC, int WD, int DPW, KTab& t) {
     t = KTab{{KK::stats_fused<0>(), KK::stats_fused<1>()},                                             \
              {KK::stats_iso<0>(), KK::stats_iso<1>()},                                                 \
              {KK::stats_hard<0>(), KK::stats_hard<1>()},                                               \
+             KK::stats_split(), KK::stats_iso_split(), KK::stats_hard_split(),                         \
              {KK::stats_two<0>(), KK::stats_two<1>(), KK::stats_two<2>()},                                \
              {KK::logz<0>(), KK::logz<1>(), KK::logz<2>()}};                                              \
     return true;                                                                                      \
@@ -1285,6 +1384,8 @@ size_t workspace_bytes(const Plan& p) {
   b += up((size_t)p.K * p.D * 4) + up((size_t)p.K * 8);  // isotropic: broadcast variances, Q
   b += 2 * up((size_t)p.K * 4);  // k-means: equal weights, variances 1/2
   b += up((size_t)p.Kpad * p.Dp * 4) + up((size_t)p.Kpad * 4);  // isotropic kernel: W, 1/(2 s^2)
+  b += up((size_t)p.Kpad * 2 * p.Dp * 2 * 2);                     // split-bf16 W (hi, lo)
+  b += up((size_t)p.Kpad * p.Dp * 2 * 2);                         // the same, isotropic
   b += up((size_t)p.R * p.Kpad * p.SR * 8);
   b += up((size_t)(p.R > p.Glogz ? p.R : p.Glogz) * 8);
   b += up((size_t)p.chunk * 4);
@@ -1312,8 +1413,9 @@ hipError_t occupancy(const Plan& p, int* occStats, int* occLogz) {
   int o1b = 0, o2b = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1, (const void*)t.fused[0], nt, 0);
   if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1b, (const void*)t.fused[1], nt, 0);
-  for (int m = 0; m < 4 && e == hipSuccess; ++m) {
-    void* kk = (m < 2) ? t.iso[m] : t.hard[m - 2];
+  void* extra[3] = {t.split, t.iso_split, t.hard_split};
+  for (int m = 0; m < 7 && e == hipSuccess; ++m) {
+    void* kk = (m < 2) ? t.iso[m] : (m < 4) ? t.hard[m - 2] : extra[m - 4];
     if (!kk) continue;
     int oi = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&oi, (const void*)kk, nt, 0);
@@ -1348,6 +1450,9 @@ hipError_t launch_precompute(const Plan& p, const Workspace& w, const float* wei
                      p.D);
   hipLaunchKernelGGL(k_precompute_w64, dim3((p.Kpad + 3) / 4), dim3(256), 0, s, means, vars, w.w64, w.abmax,
                      p.K, p.D, p.Kpad, p.Dp);
+  if (p.WD == 1)
+    hipLaunchKernelGGL(k_precompute_wsplit, dim3(grid_for(total, 256)), dim3(256), 0, s, means, vars, w.wsplit,
+                       p.K, p.D, p.Kpad, p.DPW);
   return hipGetLastError();
 }
 
@@ -1383,12 +1488,19 @@ static EArgs make_args(const Plan& p, const Workspace& w, const float* X, int64_
   a.cvec64 = w.cvec64;
   a.wiso = w.wiso;
   a.ivec = w.ivec;
+  a.wsp = w.wsplit;
   return a;
 }
 
 __global__ void k_fill_u64(unsigned long long* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     p[i] = 0ull;
+}
+
+bool split_kernel_ok(const Plan& p, int variant) {
+  KTab t;
+  if (!lookup(p.WC, p.WD, p.DPW, t)) return false;
+  return (variant == 2 ? t.hard_split : variant == 1 ? t.iso_split : t.split) != nullptr;
 }
 
 bool iso_kernel_ok(const Plan& p, const Workspace& w, bool hard) {
@@ -1402,6 +1514,9 @@ hipError_t launch_precompute_iso(const Plan& p, const Workspace& w, const float*
   const size_t total = (size_t)p.Kpad * p.DPW;
   hipLaunchKernelGGL(k_precompute_wiso, dim3(grid_for(total, 256)), dim3(256), 0, s, means, var_iso, w.wiso,
                      w.ivec, p.K, p.D, p.Kpad, p.DPW);
+  if (p.WD == 1 && p.DPW >= 32)
+    hipLaunchKernelGGL(k_precompute_wsplit_iso, dim3(grid_for(total, 256)), dim3(256), 0, s, means, var_iso,
+                       w.wsplit_iso, p.K, p.D, p.Kpad, p.DPW);
   return hipGetLastError();
 }
 
@@ -1429,6 +1544,14 @@ hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64
     void* args[] = {&a};
     pre(0);
     void* kern = (variant == 2) ? t.hard[mode] : (variant == 1) ? t.iso[mode] : t.fused[mode];
+    void* ksplit = (variant == 2) ? t.hard_split : (variant == 1) ? t.iso_split : t.split;
+    if (mode == 1 && w.split && ksplit) {
+      // split-bf16 logits: at most 6 Dp exact partial products summed in
+      // float32, plus the split's own 3 * 2^-16 relative error per feature
+      kern = ksplit;
+      a.wsp = variant ? w.wsplit_iso : w.wsplit;
+      a.kappa = (float)((6.0 * p.Dp + 8.0) * 5.9604644775390625e-08 * (1.0 + 1.0 / 64.0) + 3.1 * 1.52587890625e-05);
+    }
     if (!kern) return hipErrorInvalidValue;
     hipError_t e = hipLaunchCooperativeKernel(kern, dim3(p.G), dim3(nt), args, 0, s);
     if (e != hipSuccess) return e;
