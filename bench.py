@@ -50,20 +50,26 @@ def useful_flops(N, K, D, iso=False):
 def mfma_roofline(N, K, D, split, iso=False):
     """Peak for the fused E-step: the rate at which the matrix pipes, fully
     busy with this kernel's MFMA instruction mix, would deliver its useful
-    flops.  fp32 logits: every contraction is fp32 MFMA, so the fp32 peak.
-    Split-bf16 logits: the logit contraction (2*N*K*F flops over F features:
-    F = 2D diagonal, D isotropic) is three bf16 passes at the bf16 peak and
-    the statistics contraction (2*N*K*F) fp32 at the fp32 peak; the peak is
-    the useful count over that busy time."""
+    flops.  split 0: every contraction fp32 MFMA, so the fp32 peak.  The
+    logit and statistics contractions take 2*N*K*F flops each over F
+    features (F = 2D diagonal, D isotropic).  split 1: the logits are three
+    bf16 passes at the bf16 peak, the statistics fp32 at the fp32 peak.
+    split 2: the statistics are six bf16 passes too.  The peak is the useful
+    count over that busy time."""
     if not split:
         return MFMA_FP32_PEAK_TFLOPS, "fp32 MFMA (all contractions fp32)"
     F = D if iso else 2 * D
-    t_busy = 3 * 2.0 * N * K * F / (MFMA_BF16_PEAK_TFLOPS * 1e12) + 2.0 * N * K * F / (MFMA_FP32_PEAK_TFLOPS * 1e12)
+    bf16_passes = 3 + (6 if split == 2 else 0)
+    t_busy = bf16_passes * 2.0 * N * K * F / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if split == 1:
+        t_busy += 2.0 * N * K * F / (MFMA_FP32_PEAK_TFLOPS * 1e12)
     peak = useful_flops(N, K, D, iso) / t_busy / 1e12
     f = "D" if iso else "2D"
+    stats = ("statistics as 6 bf16 passes (12*N*K*F at 2500 TFLOP/s)" if split == 2 else
+             "statistics in fp32 (2*N*K*F at 157.3 TFLOP/s)")
     return peak, (f"matrix pipes busy with this kernel's mix: logits over F={f} features as 3 bf16 passes "
-                  f"(6*N*K*F flops at 2500 TFLOP/s) + statistics in fp32 (2*N*K*F at 157.3 TFLOP/s); useful "
-                  f"N*K*({'4D+6' if iso else '8D+2'}) over that time")
+                  f"(6*N*K*F flops at 2500 TFLOP/s) + {stats}; useful N*K*({'4D+6' if iso else '8D+2'}) over "
+                  f"that time")
 
 
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -211,7 +217,7 @@ def bench_kmeans(args):
     c = X[rows].contiguous()
     g = GMM(K, D, dev)
     lists = os.environ.get("FLASHGMM_KMEANS_FUSED", "1").strip() == "0"
-    split = (not lists) and g.split_logits_active(2)
+    split = (not lists) and g.split_level(2) > 0
     if args.warmup > 0:
         g.kmeans(X, c, args.warmup, lists=lists)
     torch.cuda.synchronize()
@@ -226,7 +232,7 @@ def bench_kmeans(args):
             "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "data": "synthetic (seeded mixture, generated on the GPU)",
             "config": {"workload": WORKLOAD_TEXT["kmeans"], "N": N, "K": K, "D": D,
-                       "path": "lists" if lists else "fused", "logit_mfma": "split-bf16" if split else "fp32"},
+                       "path": "lists" if lists else "fused", "mfma": "split-bf16 logits" if split else "fp32"},
             "distance_tflops": round(useful / (dt / args.steps) / 1e12, 2),
             # MFMA work issued per iteration: the list path runs two logit sweeps
             # over the 2D expanded features; the fused sweep runs the logits over
@@ -248,8 +254,9 @@ def main():
     ap.add_argument("--precision", default=None, choices=["refined", "fp32", "fp64"],
                     help="logit precision (default: refined; fp64 for the embed workload, whose diffuse "
                          "responsibilities would have a large share of the logits refined)")
-    ap.add_argument("--logit-mfma", default="split", choices=["split", "fp32"],
-                    help="first-pass logit instructions under refined precision (split: split-bf16 passes)")
+    ap.add_argument("--mfma", default="split", choices=["split", "split-logits", "fp32"],
+                    help="matrix instructions of the fused refined E-step: split-bf16 logits and statistics, "
+                         "split-bf16 logits only, or fp32")
     ap.add_argument("--rows", type=int, default=0, help="override N (testing only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=250_000)
@@ -278,8 +285,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": 3}), flush=True)
         return
-    from soft_clustering_amd import (GMM, LOGIT_MFMA_FP32, LOGIT_MFMA_SPLIT_BF16, PATH_AUTO, PATH_FUSED, PATH_TWO_SWEEP,
-                                     PREC_FP32, PREC_FP64, PREC_REFINED, datagen)
+    from soft_clustering_amd import (GMM, MFMA_FP32, MFMA_SPLIT_BF16, MFMA_SPLIT_LOGITS, PATH_AUTO, PATH_FUSED,
+                                     PATH_TWO_SWEEP, PREC_FP32, PREC_FP64, PREC_REFINED, datagen)
 
     wl = datagen.WORKLOADS[args.workload]
     if args.precision is None:
@@ -300,8 +307,8 @@ def main():
     g = GMM(K, D, dev)
     g.set_path({"auto": PATH_AUTO, "fused": PATH_FUSED, "two_sweep": PATH_TWO_SWEEP}[args.path])
     g.set_precision({"refined": PREC_REFINED, "fp32": PREC_FP32, "fp64": PREC_FP64}[args.precision])
-    g.set_logit_mfma(LOGIT_MFMA_SPLIT_BF16 if args.logit_mfma == "split" else LOGIT_MFMA_FP32)
-    split = g.split_logits_active(1 if iso else 0)
+    g.set_mfma({"split": MFMA_SPLIT_BF16, "split-logits": MFMA_SPLIT_LOGITS, "fp32": MFMA_FP32}[args.mfma])
+    split = g.split_level(1 if iso else 0)
     init = g.init_iso if iso else g.init
     fit = g.fit_iso if iso else g.fit
     w, mu, var = init(X, datagen.init_rows(N, K, seed=wl.init_seed), wl.var_floor)
@@ -340,8 +347,8 @@ def main():
     hl = hist.cpu().numpy()
     peak, peak_basis = mfma_roofline(N, K, D, split, iso)
     traffic = None
-    if fused and split and args.workload == "large" and args.precision == "refined" and not args.rows:
-        traffic = measured_traffic()  # taken on the default kernel (split-bf16 logits)
+    if fused and split == 2 and args.workload == "large" and args.precision == "refined" and not args.rows:
+        traffic = measured_traffic()  # taken on the default kernel (split-bf16 logits and statistics)
     line = {
         "metric": "ms per EM iteration and GFLOP/s at N=100M,K=1024,D=128 fp32; % MFMA peak",
         "value": round(gflops, 1),
@@ -353,7 +360,7 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[args.workload] if not args.rows else
                    f"{args.workload} law with N={N}", "N": N, "K": K, "D": D,
                    "path": "fused" if fused else "two_sweep", "logit_precision": args.precision,
-                   "logit_mfma": "split-bf16" if split else "fp32",
+                   "mfma": ["fp32", "split-bf16 logits", "split-bf16 logits and statistics"][split],
                    "covariance": "isotropic" if iso else "diagonal"},
         "pct_fp32_mfma_peak": round(100 * gflops / (MFMA_FP32_PEAK_TFLOPS * 1e3), 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
@@ -361,7 +368,8 @@ def main():
                      "fp32_peak_frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4),
                      "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "kernel": ("k_stats (fused E-step" + (", split-bf16 logits)" if split else ")")) if fused
+                     "kernel": ("k_stats (fused E-step" + ["", ", split-bf16 logits", ", split-bf16 logits and statistics"][split]
+                                + ")") if fused
                      else "k_logz + k_stats (two-sweep E-step)",
                      "kernel_ms_per_iteration": round(kern_ms, 3),
                      "avg_launch_ms": round(avg_ms, 3), "launches": stats_n + logz_n},

@@ -83,20 +83,29 @@ typedef enum {
     GMM_PREC_FP64 = 2
 } gmm_precision;
 
-/* Matrix instructions of the first-pass logits under REFINED precision
- * (gmm_set_logit_mfma); they decide which logits are recomputed in float64,
- * never the values of those that matter.
- * SPLIT_BF16 (default): every float of the contraction is split into two
- *   bfloat16 (x = x_hi + x_lo, within 2^-16 |x|) and the contraction is
- *   three bfloat16 MFMA passes (hi.hi + hi.lo + lo.hi), about 5x the fp32
- *   MFMA throughput; the refinement's error bound includes the split error.
- *   Used by the fused E-steps for D <= 128 (diagonal; isotropic and the
- *   k-means hard assignment for D > 16); elsewhere FP32 runs.
- * FP32: one fp32 MFMA pass. */
+/* Matrix instructions of the fused E-step contractions (gmm_set_mfma).
+ * Under REFINED precision the first-pass logits may be split-bfloat16:
+ *   every float of the contraction is split into two bfloat16 (x = x_hi +
+ *   x_lo, within 2^-16 |x|) and the contraction is three bfloat16 MFMA
+ *   passes (hi.hi + hi.lo + lo.hi), about 5x the fp32 MFMA throughput; these
+ *   logits only decide which logits are recomputed in float64 (the error
+ *   bound includes the split error), never the values of those that matter.
+ * The statistics contraction may be split-bfloat16 in three parts: a
+ *   float32 value is exactly hi + mid + lo, and the six products of order up
+ *   to two (hi.hi, hi.mid, mid.hi, hi.lo, lo.hi, mid.mid) give float32-level
+ *   accuracy at about 2.7x the fp32 MFMA throughput.
+ * SPLIT_BF16 (default): split logits and split statistics where built (the
+ *   diagonal kernel); split logits alone elsewhere they are built.
+ * SPLIT_LOGITS: split logits, fp32 statistics.
+ * FP32: fp32 MFMA for both.
+ * Split logits are built for the fused E-steps with D <= 128 (diagonal;
+ * isotropic and the k-means hard assignment for D > 16), split statistics
+ * for the diagonal one; elsewhere FP32 runs. */
 typedef enum {
-    GMM_LOGIT_MFMA_SPLIT_BF16 = 0,
-    GMM_LOGIT_MFMA_FP32 = 1
-} gmm_logit_mfma;
+    GMM_MFMA_SPLIT_BF16 = 0,
+    GMM_MFMA_SPLIT_LOGITS = 1,
+    GMM_MFMA_FP32 = 2
+} gmm_mfma_kind;
 
 /* Create a context for K components of dimension D on the current HIP device.
  * hip_stream is a hipStream_t (NULL = the null stream).  Allocates the
@@ -122,15 +131,14 @@ gmm_status gmm_set_path(gmm_ctx *ctx, int32_t path);
 /* Select the logit precision (gmm_precision) of later E-steps. */
 gmm_status gmm_set_precision(gmm_ctx *ctx, int32_t mode);
 
-/* Select the first-pass logit instructions (gmm_logit_mfma) of later
- * E-steps. */
-gmm_status gmm_set_logit_mfma(gmm_ctx *ctx, int32_t kind);
+/* Select the matrix instructions (gmm_mfma_kind) of later E-steps. */
+gmm_status gmm_set_mfma(gmm_ctx *ctx, int32_t kind);
 
-/* 1 if the E-step of ctx for model (0 diagonal, 1 isotropic, 2 the k-means
- * hard assignment), with the context's current path, precision and logit
- * setting, runs split-bfloat16 logits; 0 if not; -1 for NULL or an unknown
- * model. */
-int32_t gmm_split_logits_active(const gmm_ctx *ctx, int32_t model);
+/* What the E-step of ctx for model (0 diagonal, 1 isotropic, 2 the k-means
+ * hard assignment) runs with the context's current path, precision and
+ * instruction setting: 0 fp32 MFMA, 1 split-bfloat16 logits, 2 split-bfloat16
+ * logits and statistics; -1 for NULL or an unknown model. */
+int32_t gmm_split_level(const gmm_ctx *ctx, int32_t model);
 
 /* Initialisation (not on the pages, which warm-start from k-means):
  * means_k = X[init_rows[k]] for K distinct rows; every component gets the

@@ -5,7 +5,7 @@ ctypes binding (argument marshalling only) and the seeded input generators.
 Importing it fails loudly when the library has not been built.
 """
 from ._lib import (GMM, GMMError, PATH_AUTO, PATH_FUSED, PATH_TWO_SWEEP, PREC_FP32, PREC_FP64, PREC_REFINED,  # noqa: F401
-                   LOGIT_MFMA_FP32, LOGIT_MFMA_SPLIT_BF16, EXPORTS, LIB_PATH, raw_library)
+                   MFMA_FP32, MFMA_SPLIT_BF16, MFMA_SPLIT_LOGITS, EXPORTS, LIB_PATH, raw_library)
 
 __all__ = ["GMM", "GMMError", "PATH_AUTO", "PATH_FUSED", "PATH_TWO_SWEEP", "PREC_FP32", "PREC_FP64", "PREC_REFINED",
-           "LOGIT_MFMA_FP32", "LOGIT_MFMA_SPLIT_BF16", "EXPORTS", "LIB_PATH", "raw_library"]
+           "MFMA_FP32", "MFMA_SPLIT_BF16", "MFMA_SPLIT_LOGITS", "EXPORTS", "LIB_PATH", "raw_library"]

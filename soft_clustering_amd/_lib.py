@@ -21,10 +21,10 @@ _STATUS = {0: "GMM_OK", 1: "GMM_ERR_INVALID_ARG", 2: "GMM_ERR_UNSUPPORTED", 3: "
            4: "GMM_ERR_HIP", 5: "GMM_ERR_NUMERIC", 6: "GMM_ERR_CAPACITY"}
 PATH_AUTO, PATH_TWO_SWEEP, PATH_FUSED = 0, 1, 2
 PREC_REFINED, PREC_FP32, PREC_FP64 = 0, 1, 2
-LOGIT_MFMA_SPLIT_BF16, LOGIT_MFMA_FP32 = 0, 1
+MFMA_SPLIT_BF16, MFMA_SPLIT_LOGITS, MFMA_FP32 = 0, 1, 2
 
 EXPORTS = ["gmm_create", "gmm_destroy", "gmm_last_error", "gmm_workspace_bytes", "gmm_set_path", "gmm_set_precision",
-           "gmm_set_logit_mfma", "gmm_split_logits_active",
+           "gmm_set_mfma", "gmm_split_level",
            "gmm_init", "gmm_estep_stats", "gmm_mstep", "gmm_fit", "gmm_soft_assign", "gmm_check",
            "gmm_init_iso", "gmm_estep_stats_iso", "gmm_mstep_iso", "gmm_fit_iso", "gmm_kmeans", "gmm_init_kmeans",
            "gmm_estep_stats_host", "gmm_fit_host",
@@ -49,8 +49,8 @@ def _load():
         "gmm_workspace_bytes": (ctypes.c_size_t, [i32, i32]),
         "gmm_set_path": (i32, [vp, i32]),
         "gmm_set_precision": (i32, [vp, i32]),
-        "gmm_set_logit_mfma": (i32, [vp, i32]),
-        "gmm_split_logits_active": (i32, [vp, i32]),
+        "gmm_set_mfma": (i32, [vp, i32]),
+        "gmm_split_level": (i32, [vp, i32]),
         "gmm_init": (i32, [vp, vp, i64, i64, vp, f32, vp, vp, vp]),
         "gmm_estep_stats": (i32, [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32]),
         "gmm_mstep": (i32, [vp, vp, vp, vp, f64, f32, vp, vp, vp]),
@@ -160,12 +160,14 @@ class GMM:
     def set_precision(self, mode: int):
         self._check(_lib.gmm_set_precision(self._h, int(mode)))
 
-    def set_logit_mfma(self, kind: int):
-        self._check(_lib.gmm_set_logit_mfma(self._h, int(kind)))
+    def set_mfma(self, kind: int):
+        self._check(_lib.gmm_set_mfma(self._h, int(kind)))
 
-    def split_logits_active(self, model: int = 0) -> bool:
-        """model: 0 diagonal, 1 isotropic, 2 k-means hard assignment."""
-        return _lib.gmm_split_logits_active(self._h, int(model)) == 1
+    def split_level(self, model: int = 0) -> int:
+        """0 fp32 MFMA, 1 split-bf16 logits, 2 split-bf16 logits and
+        statistics; model: 0 diagonal, 1 isotropic, 2 k-means hard
+        assignment."""
+        return int(_lib.gmm_split_level(self._h, int(model)))
 
     def params(self):
         """Fresh fp32 (weights, means, vars) buffers on the device."""

@@ -229,7 +229,7 @@ gmm_status gmm_create(gmm_ctx** out, int32_t K, int32_t D, void* hip_stream) {
   c->ws.ivec = carve<float>(q, p.Kpad);
   c->ws.wsplit = carve<__bf16>(q, (size_t)p.Kpad * 2 * p.Dp * 2);
   c->ws.wsplit_iso = carve<__bf16>(q, (size_t)p.Kpad * p.Dp * 2);
-  c->ws.split = 1;
+  c->ws.split = 2;
   c->ws.wop64 = carve<double>(q, (size_t)p.Kpad * 2 * p.Dp);
   c->ws.cvec64 = carve<double>(q, p.Kpad);
   c->ws.f64 = 0;
@@ -345,19 +345,20 @@ gmm_status gmm_set_precision(gmm_ctx* ctx, int32_t mode) {
   return GMM_OK;
 }
 
-gmm_status gmm_set_logit_mfma(gmm_ctx* ctx, int32_t kind) {
+gmm_status gmm_set_mfma(gmm_ctx* ctx, int32_t kind) {
   if (!ctx) return GMM_ERR_INVALID_ARG;
-  if (kind != GMM_LOGIT_MFMA_SPLIT_BF16 && kind != GMM_LOGIT_MFMA_FP32)
-    return fail(ctx, GMM_ERR_INVALID_ARG, "unknown logit instruction kind %d", kind);
-  ctx->ws.split = (kind == GMM_LOGIT_MFMA_SPLIT_BF16) ? 1 : 0;
+  if (kind != GMM_MFMA_SPLIT_BF16 && kind != GMM_MFMA_SPLIT_LOGITS && kind != GMM_MFMA_FP32)
+    return fail(ctx, GMM_ERR_INVALID_ARG, "unknown matrix instruction kind %d", kind);
+  ctx->ws.split = (kind == GMM_MFMA_SPLIT_BF16) ? 2 : (kind == GMM_MFMA_SPLIT_LOGITS) ? 1 : 0;
   return GMM_OK;
 }
 
-int32_t gmm_split_logits_active(const gmm_ctx* ctx, int32_t model) {
+int32_t gmm_split_level(const gmm_ctx* ctx, int32_t model) {
   if (!ctx || model < 0 || model > 2) return -1;
   if (!want_fused(ctx) || !ctx->ws.split || !ctx->ws.refine || ctx->ws.f64) return 0;
   if (model > 0 && !gmm::iso_kernel_ok(ctx->plan, ctx->ws, model == 2)) return 0;
-  return gmm::split_kernel_ok(ctx->plan, model) ? 1 : 0;
+  if (!gmm::split_kernel_ok(ctx->plan, model)) return 0;
+  return (ctx->ws.split == 2 && gmm::split_kernel_ok(ctx->plan, model + 3)) ? 2 : 1;
 }
 
 gmm_status gmm_init(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, const int64_t* init_rows,

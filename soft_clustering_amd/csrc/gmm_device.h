@@ -435,6 +435,118 @@ __device__ __forceinline__ void logit_tile_split(const __bf16* __restrict__ xsb,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split-bfloat16 statistics.  The statistics contraction has no float64
+// safety net, so it takes the three-part split v = v_hi + v_mid + v_lo
+// (bf16 each; v - v_hi and the next remainder are exact in float32, and the
+// last remainder has at most 8 significant bits, so the three parts hold a
+// float32 v exactly) for both operands, and the six products whose parts'
+// orders add up to at most two: hi.hi, hi.mid, mid.hi, hi.lo, lo.hi,
+// mid.mid.  The products left out are below 2^-23 of |r x|, at the float32
+// rounding level of the fp32 MFMA it replaces, at six 16-cycle bf16 MFMAs
+// per 32 rows against eight 32-cycle fp32 ones.
+__device__ __forceinline__ void split3(float v, __bf16& h, __bf16& m, __bf16& l) {
+  h = (__bf16)v;
+  const float r1 = v - (float)h;
+  m = (__bf16)r1;
+  l = (__bf16)(r1 - (float)m);
+}
+
+// LDS layout of the statistics operands of one tile (diagonal model, WD = 1):
+// [part][q][fb][lane][8] bf16, q the pair of 16-row blocks (rows 32 q ..),
+// fb the 16-feature block; lane (g, f16) holds feature fb * 16 + f16 of the
+// 8 rows 32 q + 4 g + {0..3} and 32 q + 16 + 4 g + {0..3}, the rows whose
+// responsibilities lane group g holds in the logit accumulators of blocks
+// 2q and 2q + 1.  Features follow the statistics slots: quarter f / HALF of
+// the segment holds x^2 (even) or x (odd) of dims (quarter / 2) * HALF +
+// f % HALF.
+template <class SH, int DPW>
+struct StatSplit {
+  static constexpr int BN = SH::TILE / SH::RS;
+  static constexpr int NQ = BN / 32;
+  static constexpr int NFB = DPW / 8;
+  static constexpr int PS = NQ * NFB * 512;  // bf16 per part
+  static constexpr int SIZE = 3 * PS;
+};
+
+// Raw tile -> statistics operands (all threads of the workgroup; reads rows
+// any wave staged, so after a barrier that follows the staging).
+template <class SH, int DPW>
+__device__ __forceinline__ void split_stats(const float* __restrict__ xt, __bf16* __restrict__ xsb) {
+  using ST = StatSplit<SH, DPW>;
+  constexpr int HALF = DPW / 2;
+  for (int it = threadIdx.x; it < ST::NQ * ST::NFB * kWave; it += SH::NT) {
+    const int ln = it & 63, rest = it >> 6;
+    const int fb = rest % ST::NFB, q = rest / ST::NFB;
+    const int gg = ln >> 4, f = fb * 16 + (ln & 15);
+    const int quarter = f / HALF;
+    const bool sq = (quarter & 1) == 0;
+    const int dim = (quarter >> 1) * HALF + f % HALF;
+    bf16x8 h, m, l;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int row = 32 * q + ((jj < 4) ? 0 : 16) + 4 * gg + (jj & 3);
+      const float x = xt[row * SH::RS + dim];
+      __bf16 a, b, c;
+      split3(sq ? x * x : x, a, b, c);
+      h[jj] = a;
+      m[jj] = b;
+      l[jj] = c;
+    }
+    __bf16* dst = xsb + (size_t)(q * ST::NFB + fb) * 512 + ln * 8;
+    *reinterpret_cast<bf16x8*>(dst) = h;
+    *reinterpret_cast<bf16x8*>(dst + ST::PS) = m;
+    *reinterpret_cast<bf16x8*>(dst + 2 * ST::PS) = l;
+  }
+}
+
+// Statistics of one wave from the split operands: r of the lane's rows
+// (the logit accumulators, already responsibilities) split in registers per
+// pair of row blocks, B operands one feature block ahead, six MFMAs per
+// (component block, feature block), small products first.
+template <class SH, int DPW>
+__device__ __forceinline__ void stats_tile_split(const f4 (&r)[SH::NPB][2], const __bf16* __restrict__ xsb,
+                                                 f4 (&sacc)[2][DPW / 8], int lane) {
+  using ST = StatSplit<SH, DPW>;
+#pragma unroll
+  for (int q = 0; q < ST::NQ; ++q) {
+    bf16x8 ah[2], am[2], al[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        __bf16 a, b, c;
+        split3((jj < 4) ? r[2 * q][cb][jj] : r[2 * q + 1][cb][jj - 4], a, b, c);
+        ah[cb][jj] = a;
+        am[cb][jj] = b;
+        al[cb][jj] = c;
+      }
+    const __bf16* bq = xsb + (size_t)q * ST::NFB * 512 + lane * 8;
+    auto ldb = [&](int fb, int part) { return *reinterpret_cast<const bf16x8*>(bq + fb * 512 + part * ST::PS); };
+    bf16x8 bh = ldb(0, 0), bm = ldb(0, 1), bl = ldb(0, 2);
+#pragma unroll
+    for (int fb = 0; fb < ST::NFB; ++fb) {
+      const int nx = (fb + 1 < ST::NFB) ? fb + 1 : fb;
+      const bf16x8 bhn = ldb(nx, 0), bmn = ldb(nx, 1), bln = ldb(nx, 2);
+      sacc[0][fb] = mfma_bf16(al[0], bh, sacc[0][fb]);
+      sacc[1][fb] = mfma_bf16(al[1], bh, sacc[1][fb]);
+      sacc[0][fb] = mfma_bf16(ah[0], bl, sacc[0][fb]);
+      sacc[1][fb] = mfma_bf16(ah[1], bl, sacc[1][fb]);
+      sacc[0][fb] = mfma_bf16(am[0], bm, sacc[0][fb]);
+      sacc[1][fb] = mfma_bf16(am[1], bm, sacc[1][fb]);
+      sacc[0][fb] = mfma_bf16(am[0], bh, sacc[0][fb]);
+      sacc[1][fb] = mfma_bf16(am[1], bh, sacc[1][fb]);
+      sacc[0][fb] = mfma_bf16(ah[0], bm, sacc[0][fb]);
+      sacc[1][fb] = mfma_bf16(ah[1], bm, sacc[1][fb]);
+      sacc[0][fb] = mfma_bf16(ah[0], bh, sacc[0][fb]);
+      sacc[1][fb] = mfma_bf16(ah[1], bh, sacc[1][fb]);
+      bh = bhn;
+      bm = bmn;
+      bl = bln;
+    }
+  }
+}
+
 // With WD > 1 the WD waves of a component group hold partial logits over
 // their dim segments; sum them in a fixed order through LDS so every wave of
 // the group ends with bit-identical full logits.

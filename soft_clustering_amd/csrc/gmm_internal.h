@@ -68,7 +68,7 @@ struct Workspace {
   float* ivec;       // Kpad       isotropic kernel: 1 / (2 s^2)
   __bf16* wsplit;    // Kpad * 2*Dp * 2  split-bf16 [a | b] (hi, lo), WD = 1
   __bf16* wsplit_iso;  // Kpad * Dp * 2  split-bf16 mu / s^2 (hi, lo), isotropic kernel
-  int split;         // 1: the fused refined diagonal E-step takes split-bf16 logits
+  int split;         // fused refined E-steps: 0 fp32 MFMA, 1 split-bf16 logits, 2 logits and statistics
   int colG;
   // soft assignment
   int32_t* asel;                 // assignChunk * 9  per-row selections
@@ -100,7 +100,8 @@ struct LaunchHooks {
 hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx,
                         bool fused, hipStream_t s, const LaunchHooks* hooks, int* nslots, int variant = 0);
 bool iso_kernel_ok(const Plan& p, const Workspace& w, bool hard);
-// split-bf16 logit kernel built for this shape (variant as launch_estep)
+// split-bf16 kernel built for this shape: variant as launch_estep (split
+// logits), or 3 + variant (split logits and statistics)
 bool split_kernel_ok(const Plan& p, int variant);
 hipError_t launch_kmeans_update(const Plan& p, const double* Nk, const double* S1, float* centres, double* counts,
                                 hipStream_t s);

@@ -184,7 +184,7 @@ __device__ __forceinline__ void row_exchange(const EArgs& a, int rg, int p, int 
 // accumulated.  With equal weights and variances 1/2 the largest logit is the
 // nearest centre.
 template <int WC, int WD, int DPW, int BN, bool FUSED, int MODE, bool ISO = false, bool HARD = false,
-          bool SPLIT = false>
+          int SPLIT = 0>
 __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats(EArgs a) {
   using SH = Shape<WC, WD, DPW, BN>;
   constexpr bool REFINE = MODE == MODE_REFINE, F64 = MODE == MODE_FP64;
@@ -193,6 +193,15 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   static_assert(!SPLIT || (FUSED && REFINE && WD == 1), "split-bf16 logits: fused refined kernels, WD = 1");
   static_assert(!SPLIT || !ISO || DPW >= 32, "isotropic split logits: 8 dims per lane group and step");
   using SPR = SplitRow<DPW, ISO>;
+  // SPLIT 2: the statistics contraction split too (three-part bf16 operands
+  // in LDS); its operands share the region of the logit operands, and the
+  // raw tile is single-buffered to make room (the next tile streams in
+  // behind the statistics phase instead of behind the whole tile)
+  static_assert(SPLIT < 2 || (!ISO && BN % 32 == 0), "split statistics: diagonal kernel, 32-row pairs");
+  using SST = StatSplit<SH, DPW>;
+  constexpr int NB = (SPLIT == 2) ? 1 : SH::NBUF;
+  constexpr int XSB = (SPLIT == 0) ? 8
+                      : (SPLIT == 2 && SST::SIZE > BN * SPR::XSR) ? SST::SIZE : BN * SPR::XSR;
   static_assert(!SPLIT || SH::CPR <= kWave, "split rows follow the one-instruction-per-row DMA assignment");
   constexpr int NPB = SH::NPB;
   constexpr int NFB = ISO ? DPW / 16 : SH::NFB;  // statistics feature blocks
@@ -203,7 +212,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   // row group would hold the whole group up once per member)
   constexpr int QP = (SH::NT / BN) > 0 ? (SH::NT / BN) : 1;
 
-  __shared__ __attribute__((aligned(16))) float xt[SH::NBUF][SH::TILE];
+  __shared__ __attribute__((aligned(16))) float xt[NB][SH::TILE];
   __shared__ __attribute__((aligned(16))) float red[F64 ? 1 : SH::RED];
   __shared__ double red64[F64 ? SH::RED : 1];
   __shared__ __attribute__((aligned(16))) float lzt[BN];
@@ -219,7 +228,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   __shared__ int lidx[HARD ? WC : 1][BN];                             // HARD: per-wave argmax
   __shared__ int exk[HARD ? QP : 1][BN];
   __shared__ int garg[HARD ? BN : 1];                                 // HARD: the row's argmax
-  __shared__ __attribute__((aligned(16))) __bf16 xsb[SPLIT ? BN * SPR::XSR : 8];  // split operands
+  __shared__ __attribute__((aligned(16))) __bf16 xsb[XSB];  // split operands
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wc = w % WC, wd = w / WC;
@@ -345,12 +354,12 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   }
   __syncthreads();
   for (; t < nt; t += a.R, ++j) {
-    const int cur = (SH::NBUF == 2) ? (j & 1) : 0;
+    const int cur = (NB == 2) ? (j & 1) : 0;
     const int64_t trow = (int64_t)t * BN;
     const int rows = (int)min((int64_t)BN, a.nrows - trow);
     const int tn = t + a.R;
     const bool has_next = tn < nt;
-    const bool async_next = (SH::NBUF == 2) && has_next && a.dma;
+    const bool async_next = (NB == 2) && has_next && a.dma;
     if (async_next)  // the other buffer was released by the last end-of-tile barrier
       stage_dma<SH>(xt[cur ^ 1], a.X, a.ldx, a.row0 + (int64_t)tn * BN,
                     (int)min((int64_t)BN, a.nrows - (int64_t)tn * BN));
@@ -416,7 +425,15 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
           for (int k = 0; k < WC; ++k) m = fmaxf(m, lpart[k][tid]);
           vtmp[tid] = m;
         }
-        row_exchange<BN, QP, false>(a, rg, p, j, 0, vtmp, exm, exs, thrs);
+        if constexpr (SPLIT == 2) {
+          // the statistics operands are built while the peers' words travel
+          // (every wave is past the logits, so the region is free)
+          if (tid < BN) xpost<BN>(a, rg, p, j, 0, vtmp[tid]);
+          split_stats<SH, DPW>(xt[cur], xsb);
+          xgather<BN, QP, false>(a, rg, j, 0, exm, exs, thrs);
+        } else {
+          row_exchange<BN, QP, false>(a, rg, p, j, 0, vtmp, exm, exs, thrs);
+        }
         if (tid < BN) thrs[tid] = (tid < rows) ? thrs[tid] - (HARD ? 0.f : kDelta) : kPosInf;
       } else {
         // reference: the row's final log Z from the first sweep
@@ -486,6 +503,12 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
       if (tid < BN) lzt[tid] = (tid < rows) ? a.logz[trow + tid] : kPosInf;
     }
     __syncthreads();
+    if constexpr (SPLIT == 2) {
+      // nothing reads the raw tile any more: the next one streams in behind
+      // the statistics
+      if (has_next && a.dma)
+        stage_dma<SH>(xt[0], a.X, a.ldx, a.row0 + (int64_t)tn * BN, (int)min((int64_t)BN, a.nrows - (int64_t)tn * BN));
+    }
 
     // ---- responsibilities and statistics: r goes from the logit
     // accumulators straight into the A operand; B operands are this lane's
@@ -538,6 +561,9 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
         }
       }
     }
+    if constexpr (SPLIT == 2) {
+      stats_tile_split<SH, DPW>(acc, xsb, sacc, lane);
+    } else {
     // one B operand per feature block: each is reloaded for the next point
     // step right after its two MFMAs have read it
     float bx[NFB];
@@ -561,16 +587,30 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    }
+    if constexpr (SPLIT == 2) {
+      if (has_next) {
+        if (a.dma) dma_wait();
+        else stage_now(xt[0], tn);  // every read of the raw tile preceded the statistics
+      }
+      if ((j + 1 + fphase) % FLUSH == 0) flush();
+      __syncthreads();  // statistics operands released, next rows visible
+      if (has_next) {
+        split_rows<SH, DPW, false>(xt[0], xsb, w);
+        __syncthreads();
+      }
+      continue;
+    }
     if (has_next) {
       if (async_next) {
         dma_wait();  // this wave's share of the next tile has landed
       } else {
-        if constexpr (SH::NBUF == 1) __syncthreads();  // every wave is done with the buffer
-        stage_now(xt[(SH::NBUF == 2) ? (cur ^ 1) : 0], tn);
+        if constexpr (NB == 1) __syncthreads();  // every wave is done with the buffer
+        stage_now(xt[(NB == 2) ? (cur ^ 1) : 0], tn);
       }
       // every wave finished this tile's logits (barriers since), so the
       // split operands can be overwritten
-      split_now(xt[(SH::NBUF == 2) ? (cur ^ 1) : 0]);
+      split_now(xt[(NB == 2) ? (cur ^ 1) : 0]);
     }
     if ((j + 1 + fphase) % FLUSH == 0) flush();
     __syncthreads();
@@ -1263,15 +1303,19 @@ struct Kern {
     else return nullptr;
   }
   static void* stats_split() {
-    if constexpr (WD == 1) return (void*)&k_stats<WC, WD, DPW, BN, true, MODE_REFINE, false, false, true>;
+    if constexpr (WD == 1) return (void*)&k_stats<WC, WD, DPW, BN, true, MODE_REFINE, false, false, 1>;
+    else return nullptr;
+  }
+  static void* stats_split2() {
+    if constexpr (WD == 1 && BN % 32 == 0) return (void*)&k_stats<WC, WD, DPW, BN, true, MODE_REFINE, false, false, 2>;
     else return nullptr;
   }
   static void* stats_iso_split() {
-    if constexpr (WD == 1 && DPW >= 32) return (void*)&k_stats<WC, WD, DPW, BN, true, MODE_REFINE, true, false, true>;
+    if constexpr (WD == 1 && DPW >= 32) return (void*)&k_stats<WC, WD, DPW, BN, true, MODE_REFINE, true, false, 1>;
     else return nullptr;
   }
   static void* stats_hard_split() {
-    if constexpr (WD == 1 && DPW >= 32) return (void*)&k_stats<WC, WD, DPW, BN, true, MODE_REFINE, true, true, true>;
+    if constexpr (WD == 1 && DPW >= 32) return (void*)&k_stats<WC, WD, DPW, BN, true, MODE_REFINE, true, true, 1>;
     else return nullptr;
   }
 };
@@ -1285,6 +1329,7 @@ struct KTab {
   void* split;    // fused diagonal refined kernel with split-bf16 logits (nullptr where not built)
   void* iso_split;   // the same for the isotropic kernel
   void* hard_split;  // and its hard-assignment mode
+  void* split2;      // diagonal kernel with split-bf16 logits and statistics
   void* two[3];
   void* logz[3];
 };
@@ -1296,7 +1341,7 @@ static bool lookup(int WC, int WD, int DPW, KTab& t) {
     t = KTab{{KK::stats_fused<0>(), KK::stats_fused<1>()},                                             \
              {KK::stats_iso<0>(), KK::stats_iso<1>()},                                                 \
              {KK::stats_hard<0>(), KK::stats_hard<1>()},                                               \
-             KK::stats_split(), KK::stats_iso_split(), KK::stats_hard_split(),                         \
+             KK::stats_split(), KK::stats_iso_split(), KK::stats_hard_split(), KK::stats_split2(),    \
              {KK::stats_two<0>(), KK::stats_two<1>(), KK::stats_two<2>()},                                \
              {KK::logz<0>(), KK::logz<1>(), KK::logz<2>()}};                                              \
     return true;                                                                                      \
@@ -1413,8 +1458,8 @@ hipError_t occupancy(const Plan& p, int* occStats, int* occLogz) {
   int o1b = 0, o2b = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1, (const void*)t.fused[0], nt, 0);
   if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1b, (const void*)t.fused[1], nt, 0);
-  void* extra[3] = {t.split, t.iso_split, t.hard_split};
-  for (int m = 0; m < 7 && e == hipSuccess; ++m) {
+  void* extra[4] = {t.split, t.iso_split, t.hard_split, t.split2};
+  for (int m = 0; m < 8 && e == hipSuccess; ++m) {
     void* kk = (m < 2) ? t.iso[m] : (m < 4) ? t.hard[m - 2] : extra[m - 4];
     if (!kk) continue;
     int oi = 0;
@@ -1500,7 +1545,8 @@ __global__ void k_fill_u64(unsigned long long* p, size_t n) {
 bool split_kernel_ok(const Plan& p, int variant) {
   KTab t;
   if (!lookup(p.WC, p.WD, p.DPW, t)) return false;
-  return (variant == 2 ? t.hard_split : variant == 1 ? t.iso_split : t.split) != nullptr;
+  void* k[6] = {t.split, t.iso_split, t.hard_split, t.split2, nullptr, nullptr};
+  return variant >= 0 && variant < 6 && k[variant] != nullptr;
 }
 
 bool iso_kernel_ok(const Plan& p, const Workspace& w, bool hard) {
@@ -1545,6 +1591,7 @@ hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64
     pre(0);
     void* kern = (variant == 2) ? t.hard[mode] : (variant == 1) ? t.iso[mode] : t.fused[mode];
     void* ksplit = (variant == 2) ? t.hard_split : (variant == 1) ? t.iso_split : t.split;
+    if (variant == 0 && w.split == 2 && t.split2) ksplit = t.split2;  // statistics split too
     if (mode == 1 && w.split && ksplit) {
       // split-bf16 logits: at most 6 Dp exact partial products summed in
       // float32, plus the split's own 3 * 2^-16 relative error per feature

@@ -88,7 +88,7 @@ def check_params_iso(got, want, Nk_ref, N, tol):
 def test_estep_iso_parity(name, path):
     """fused: the isotropic kernel (split-bfloat16 first-pass logits for
     16 < D <= 128); fused_fp32mfma: the same with fp32 MFMA logits."""
-    from soft_clustering_amd import GMM, LOGIT_MFMA_FP32, PATH_FUSED, PATH_TWO_SWEEP, PREC_FP64
+    from soft_clustering_amd import GMM, MFMA_FP32, PATH_FUSED, PATH_TWO_SWEEP, PREC_FP64
     Xn, Xg, params, _ = data(name)
     N, D = Xn.shape
     K = params[1].shape[0]
@@ -101,8 +101,8 @@ def test_estep_iso_parity(name, path):
     if path.endswith("fp64"):
         g.set_precision(PREC_FP64)
     if path == "fused_fp32mfma":
-        g.set_logit_mfma(LOGIT_MFMA_FP32)
-    assert g.split_logits_active(1) == (path == "fused" and 16 < D <= 128)
+        g.set_mfma(MFMA_FP32)
+    assert g.split_level(1) == (1 if (path == "fused" and 16 < D <= 128) else 0)
     got = [t.cpu().numpy() for t in g.estep_stats_iso(Xg, *gpu(params))]
     g.check()
     want = OI.estep_stats(Xn, *params, method="gemm" if N * K * D > 3e7 else "direct")

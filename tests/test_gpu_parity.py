@@ -65,14 +65,16 @@ def gpu_params(params):
     return tuple(torch.as_tensor(a).to(DEV) for a in params)
 
 
-@pytest.mark.parametrize("path", ["fused", "fused_fp32mfma", "fused_wc4", "two_sweep", "two_sweep_fp64"])
+@pytest.mark.parametrize("path", ["fused", "fused_split_logits", "fused_fp32mfma", "fused_wc4", "two_sweep",
+                                  "two_sweep_fp64"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_estep_parity(name, path, monkeypatch):
     """fused: the default fused kernel (8-wave workgroups where K allows;
-    split-bfloat16 first-pass logits for D <= 128); fused_fp32mfma: the same
-    with fp32 MFMA logits; fused_wc4: 4-wave workgroups, two per CU;
-    two_sweep_fp64: float64 MFMA logits (GMM_PREC_FP64)."""
-    from soft_clustering_amd import GMM, LOGIT_MFMA_FP32, PATH_FUSED, PATH_TWO_SWEEP, PREC_FP64
+    split-bfloat16 logits and statistics for D <= 128); fused_split_logits:
+    split logits, fp32 statistics; fused_fp32mfma: fp32 MFMA for both;
+    fused_wc4: 4-wave workgroups, two per CU; two_sweep_fp64: float64 MFMA
+    logits (GMM_PREC_FP64)."""
+    from soft_clustering_amd import GMM, MFMA_FP32, MFMA_SPLIT_LOGITS, PATH_FUSED, PATH_TWO_SWEEP, PREC_FP64
     if path == "fused_wc4":
         monkeypatch.setenv("FLASHGMM_WC", "4")
     Xn, Xg, params, _, _ = case_data(name)
@@ -87,8 +89,12 @@ def test_estep_parity(name, path, monkeypatch):
     if path.endswith("_fp64"):
         g.set_precision(PREC_FP64)
     if path == "fused_fp32mfma":
-        g.set_logit_mfma(LOGIT_MFMA_FP32)
-    assert g.split_logits_active() == (path in ("fused", "fused_wc4") and D <= 128)
+        g.set_mfma(MFMA_FP32)
+    if path == "fused_split_logits":
+        g.set_mfma(MFMA_SPLIT_LOGITS)
+    want_level = 0 if (path.startswith("two_sweep") or path == "fused_fp32mfma" or D > 128) else \
+        (1 if path == "fused_split_logits" else 2)
+    assert g.split_level(0) == want_level
     got = g.estep_stats(Xg, *gpu_params(params))
     g.check()
     got = [t.cpu().numpy() for t in got]
