@@ -217,7 +217,7 @@ def bench_kmeans(args):
     c = X[rows].contiguous()
     g = GMM(K, D, dev)
     lists = os.environ.get("FLASHGMM_KMEANS_FUSED", "1").strip() == "0"
-    split = (not lists) and g.split_level(2) > 0
+    split = 0 if lists else g.split_level(2)
     if args.warmup > 0:
         g.kmeans(X, c, args.warmup, lists=lists)
     torch.cuda.synchronize()
@@ -232,13 +232,15 @@ def bench_kmeans(args):
             "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "data": "synthetic (seeded mixture, generated on the GPU)",
             "config": {"workload": WORKLOAD_TEXT["kmeans"], "N": N, "K": K, "D": D,
-                       "path": "lists" if lists else "fused", "mfma": "split-bf16 logits" if split else "fp32"},
+                       "path": "lists" if lists else "fused",
+                       "mfma": ["fp32", "split-bf16 logits", "split-bf16 logits and statistics"][split]},
             "distance_tflops": round(useful / (dt / args.steps) / 1e12, 2),
             # MFMA work issued per iteration: the list path runs two logit sweeps
             # over the 2D expanded features; the fused sweep runs the logits over
-            # D features (three bf16 passes with split logits) and the (one-hot)
-            # statistics product over D
-            "issued_mfma_tflops": round((8.0 if lists else (8.0 if split else 4.0)) * N * K * D
+            # D features (three bf16 passes when split) and the one-hot
+            # statistics product over D (three bf16 passes when split: r is
+            # exact in bf16)
+            "issued_mfma_tflops": round((8.0 if lists else {0: 4.0, 1: 8.0, 2: 12.0}[split]) * N * K * D
                                         / (dt / args.steps) / 1e12, 2),
             "empty_clusters": int((counts == 0).sum().item())}
     print(json.dumps(line), flush=True)

@@ -452,36 +452,36 @@ __device__ __forceinline__ void split3(float v, __bf16& h, __bf16& m, __bf16& l)
   l = (__bf16)(r1 - (float)m);
 }
 
-// LDS layout of the statistics operands of one tile (diagonal model, WD = 1):
+// LDS layout of the statistics operands of one tile (WD = 1):
 // [part][q][fb][lane][8] bf16, q the pair of 16-row blocks (rows 32 q ..),
 // fb the 16-feature block; lane (g, f16) holds feature fb * 16 + f16 of the
 // 8 rows 32 q + 4 g + {0..3} and 32 q + 16 + 4 g + {0..3}, the rows whose
 // responsibilities lane group g holds in the logit accumulators of blocks
-// 2q and 2q + 1.  Features follow the statistics slots: quarter f / HALF of
-// the segment holds x^2 (even) or x (odd) of dims (quarter / 2) * HALF +
-// f % HALF.
-template <class SH, int DPW>
+// 2q and 2q + 1.  Features follow the statistics slots.  Diagonal model:
+// quarter f / HALF of the segment holds x^2 (even) or x (odd) of dims
+// (quarter / 2) * HALF + f % HALF.  Isotropic model: feature f is x of dim f.
+template <class SH, int DPW, bool ISO = false>
 struct StatSplit {
   static constexpr int BN = SH::TILE / SH::RS;
   static constexpr int NQ = BN / 32;
-  static constexpr int NFB = DPW / 8;
+  static constexpr int NFB = ISO ? DPW / 16 : DPW / 8;
   static constexpr int PS = NQ * NFB * 512;  // bf16 per part
   static constexpr int SIZE = 3 * PS;
 };
 
 // Raw tile -> statistics operands (all threads of the workgroup; reads rows
 // any wave staged, so after a barrier that follows the staging).
-template <class SH, int DPW>
+template <class SH, int DPW, bool ISO>
 __device__ __forceinline__ void split_stats(const float* __restrict__ xt, __bf16* __restrict__ xsb) {
-  using ST = StatSplit<SH, DPW>;
+  using ST = StatSplit<SH, DPW, ISO>;
   constexpr int HALF = DPW / 2;
   for (int it = threadIdx.x; it < ST::NQ * ST::NFB * kWave; it += SH::NT) {
     const int ln = it & 63, rest = it >> 6;
     const int fb = rest % ST::NFB, q = rest / ST::NFB;
     const int gg = ln >> 4, f = fb * 16 + (ln & 15);
     const int quarter = f / HALF;
-    const bool sq = (quarter & 1) == 0;
-    const int dim = (quarter >> 1) * HALF + f % HALF;
+    const bool sq = !ISO && (quarter & 1) == 0;
+    const int dim = ISO ? f : (quarter >> 1) * HALF + f % HALF;
     bf16x8 h, m, l;
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
@@ -503,11 +503,13 @@ __device__ __forceinline__ void split_stats(const float* __restrict__ xt, __bf16
 // Statistics of one wave from the split operands: r of the lane's rows
 // (the logit accumulators, already responsibilities) split in registers per
 // pair of row blocks, B operands one feature block ahead, six MFMAs per
-// (component block, feature block), small products first.
-template <class SH, int DPW>
+// (component block, feature block), small products first.  ONEHOT (r is 0
+// or 1, exact in bf16): r_mid = r_lo = 0, so three MFMAs, r against the three
+// parts of x.
+template <class SH, int DPW, bool ISO, bool ONEHOT>
 __device__ __forceinline__ void stats_tile_split(const f4 (&r)[SH::NPB][2], const __bf16* __restrict__ xsb,
-                                                 f4 (&sacc)[2][DPW / 8], int lane) {
-  using ST = StatSplit<SH, DPW>;
+                                                 f4 (&sacc)[2][StatSplit<SH, DPW, ISO>::NFB], int lane) {
+  using ST = StatSplit<SH, DPW, ISO>;
 #pragma unroll
   for (int q = 0; q < ST::NQ; ++q) {
     bf16x8 ah[2], am[2], al[2];
@@ -528,6 +530,18 @@ __device__ __forceinline__ void stats_tile_split(const f4 (&r)[SH::NPB][2], cons
     for (int fb = 0; fb < ST::NFB; ++fb) {
       const int nx = (fb + 1 < ST::NFB) ? fb + 1 : fb;
       const bf16x8 bhn = ldb(nx, 0), bmn = ldb(nx, 1), bln = ldb(nx, 2);
+      if constexpr (ONEHOT) {
+        sacc[0][fb] = mfma_bf16(ah[0], bl, sacc[0][fb]);
+        sacc[1][fb] = mfma_bf16(ah[1], bl, sacc[1][fb]);
+        sacc[0][fb] = mfma_bf16(ah[0], bm, sacc[0][fb]);
+        sacc[1][fb] = mfma_bf16(ah[1], bm, sacc[1][fb]);
+        sacc[0][fb] = mfma_bf16(ah[0], bh, sacc[0][fb]);
+        sacc[1][fb] = mfma_bf16(ah[1], bh, sacc[1][fb]);
+        bh = bhn;
+        bm = bmn;
+        bl = bln;
+        continue;
+      }
       sacc[0][fb] = mfma_bf16(al[0], bh, sacc[0][fb]);
       sacc[1][fb] = mfma_bf16(al[1], bh, sacc[1][fb]);
       sacc[0][fb] = mfma_bf16(ah[0], bl, sacc[0][fb]);

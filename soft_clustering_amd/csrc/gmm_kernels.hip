@@ -197,8 +197,8 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   // in LDS); its operands share the region of the logit operands, and the
   // raw tile is single-buffered to make room (the next tile streams in
   // behind the statistics phase instead of behind the whole tile)
-  static_assert(SPLIT < 2 || (!ISO && BN % 32 == 0), "split statistics: diagonal kernel, 32-row pairs");
-  using SST = StatSplit<SH, DPW>;
+  static_assert(SPLIT < 2 || BN % 32 == 0, "split statistics: 32-row pairs");
+  using SST = StatSplit<SH, DPW, ISO>;
   constexpr int NB = (SPLIT == 2) ? 1 : SH::NBUF;
   constexpr int XSB = (SPLIT == 0) ? 8
                       : (SPLIT == 2 && SST::SIZE > BN * SPR::XSR) ? SST::SIZE : BN * SPR::XSR;
@@ -429,7 +429,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
           // the statistics operands are built while the peers' words travel
           // (every wave is past the logits, so the region is free)
           if (tid < BN) xpost<BN>(a, rg, p, j, 0, vtmp[tid]);
-          split_stats<SH, DPW>(xt[cur], xsb);
+          split_stats<SH, DPW, ISO>(xt[cur], xsb);
           xgather<BN, QP, false>(a, rg, j, 0, exm, exs, thrs);
         } else {
           row_exchange<BN, QP, false>(a, rg, p, j, 0, vtmp, exm, exs, thrs);
@@ -562,7 +562,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
       }
     }
     if constexpr (SPLIT == 2) {
-      stats_tile_split<SH, DPW>(acc, xsb, sacc, lane);
+      stats_tile_split<SH, DPW, ISO, HARD>(acc, xsb, sacc, lane);
     } else {
     // one B operand per feature block: each is reloaded for the next point
     // step right after its two MFMAs have read it
@@ -596,7 +596,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
       if ((j + 1 + fphase) % FLUSH == 0) flush();
       __syncthreads();  // statistics operands released, next rows visible
       if (has_next) {
-        split_rows<SH, DPW, false>(xt[0], xsb, w);
+        split_rows<SH, DPW, ISO>(xt[0], xsb, w);
         __syncthreads();
       }
       continue;
@@ -1310,6 +1310,16 @@ struct Kern {
     if constexpr (WD == 1 && BN % 32 == 0) return (void*)&k_stats<WC, WD, DPW, BN, true, MODE_REFINE, false, false, 2>;
     else return nullptr;
   }
+  static void* stats_iso_split2() {
+    if constexpr (WD == 1 && DPW >= 32 && BN % 32 == 0)
+      return (void*)&k_stats<WC, WD, DPW, BN, true, MODE_REFINE, true, false, 2>;
+    else return nullptr;
+  }
+  static void* stats_hard_split2() {
+    if constexpr (WD == 1 && DPW >= 32 && BN % 32 == 0)
+      return (void*)&k_stats<WC, WD, DPW, BN, true, MODE_REFINE, true, true, 2>;
+    else return nullptr;
+  }
   static void* stats_iso_split() {
     if constexpr (WD == 1 && DPW >= 32) return (void*)&k_stats<WC, WD, DPW, BN, true, MODE_REFINE, true, false, 1>;
     else return nullptr;
@@ -1330,6 +1340,8 @@ struct KTab {
   void* iso_split;   // the same for the isotropic kernel
   void* hard_split;  // and its hard-assignment mode
   void* split2;      // diagonal kernel with split-bf16 logits and statistics
+  void* iso_split2;  // the same for the isotropic kernel
+  void* hard_split2; // and its hard-assignment mode
   void* two[3];
   void* logz[3];
 };
@@ -1342,6 +1354,7 @@ static bool lookup(int WC, int WD, int DPW, KTab& t) {
              {KK::stats_iso<0>(), KK::stats_iso<1>()},                                                 \
              {KK::stats_hard<0>(), KK::stats_hard<1>()},                                               \
              KK::stats_split(), KK::stats_iso_split(), KK::stats_hard_split(), KK::stats_split2(),    \
+             KK::stats_iso_split2(), KK::stats_hard_split2(),                                          \
              {KK::stats_two<0>(), KK::stats_two<1>(), KK::stats_two<2>()},                                \
              {KK::logz<0>(), KK::logz<1>(), KK::logz<2>()}};                                              \
     return true;                                                                                      \
@@ -1458,8 +1471,8 @@ hipError_t occupancy(const Plan& p, int* occStats, int* occLogz) {
   int o1b = 0, o2b = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1, (const void*)t.fused[0], nt, 0);
   if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1b, (const void*)t.fused[1], nt, 0);
-  void* extra[4] = {t.split, t.iso_split, t.hard_split, t.split2};
-  for (int m = 0; m < 8 && e == hipSuccess; ++m) {
+  void* extra[6] = {t.split, t.iso_split, t.hard_split, t.split2, t.iso_split2, t.hard_split2};
+  for (int m = 0; m < 10 && e == hipSuccess; ++m) {
     void* kk = (m < 2) ? t.iso[m] : (m < 4) ? t.hard[m - 2] : extra[m - 4];
     if (!kk) continue;
     int oi = 0;
@@ -1545,7 +1558,7 @@ __global__ void k_fill_u64(unsigned long long* p, size_t n) {
 bool split_kernel_ok(const Plan& p, int variant) {
   KTab t;
   if (!lookup(p.WC, p.WD, p.DPW, t)) return false;
-  void* k[6] = {t.split, t.iso_split, t.hard_split, t.split2, nullptr, nullptr};
+  void* k[6] = {t.split, t.iso_split, t.hard_split, t.split2, t.iso_split2, t.hard_split2};
   return variant >= 0 && variant < 6 && k[variant] != nullptr;
 }
 
@@ -1591,7 +1604,8 @@ hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64
     pre(0);
     void* kern = (variant == 2) ? t.hard[mode] : (variant == 1) ? t.iso[mode] : t.fused[mode];
     void* ksplit = (variant == 2) ? t.hard_split : (variant == 1) ? t.iso_split : t.split;
-    if (variant == 0 && w.split == 2 && t.split2) ksplit = t.split2;  // statistics split too
+    void* ksplit2 = (variant == 2) ? t.hard_split2 : (variant == 1) ? t.iso_split2 : t.split2;
+    if (w.split == 2 && ksplit2) ksplit = ksplit2;  // statistics split too
     if (mode == 1 && w.split && ksplit) {
       // split-bf16 logits: at most 6 Dp exact partial products summed in
       // float32, plus the split's own 3 * 2^-16 relative error per feature

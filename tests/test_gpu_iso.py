@@ -83,12 +83,13 @@ def check_params_iso(got, want, Nk_ref, N, tol):
     return errs
 
 
-@pytest.mark.parametrize("path", ["fused", "fused_fp32mfma", "two_sweep", "two_sweep_fp64"])
+@pytest.mark.parametrize("path", ["fused", "fused_split_logits", "fused_fp32mfma", "two_sweep", "two_sweep_fp64"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_estep_iso_parity(name, path):
-    """fused: the isotropic kernel (split-bfloat16 first-pass logits for
-    16 < D <= 128); fused_fp32mfma: the same with fp32 MFMA logits."""
-    from soft_clustering_amd import GMM, MFMA_FP32, PATH_FUSED, PATH_TWO_SWEEP, PREC_FP64
+    """fused: the isotropic kernel (split-bfloat16 logits and statistics for
+    16 < D <= 128); fused_split_logits: split logits, fp32 statistics;
+    fused_fp32mfma: fp32 MFMA for both."""
+    from soft_clustering_amd import GMM, MFMA_FP32, MFMA_SPLIT_LOGITS, PATH_FUSED, PATH_TWO_SWEEP, PREC_FP64
     Xn, Xg, params, _ = data(name)
     N, D = Xn.shape
     K = params[1].shape[0]
@@ -102,7 +103,10 @@ def test_estep_iso_parity(name, path):
         g.set_precision(PREC_FP64)
     if path == "fused_fp32mfma":
         g.set_mfma(MFMA_FP32)
-    assert g.split_level(1) == (1 if (path == "fused" and 16 < D <= 128) else 0)
+    if path == "fused_split_logits":
+        g.set_mfma(MFMA_SPLIT_LOGITS)
+    split_ok = path in ("fused", "fused_split_logits") and 16 < D <= 128
+    assert g.split_level(1) == ((2 if path == "fused" else 1) if split_ok else 0)
     got = [t.cpu().numpy() for t in g.estep_stats_iso(Xg, *gpu(params))]
     g.check()
     want = OI.estep_stats(Xn, *params, method="gemm" if N * K * D > 3e7 else "direct")

@@ -105,7 +105,7 @@ def test_kmeans_lloyd_step_parity(name, fused, monkeypatch):
     log(f"[kmeans] case={name} fused={fused} N={N} D={D} K={K}")
     g = GMM(K, D)
     if fused == "1":  # split-bfloat16 first-pass logits where the shape allows
-        assert g.split_level(2) == (1 if 16 < D <= 128 else 0)
+        assert g.split_level(2) == (2 if 16 < D <= 128 else 0)
     c = torch.as_tensor(c0).to(DEV)
     rtol = 1e-5 if fused == "1" else 2e-7
     for it in range(3):
