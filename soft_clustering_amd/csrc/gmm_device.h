@@ -391,8 +391,11 @@ __device__ __forceinline__ void split_rows(const float* __restrict__ xt, __bf16*
 }
 
 // Logits of one wave (WD = 1) from the split operands: per step the W hi/lo
-// of both component blocks (fetched one step ahead from L2), per point block
-// the x hi/lo of 16 rows (one ds_read_b128 each), three MFMAs per block.
+// of both component blocks (from L2), per point block the x hi/lo of 16 rows
+// (one ds_read_b128 each), three MFMAs per block.  No operand is fetched a
+// step ahead and the step loop is not unrolled: the registers that would
+// take cost more in spills of the whole kernel than the exposed load latency
+// (measured 748 against 813 ms per EM iteration at N=1e8, K=1024).
 // ws0/ws1: the two component blocks' split W, [step][hi, lo][lane][8].
 // acc must hold the starting value.
 template <class SH, int DPW, bool ISO>
@@ -404,11 +407,9 @@ __device__ __forceinline__ void logit_tile_split(const __bf16* __restrict__ xsb,
   auto wl = [&](const __bf16* wb, int st, int hl) {
     return *reinterpret_cast<const bf16x8*>(wb + ((st * 2 + hl) * kWave + lane) * 8);
   };
-  bf16x8 h0 = wl(ws0, 0, 0), l0 = wl(ws0, 0, 1), h1 = wl(ws1, 0, 0), l1 = wl(ws1, 0, 1);
-#pragma unroll 2
+#pragma unroll 1
   for (int st = 0; st < SR::S; ++st) {
-    const int nx = (st + 1 < SR::S) ? st + 1 : st;
-    const bf16x8 h0n = wl(ws0, nx, 0), l0n = wl(ws0, nx, 1), h1n = wl(ws1, nx, 0), l1n = wl(ws1, nx, 1);
+    const bf16x8 h0 = wl(ws0, st, 0), l0 = wl(ws0, st, 1), h1 = wl(ws1, st, 0), l1 = wl(ws1, st, 1);
     auto ld = [&](int pb, int off) {
       return *reinterpret_cast<const bf16x8*>(arow + pb * 16 * SR::XSR + off + st * 32);
     };
@@ -428,10 +429,6 @@ __device__ __forceinline__ void logit_tile_split(const __bf16* __restrict__ xsb,
       acc[pb][0] = mfma_bf16(ah, h0, acc[pb][0]);
       acc[pb][1] = mfma_bf16(ah, h1, acc[pb][1]);
     }
-    h0 = h0n;
-    l0 = l0n;
-    h1 = h1n;
-    l1 = l1n;
   }
 }
 
@@ -502,7 +499,8 @@ __device__ __forceinline__ void split_stats(const float* __restrict__ xt, __bf16
 
 // Statistics of one wave from the split operands: r of the lane's rows
 // (the logit accumulators, already responsibilities) split in registers per
-// pair of row blocks, B operands one feature block ahead, six MFMAs per
+// pair of row blocks, B operands from LDS per feature block (not fetched
+// ahead, for the same register reason as the logits), six MFMAs per
 // (component block, feature block), small products first.  ONEHOT (r is 0
 // or 1, exact in bf16): r_mid = r_lo = 0, so three MFMAs, r against the three
 // parts of x.
@@ -525,11 +523,9 @@ __device__ __forceinline__ void stats_tile_split(const f4 (&r)[SH::NPB][2], cons
       }
     const __bf16* bq = xsb + (size_t)q * ST::NFB * 512 + lane * 8;
     auto ldb = [&](int fb, int part) { return *reinterpret_cast<const bf16x8*>(bq + fb * 512 + part * ST::PS); };
-    bf16x8 bh = ldb(0, 0), bm = ldb(0, 1), bl = ldb(0, 2);
 #pragma unroll
     for (int fb = 0; fb < ST::NFB; ++fb) {
-      const int nx = (fb + 1 < ST::NFB) ? fb + 1 : fb;
-      const bf16x8 bhn = ldb(nx, 0), bmn = ldb(nx, 1), bln = ldb(nx, 2);
+      const bf16x8 bh = ldb(fb, 0), bm = ldb(fb, 1), bl = ldb(fb, 2);
       if constexpr (ONEHOT) {
         sacc[0][fb] = mfma_bf16(ah[0], bl, sacc[0][fb]);
         sacc[1][fb] = mfma_bf16(ah[1], bl, sacc[1][fb]);
@@ -537,9 +533,6 @@ __device__ __forceinline__ void stats_tile_split(const f4 (&r)[SH::NPB][2], cons
         sacc[1][fb] = mfma_bf16(ah[1], bm, sacc[1][fb]);
         sacc[0][fb] = mfma_bf16(ah[0], bh, sacc[0][fb]);
         sacc[1][fb] = mfma_bf16(ah[1], bh, sacc[1][fb]);
-        bh = bhn;
-        bm = bmn;
-        bl = bln;
         continue;
       }
       sacc[0][fb] = mfma_bf16(al[0], bh, sacc[0][fb]);
@@ -554,9 +547,6 @@ __device__ __forceinline__ void stats_tile_split(const f4 (&r)[SH::NPB][2], cons
       sacc[1][fb] = mfma_bf16(ah[1], bm, sacc[1][fb]);
       sacc[0][fb] = mfma_bf16(ah[0], bh, sacc[0][fb]);
       sacc[1][fb] = mfma_bf16(ah[1], bh, sacc[1][fb]);
-      bh = bhn;
-      bm = bmn;
-      bl = bln;
     }
   }
 }
