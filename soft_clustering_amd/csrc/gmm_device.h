@@ -349,7 +349,7 @@ __device__ __forceinline__ void split_rows(const float* __restrict__ xt, __bf16*
   constexpr int RPW = (BN + NW - 1) / NW;     // rows per wave
   constexpr int HS = DPW / 16;                // chunks per half (= S)
   const int lane = threadIdx.x & 63;
-#pragma unroll
+#pragma unroll 1  // one item at a time (registers, as in split_stats)
   for (int it = lane; it < RPW * CH; it += kWave) {
     const int rl = it / CH, c = it - rl * CH;
     const int pt = w + rl * NW;
@@ -472,6 +472,9 @@ template <class SH, int DPW, bool ISO>
 __device__ __forceinline__ void split_stats(const float* __restrict__ xt, __bf16* __restrict__ xsb) {
   using ST = StatSplit<SH, DPW, ISO>;
   constexpr int HALF = DPW / 2;
+  // one item at a time: the build runs while every accumulator is live, and
+  // items in flight together would spill them
+#pragma unroll 1
   for (int it = threadIdx.x; it < ST::NQ * ST::NFB * kWave; it += SH::NT) {
     const int ln = it & 63, rest = it >> 6;
     const int fb = rest % ST::NFB, q = rest / ST::NFB;
