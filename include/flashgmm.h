@@ -99,8 +99,9 @@ typedef enum {
  * SPLIT_LOGITS: split logits, fp32 statistics.
  * FP32: fp32 MFMA for both.
  * Split logits are built for the fused E-steps with D <= 128 (diagonal;
- * isotropic and the k-means hard assignment for D > 16), split statistics
- * for the diagonal one; elsewhere FP32 runs. */
+ * isotropic and the k-means hard assignment for D > 16) and for the soft
+ * assignment (gmm_soft_assign, D <= 128); split statistics for the fused
+ * E-steps; elsewhere FP32 runs. */
 typedef enum {
     GMM_MFMA_SPLIT_BF16 = 0,
     GMM_MFMA_SPLIT_LOGITS = 1,

@@ -71,10 +71,14 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int WC, int WD, int DPW, int BN, int MODE>
+// SPLIT: split-bfloat16 first-pass logits (refined mode, WD = 1); the tile's
+// split operands are built once and serve every component group.
+template <int WC, int WD, int DPW, int BN, int MODE, bool SPLIT = false>
 __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
   using SH = Shape<WC, WD, DPW, BN>;
   constexpr bool REFINE = MODE == MODE_REFINE, F64 = MODE == MODE_FP64;
+  static_assert(!SPLIT || (REFINE && WD == 1), "split-bf16 logits: refined mode, WD = 1");
+  using SPR = SplitRow<DPW, false>;
   constexpr int NPB = SH::NPB;
   constexpr int TLW = 16 * (BN + 1);        // one wave's transposed 16-component block
   constexpr int LSTW = 2 * kTopN * BN;      // one wave's lists (values, indices)
@@ -88,6 +92,7 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
   __shared__ __attribute__((aligned(16))) float thrw[WC][BN];
   __shared__ float rlist[SH::COOP ? WC : WC * WD][kRefineCap];  // refinement lists (per group or wave)
   __shared__ unsigned short elist[SH::COOP ? WC : WC * WD][kRefineCap];
+  __shared__ __attribute__((aligned(16))) __bf16 xsb[SPLIT ? BN * SPR::XSR : 8];  // split operands
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wc = w % WC, wd = w / WC;
@@ -110,6 +115,7 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
       stg.store(xt);
     }
     __syncthreads();
+    if constexpr (SPLIT) split_rows<SH, DPW, false>(xt, xsb, w);  // published by the barrier below
     if constexpr (REFINE) {
       row_norms2<SH, DPW>(xt, nrm, a.Dp);
       __syncthreads();
@@ -147,9 +153,14 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
           acc[pb][0] = f4{c0, c0, c0, c0};
           acc[pb][1] = f4{c1, c1, c1, c1};
         }
-        logit_tile<SH, DPW>(xt, wop_block(a.wop, compbase >> 4, WD, wd, DPW),
-                            wop_block(a.wop, (compbase >> 4) + 1, WD, wd, DPW), acc, lane, wd);
-        reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
+        if constexpr (SPLIT) {
+          logit_tile_split<SH, DPW, false>(xsb, a.wsp + (size_t)(compbase >> 4) * SPR::WBLK,
+                                           a.wsp + (size_t)((compbase >> 4) + 1) * SPR::WBLK, acc, lane);
+        } else {
+          logit_tile<SH, DPW>(xt, wop_block(a.wop, compbase >> 4, WD, wd, DPW),
+                              wop_block(a.wop, (compbase >> 4) + 1, WD, wd, DPW), acc, lane, wd);
+          reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
+        }
       }
       if constexpr (REFINE) {
         // running maximum of guaranteed lower bounds L - E of the row's
@@ -379,14 +390,21 @@ struct AKern {
   static constexpr int BN = bn_for(WD, DPW);
   template <int M>
   static void* assign() { return (void*)&k_assign<WC, WD, DPW, BN, M>; }
+  static void* assign_split() {
+    if constexpr (WD == 1) return (void*)&k_assign<WC, WD, DPW, BN, MODE_REFINE, true>;
+    else return nullptr;
+  }
 };
 
-static bool alookup(int WC, int WD, int DPW, void* (&t)[3]) {
+// t[0..2]: float32, refined, float64 logits; t[3]: refined with split-bf16
+// first-pass logits (nullptr where not built)
+static bool alookup(int WC, int WD, int DPW, void* (&t)[4]) {
 #define GMM_A(wc, wd, dpw)                                           \
   if (WC == wc && WD == wd && DPW == dpw) {                          \
     t[0] = AKern<wc, wd, dpw>::assign<0>();                          \
     t[1] = AKern<wc, wd, dpw>::assign<1>();                          \
     t[2] = AKern<wc, wd, dpw>::assign<2>();                          \
+    t[3] = AKern<wc, wd, dpw>::assign_split();                       \
     return true;                                                     \
   }
   GMM_A(1, 1, 16) GMM_A(1, 1, 32) GMM_A(1, 1, 64) GMM_A(1, 1, 128)
@@ -408,21 +426,24 @@ static int assign_wc(const Plan& p) {
 }
 
 hipError_t assign_occupancy(const Plan& p, int* occ) {
-  void* t[3];
+  void* t[4];
   const int wc = assign_wc(p);
   *occ = 0;
   if (!alookup(wc, p.WD, p.DPW, t)) return hipSuccess;  // no assignment kernel for this shape
-  int o0 = 0, o1 = 0;
+  int o0 = 0, o1 = 0, o3 = 1 << 30;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o0, (const void*)t[0], 64 * wc * p.WD, 0);
   if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1, (const void*)t[1], 64 * wc * p.WD, 0);
+  if (e == hipSuccess && t[3])
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o3, (const void*)t[3], 64 * wc * p.WD, 0);
   if (e != hipSuccess) return e;
   *occ = o0 < o1 ? o0 : o1;
+  if (o3 < *occ) *occ = o3;
   return hipSuccess;
 }
 
 hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* X, int64_t row0, int64_t rows,
                                 int64_t ldx, float threshold, int max_extra, bool count, hipStream_t s) {
-  void* t[3];
+  void* t[4];
   const int wc = assign_wc(p);
   if (!alookup(wc, p.WD, p.DPW, t)) return hipErrorInvalidValue;
   EArgs a{};
@@ -460,7 +481,14 @@ hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* 
   const int64_t tiles = (rows + p.BN - 1) / p.BN;
   const int64_t gmax = (int64_t)p.numCU * (p.occAssign > 0 ? p.occAssign : 1);
   const int grid = (int)(tiles < gmax ? tiles : gmax);
-  return hipLaunchKernel(t[w.f64 ? 2 : (w.refine ? 1 : 0)], dim3(grid), dim3(64 * wc * p.WD), args, 0, s);
+  void* kern = t[w.f64 ? 2 : (w.refine ? 1 : 0)];
+  if (!w.f64 && w.refine && w.split && t[3]) {
+    // split-bf16 first-pass logits, the refinement bound widened to match
+    kern = t[3];
+    a.wsp = w.wsplit;
+    a.kappa = (float)((6.0 * p.Dp + 8.0) * 5.9604644775390625e-08 * (1.0 + 1.0 / 64.0) + 3.1 * 1.52587890625e-05);
+  }
+  return hipLaunchKernel(kern, dim3(grid), dim3(64 * wc * p.WD), args, 0, s);
 }
 
 hipError_t launch_assign_begin(const Plan& p, const Workspace& w, hipStream_t s) {

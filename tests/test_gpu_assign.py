@@ -107,10 +107,13 @@ def compare(gpu_rows, lists, boundary, what):
     return int(diff.sum())
 
 
+@pytest.mark.parametrize("mfma", ["split", "fp32"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_soft_assign_parity(name):
+def test_soft_assign_parity(name, mfma):
+    """mfma: split-bfloat16 first-pass logits (default, D <= 128) or fp32
+    MFMA logits."""
     law, N, D, K, ldx, thr, m, iters = CASES[name]
-    log(f"soft_assign parity {name}: N={N} D={D} K={K} thr={thr} m={m}")
+    log(f"soft_assign parity {name} ({mfma}): N={N} D={D} K={K} thr={thr} m={m}")
     mix = datagen.mixture(law, D, K, seed=0)
     Xc = datagen.sample(mix, N, seed=0)
     Xn = Xc.numpy()
@@ -121,6 +124,9 @@ def test_soft_assign_parity(name):
         from soft_clustering_amd import PREC_FP64
         g.set_precision(PREC_FP64)
     w, mu, var = trained_params(g, Xg, Xn, K, floor, iters)
+    if mfma == "fp32":
+        from soft_clustering_amd import MFMA_FP32
+        g.set_mfma(MFMA_FP32)
     offsets, ids = g.soft_assign(Xg, w, mu, var, thr, m)
     torch.cuda.synchronize()
     wn, mun, varn = (a.cpu().numpy() for a in (w, mu, var))
