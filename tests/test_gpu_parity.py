@@ -105,6 +105,44 @@ def test_estep_parity(name, path, monkeypatch):
     assert not errs, "\n".join(errs)
 
 
+@pytest.mark.parametrize("mfma", ["split", "split_logits", "fp32"])
+def test_estep_parity_far_from_origin(mfma):
+    """Rows and means near 50 in every dimension: the expanded quadratic
+    cancels terms of about 2500 / s^2 per dimension, so the first-pass logits
+    carry large errors (the split-bf16 ones the largest) and the float64
+    refinement carries the result; every instruction setting must still
+    match the oracle.  Parameters after three GPU EM iterations (tighter
+    variances, larger cancelled terms).  At this offset about a quarter of
+    the logits are refined, and without refinement (GMM_PREC_FP32) N_k and
+    S1 fall outside the tolerance."""
+    from soft_clustering_amd import GMM, MFMA_FP32, MFMA_SPLIT_LOGITS, PATH_FUSED
+    N, D, K = 6_007, 16, 24
+    mix = datagen.mixture("tiny", D, K, seed=3)
+    Xc = datagen.sample(mix, N, seed=3) + 50.0
+    Xn = Xc.numpy()
+    params = tuple(a.astype(np.float32) for a in O.init(Xn, datagen.init_rows(N, K, seed=4), 1e-6))
+    log(f"[estep far] mfma={mfma} N={N} D={D} K={K}")
+    g = GMM(K, D)
+    g.set_path(PATH_FUSED)
+    if mfma == "fp32":
+        g.set_mfma(MFMA_FP32)
+    if mfma == "split_logits":
+        g.set_mfma(MFMA_SPLIT_LOGITS)
+    assert g.split_level(0) == {"split": 2, "split_logits": 1, "fp32": 0}[mfma]
+    Xg = Xc.to(DEV)
+    w, mu, var = gpu_params(params)
+    g.fit(Xg, w, mu, var, 3, 1e-6)
+    g.check()
+    th = tuple(a.cpu().numpy().copy() for a in (w, mu, var))
+    got = [t.cpu().numpy() for t in g.estep_stats(Xg, w, mu, var)]
+    g.check()
+    want = O.estep_stats(Xn, *th, method="direct")
+    ms, rms = data_scales(Xn)
+    errs = check_stats((got[0], got[1], got[2], got[3][0]), want, ms, rms,
+                       np.sqrt(th[2].astype(np.float64)), 1e-4)
+    assert not errs, "\n".join(errs)
+
+
 def test_mstep_parity():
     from soft_clustering_amd import GMM
     Xn, Xg, params, _, floor = case_data("mid_prefix")
