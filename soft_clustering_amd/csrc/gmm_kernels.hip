@@ -368,10 +368,22 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
     if constexpr (F64) {
       logits_f64<SH, WC, WD, DPW>(xt[cur], w0d, w1d, c0d, c1d, acc, red64, lane, wc, wd);
     } else {
+      // diagonal kernel with split statistics: the per-lane constants are
+      // reloaded each tile (through an index the compiler cannot hoist), so
+      // they are not live across the whole tile; that takes 10 VGPRs off its
+      // spills (4.5 % faster; the isotropic kernel is better without)
+      constexpr bool RELOAD = SPLIT == 2 && !ISO;
+      float c0t = c0, c1t = c1;
+      if constexpr (RELOAD) {
+        int kk = compbase + r16;
+        asm volatile("" : "+v"(kk));
+        c0t = (wd == 0) ? a.cvec[kk] : 0.f;
+        c1t = (wd == 0) ? a.cvec[kk + 16] : 0.f;
+      }
 #pragma unroll
       for (int pb = 0; pb < NPB; ++pb) {
-        acc[pb][0] = f4{c0, c0, c0, c0};
-        acc[pb][1] = f4{c1, c1, c1, c1};
+        acc[pb][0] = f4{c0t, c0t, c0t, c0t};
+        acc[pb][1] = f4{c1t, c1t, c1t, c1t};
       }
       if constexpr (ISO) {
         row_norms_iso<SH, DPW>(xt[cur], nrm, xn2);
@@ -396,6 +408,11 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
     }
 
     // ---- float64 refinement of the logits that can matter
+    if constexpr (REFINE && SPLIT == 2 && !ISO) {  // per-tile reload, as c0 / c1 above
+      int cbo = compbase;
+      asm volatile("" : "+v"(cbo));
+      lane_coefs(a, cbo, r16, co);
+    }
     if constexpr (REFINE) {
       if constexpr (!ISO) {
         row_norms2<SH, DPW>(xt[cur], nrm, a.Dp);
