@@ -65,12 +65,12 @@ typedef enum {
 } gmm_path;
 
 /* Precision of the logits (gmm_set_precision).
- * REFINED (default): the K logits of every point come from the fp32 MFMA
- *   contraction, and each logit that can carry a responsibility above
- *   e^-16 of the point's largest one (judged with a rigorous bound on the
- *   fp32 error) is recomputed in float64 before the log-sum-exp, so
- *   responsibilities, statistics and log-likelihood carry float64-grade
- *   logits wherever they matter.
+ * REFINED (default): the K logits of every point come from a first-pass
+ *   MFMA contraction (split-bfloat16 or fp32, gmm_set_mfma), and each logit
+ *   that can carry a responsibility above e^-16 of the point's largest one
+ *   (judged with a rigorous bound on the first pass's error) is recomputed
+ *   in float64 before the log-sum-exp, so responsibilities, statistics and
+ *   log-likelihood carry float64-grade logits wherever they matter.
  * FP32: no refinement; fp32 expanded-quadratic logits throughout (errors of
  *   1e-4..1e-2 nats on data spread over many cluster widths).
  * FP64: every logit from a float64 MFMA contraction (v_mfma_f64, half the
