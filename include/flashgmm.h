@@ -45,7 +45,7 @@ typedef struct gmm_ctx gmm_ctx;
 typedef enum {
     GMM_OK = 0,
     GMM_ERR_INVALID_ARG = 1, /* a pointer, size or option is out of range */
-    GMM_ERR_UNSUPPORTED = 2, /* valid request this build/device cannot run */
+    GMM_ERR_UNSUPPORTED = 2, /* valid request that the library or device cannot run */
     GMM_ERR_OOM = 3,         /* workspace allocation failed */
     GMM_ERR_HIP = 4,         /* a HIP runtime call or kernel failed */
     GMM_ERR_NUMERIC = 5,     /* non-finite log-likelihood or statistics */
