@@ -114,6 +114,36 @@ def test_estep_iso_parity(name, path):
     assert not errs, "\n".join(errs)
 
 
+@pytest.mark.parametrize("mfma", ["split", "fp32"])
+def test_estep_iso_far_from_origin(mfma):
+    """Rows and means near 50 in every dimension (x . mu / s^2 and
+    ||x||^2 / (2 s^2) cancel terms of about 2500 / s^2 per dimension): the
+    float64 refinement carries the result for split-bf16 and fp32 MFMA
+    alike.  Parameters after three GPU EM iterations."""
+    from soft_clustering_amd import GMM, MFMA_FP32, PATH_FUSED
+    N, D, K = 6_007, 32, 24
+    mix = datagen.mixture("iso", D, K, seed=3)
+    Xc = datagen.sample(mix, N, seed=3) + 50.0
+    Xn = Xc.numpy()
+    params = tuple(np.asarray(a, np.float32) for a in OI.init(Xn, datagen.init_rows(N, K, seed=4), 1e-6))
+    log(f"[iso far] mfma={mfma} N={N} D={D} K={K}")
+    g = GMM(K, D)
+    g.set_path(PATH_FUSED)
+    if mfma == "fp32":
+        g.set_mfma(MFMA_FP32)
+    assert g.split_level(1) == (2 if mfma == "split" else 0)
+    Xg = Xc.to(DEV)
+    w, mu, v = gpu(params)
+    g.fit_iso(Xg, w, mu, v, 3, 1e-6)
+    g.check()
+    th = tuple(a.cpu().numpy().copy() for a in (w, mu, v))
+    got = [t.cpu().numpy() for t in g.estep_stats_iso(Xg, w, mu, v)]
+    g.check()
+    want = OI.estep_stats(Xn, *th)
+    errs = check_stats_iso((got[0], got[1], got[2], got[3][0]), want, Xn, th[2], 1e-4)
+    assert not errs, errs
+
+
 def test_estep_iso_accumulate_over_chunks():
     from soft_clustering_amd import GMM
     Xn, Xg, params, _ = data("d200_k100")

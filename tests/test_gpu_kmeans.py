@@ -183,3 +183,29 @@ def test_kmeans_without_lists(name, monkeypatch):
     monkeypatch.setenv("FLASHGMM_KMEANS_FUSED", "0")
     with pytest.raises(GMMError):
         g.kmeans(Xg, torch.as_tensor(c0).to(DEV), 1, lists=False)
+
+
+def test_kmeans_step_far_from_origin():
+    """Rows near 50 in every dimension: the squared distances cancel terms
+    of about 2 * 2500 per dimension, so the first-pass logits are far off and
+    the nearest centre is decided by the float64-recomputed candidates.  One
+    fused Lloyd iteration against the oracle's step (near ties as above)."""
+    from soft_clustering_amd import GMM
+    N, D, K = 8_009, 32, 40
+    mix = datagen.mixture("tiny", D, K, seed=5)
+    Xc = datagen.sample(mix, N, seed=5) + 50.0
+    Xn = Xc.numpy()
+    c0 = Xn[datagen.init_rows(N, K, seed=6)].astype(np.float32)
+    log(f"[kmeans far] N={N} D={D} K={K}")
+    g = GMM(K, D)
+    assert g.split_level(2) == 2
+    c = torch.as_tensor(c0).to(DEV)
+    _, counts, _, _ = g.kmeans(Xc.to(DEV), c, 1, lists=False)
+    a_ref, tie, tol, _ = near_ties(Xn, c0)
+    got_n, got_c = counts.cpu().numpy(), c.cpu().numpy()
+    ok = any(np.array_equal(got_n, cnt) and np.allclose(got_c, want.astype(np.float32), rtol=1e-5, atol=1e-4)
+             for cnt, want in acceptable_updates(Xn, c0, a_ref, tie, tol))
+    if not ok:
+        cnt, want = KM.update(Xn, a_ref, c0)
+        np.testing.assert_array_equal(got_n, cnt)
+        np.testing.assert_allclose(got_c, want.astype(np.float32), rtol=1e-5, atol=1e-4)
