@@ -599,8 +599,10 @@ gmm_status kmeans_assign(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx, c
 
 // Out-of-core E-step: rows [r0, r0 + rows) of a host X are copied into
 // alternating device staging buffers on the copy stream while the E-step of
-// the previous chunk runs on the context's stream; an event per buffer keeps
-// a copy from overwriting a chunk whose E-step has not finished.  The
+// the previous chunk runs on the context's stream; an event per buffer,
+// recorded after every E-step that reads the buffer and kept across calls,
+// keeps a copy from overwriting a chunk whose E-step has not finished, also
+// that of the previous call or fit iteration.  The
 // statistics accumulate over the chunks exactly as gmm_estep_stats with
 // accumulate = 1 on the same row ranges.  Staging rows have a stride of D
 // rounded up to 4 floats; the padding floats are never read as data.
@@ -643,8 +645,9 @@ gmm_status estep_host(gmm_ctx* c, const float* Xh, int64_t N, int64_t ldx, const
   for (int64_t r0 = 0; r0 < N; r0 += chunk, ++i) {
     const int64_t rows = (N - r0 < chunk) ? N - r0 : chunk;
     const int b = i & 1;
-    hipError_t e = hipSuccess;
-    if (i >= 2) e = hipStreamWaitEvent(c->copy_stream, c->ev_used[b], 0);
+    // the last E-step that read buffer b, in this call or an earlier one
+    // (waiting on an event never recorded returns at once)
+    hipError_t e = hipStreamWaitEvent(c->copy_stream, c->ev_used[b], 0);
     if (e == hipSuccess)
       e = hipMemcpy2DAsync(c->stage[b], (size_t)ld * sizeof(float), Xh + r0 * ldx, (size_t)ldx * sizeof(float),
                            (size_t)D * sizeof(float), (size_t)rows, hipMemcpyHostToDevice, c->copy_stream);

@@ -80,3 +80,45 @@ def test_fit_host_per_iteration_and_single_chunk():
     hb = g.fit(torch.as_tensor(Xn).to(DEV), *b, 4, 1e-6)[3]
     g.check()
     assert torch.equal(ha, hb) and all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("pinned", [True, False])
+def test_fit_host_chunks_reused_across_iterations(pinned):
+    """Several chunks per iteration at K=1024, D=128 (the E-step of a chunk
+    takes longer than its copy), so a copy issued for the next iteration or
+    the next call would overwrite a staging buffer still being read unless
+    it waits for that buffer's last E-step.  T iterations in one call must
+    equal T calls of one iteration, and back-to-back E-step calls must equal
+    the device E-step, bit for bit."""
+    from soft_clustering_amd import GMM
+    Xn, Xh, params = case("mid", 40_011, 128, 1024, pinned=pinned)
+    g = GMM(1024, 128)
+    chunk = 9_000  # 5 chunks, the last one ragged
+    a = [t.clone() for t in params]
+    ha = g.fit_host(Xh, *a, 3, 1e-6, chunk)[3].clone()
+    b = [t.clone() for t in params]
+    hb = []
+    for _ in range(3):
+        hb.append(g.fit_host(Xh, *b, 1, 1e-6, chunk)[3].clone())
+        g.check()
+    g.check()
+    assert torch.equal(ha, torch.cat(hb))
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+    # two E-step calls queued back to back (no host synchronisation between)
+    o1 = [t.clone() for t in g.estep_stats_host(Xh, *params, chunk)]
+    o2 = g.estep_stats_host(Xh, *a, chunk)
+    g.check()
+    Xd = torch.as_tensor(Xn).to(DEV)
+
+    def device_chunks(prm):
+        out = None
+        for r0 in range(0, Xd.shape[0], chunk):
+            out = g.estep_stats(Xd[r0:r0 + chunk], *prm, out=out, accumulate=r0 > 0)
+        return [t.clone() for t in out]
+    d1 = device_chunks(params)
+    d2 = device_chunks(a)
+    g.check()
+    for x, y, what in zip(o1, d1, ("Nk", "S1", "S2", "LL")):
+        assert torch.equal(x, y), f"first call: {what} differs"
+    for x, y, what in zip(o2, d2, ("Nk", "S1", "S2", "LL")):
+        assert torch.equal(x, y), f"second call: {what} differs"
