@@ -216,26 +216,38 @@ def assign_rows(r, threshold, max_extra):
 
 
 def boundary_rows(r, threshold, max_extra, eps=1e-5):
-    """Rows whose list membership can flip under a responsibility error of
-    eps: some r within eps of the threshold, the two largest r within eps of
-    each other (argmax tie), or, when more than max_extra other components
-    clear the threshold, the last one kept within eps of the first one cut."""
+    """Rows whose list can change when responsibilities move by up to eps
+    (the configured 1e-5 exemption, with the rank-tie extension of the
+    scope's tolerance table).  With a the argmax and o_1 >= o_2 >= ... the
+    other responsibilities of the row:
+      * argmax tie: some o_i within eps of r_a (the argmax may move);
+      * threshold: some o_i with i <= max_extra (a candidate whose rank keeps
+        it if it clears the threshold) within eps of the threshold;
+      * rank cut: o_m and o_(m+1), m = max_extra, within eps of each other,
+        with o_(m+1) able to clear the threshold (o_(m+1) >= threshold - eps).
+    The argmax's own responsibility is never tested against the threshold
+    (the argmax is kept whatever its value), and with max_extra = 0 only the
+    argmax tie counts."""
+    r = np.asarray(r, dtype=np.float64)
     flags = np.zeros(r.shape[0], dtype=bool)
+    m = int(max_extra)
     for n in range(r.shape[0]):
         rn = r[n]
-        if np.any(np.abs(rn - threshold) <= eps):
+        a = int(np.argmax(rn))
+        others = np.sort(np.delete(rn, a))[::-1]
+        if others.shape[0] == 0:
+            continue
+        if rn[a] - others[0] <= eps:
             flags[n] = True
             continue
-        if rn.shape[0] > 1:
-            top2 = np.partition(rn, rn.shape[0] - 2)[-2:]
-            if top2[1] - top2[0] <= eps:
-                flags[n] = True
-                continue
-        top = int(np.argmax(rn))
-        extra = np.sort(np.delete(rn, top)[np.delete(rn, top) >= threshold])[::-1]
-        if max_extra >= 1 and extra.shape[0] > max_extra:
-            if extra[max_extra - 1] - extra[max_extra] <= eps:
-                flags[n] = True
+        if m == 0:
+            continue
+        kept_rank = others[:m]
+        if np.any(np.abs(kept_rank - threshold) <= eps):
+            flags[n] = True
+            continue
+        if others.shape[0] > m and others[m] >= threshold - eps and others[m - 1] - others[m] <= eps:
+            flags[n] = True
     return flags
 
 

@@ -320,6 +320,55 @@ def check_soft_assign_invariants(o):
                 assert len(lists[n]) == 1, "threshold above 1 leaves only the argmax"
 
 
+def check_boundary_rows(o):
+    """Hand-built rows (threshold 0.1, eps 1e-5) whose flag follows from the
+    rule by inspection: a row is exempt only where a 1e-5 move of some r can
+    change its list (argmax tie, a keepable candidate at the threshold, a
+    rank tie at the cut m that the (m+1)-th could win)."""
+    e = 1e-5
+    cases = [  # (r, threshold, max_extra, flagged?)
+        ([0.60, 0.30, 0.1 + 0.5 * e, 0.1 - 0.5 * e - 0.0], 0.1, 3, True),    # candidate at the threshold
+        ([0.60, 0.30, 0.1 + 2.0 * e, 0.1 - 2.0 * e], 0.1, 3, False),          # both clear of the threshold
+        ([0.45, 0.45 + 0.5 * e, 0.05, 0.05 - 0.5 * e], 0.1, 3, True),        # argmax tie
+        ([0.70, 0.20, 0.05, 0.05], 0.1, 3, False),                            # nothing near anything
+        ([1.0 - 1e-7, 1e-7], 1.0, 0, False),                                  # argmax at the threshold: kept anyway
+        ([0.3 + 0.5 * e, 0.25, 0.25 - 0.01, 0.2 + 0.01 - 0.5 * e], 0.3, 2, False),  # the same with extras
+        ([0.5 + 3e-6, 0.5 - 3e-6], 1.0, 0, True),                             # argmax tie, argmax-only lists
+        ([0.80, 0.1 + 1e-6, 0.1 - 1e-6], 0.1, 0, False),                      # no extras: the threshold is moot
+        ([0.50, 0.20, 0.2 - 0.5 * e, 0.10 - 0.01], 0.1, 1, True),            # rank tie at the cut m = 1
+        ([0.80, 0.05, 0.05 - 1e-6, 0.03], 0.1, 1, False),                    # tie at the cut, both below
+        ([0.50, 0.30, 0.1 + 1e-6, 0.1 - 1e-6], 0.1, 1, False),              # at the threshold but ranked out
+        ([0.50, 0.30, 0.1 + 1e-6, 0.1 - 1e-6], 0.1, 2, True),               # the same row, now keepable
+        ([0.90], 0.1, 3, False),                                              # one component
+    ]
+    for r, thr, m, want in cases:
+        got = bool(o.boundary_rows(np.array([r], np.float64), thr, m)[0])
+        assert got == want, f"boundary_rows({r}, thr={thr}, m={m}) = {got}, expected {want}"
+    # row-wise: a stack of the rows gives the same flags
+    rows = np.array([c[0] + [0.0] * (4 - len(c[0])) for c in cases if c[1] == 0.1 and c[2] == 3], np.float64)
+    flags = o.boundary_rows(rows, 0.1, 3)
+    assert flags.tolist() == [c[3] for c in cases if c[1] == 0.1 and c[2] == 3]
+
+
+def check_csr_to_lists(o):
+    """Per-row lists recovered from CSR built by hand with dicts: every row's
+    components in ascending order, rows in no list give empty lists."""
+    rng = np.random.default_rng(11)
+    N, K = 40, 7
+    lists = [sorted(rng.choice(K, rng.integers(0, 4), replace=False).tolist()) for _ in range(N)]
+    inv = {k: [n for n in range(N) if k in lists[n]] for k in range(K)}
+    offsets, ids = [0], []
+    for k in range(K):
+        ids += inv[k]
+        offsets.append(len(ids))
+    got = o.csr_to_lists(np.array(offsets, np.int64), np.array(ids, np.int32), N)
+    assert len(got) == N
+    for n in range(N):
+        assert got[n].tolist() == lists[n], f"row {n}: {got[n].tolist()} != {lists[n]}"
+    off, ids2 = o.build_csr([np.array(lst, np.int64) for lst in lists], K)
+    assert off.tolist() == offsets and ids2.tolist() == ids, "build_csr against the hand-built CSR"
+
+
 def check_two_component_logistic(o):
     """Closed form: two equal-weight components at -a and +a with common
     variance s in one dimension give r_2(x) = 1 / (1 + exp(-2 a x / s)) and
@@ -345,5 +394,5 @@ ALL_CHECKS = [
     check_stats_bruteforce, check_stats_invariants, check_k1_closed_form,
     check_mstep_two_pass, check_sklearn_one_step, check_ll_monotone, check_recovery,
     check_floor_and_empty, check_init, check_soft_assign_bruteforce,
-    check_soft_assign_invariants,
+    check_soft_assign_invariants, check_boundary_rows, check_csr_to_lists,
 ]

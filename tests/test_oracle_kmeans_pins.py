@@ -66,20 +66,31 @@ def check_ties_and_empty(o):
 
 
 def check_mixture_from_clusters(o):
-    """Weights N_k / N, means the centres, per-dimension population variance
-    of each cluster about its centre (averaged for the isotropic model)."""
-    X, c0 = _data(5, N=300, D=3, K=4)
-    c, _, _ = o.lloyd(X, c0, 5, store_f32=False)
-    w, mu, v = o.mixture_from_clusters(X, c, 1e-9)
-    a, _ = o.assign(X, c)
-    x = X.astype(np.float64)
-    for k in range(4):
-        rows = x[a == k]
-        np.testing.assert_allclose(w[k], rows.shape[0] / x.shape[0], rtol=1e-15)
-        np.testing.assert_allclose(v[k], np.mean((rows - c[k]) ** 2, axis=0), rtol=1e-12)
-    _, _, vi = o.mixture_from_clusters(X, c, 1e-9, isotropic=True)
-    np.testing.assert_allclose(vi, v.mean(axis=1), rtol=1e-14)
+    """Hand-computed example: rows (0,0), (2,0), (0,4) around the centre
+    (1,2) have squared deviations 1 and 4 in every row, so variances (1, 4)
+    (isotropic 2.5); the row (10,10) sits on its centre (variance 0, floored);
+    a centre at (100,100) gets no rows, hence the all-rows population
+    variances (17, 16.75) of the data; weights 3/4, 1/4, 0.  Then, at a
+    converged clustering (every centre the mean of its rows), each cluster's
+    variances are numpy's population variance of its rows."""
+    X = np.array([[0, 0], [2, 0], [0, 4], [10, 10]], np.float32)
+    c = np.array([[1, 2], [10, 10], [100, 100]], np.float64)
+    w, mu, v = o.mixture_from_clusters(X, c, 1e-3)
+    np.testing.assert_allclose(w, [0.75, 0.25, 0.0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(v, [[1.0, 4.0], [1e-3, 1e-3], [17.0, 16.75]], rtol=1e-15)
     np.testing.assert_array_equal(mu, c)
+    _, _, vi = o.mixture_from_clusters(X, c, 1e-3, isotropic=True)
+    np.testing.assert_allclose(vi, [2.5, 1e-3, 16.875], rtol=1e-15)
+    X, c0 = _data(5, N=300, D=3, K=4)
+    c, _, _ = o.lloyd(X, c0, 50, store_f32=False)
+    a, _ = o.assign(X, c)
+    c_mean = np.stack([X[a == k].astype(np.float64).mean(axis=0) for k in range(4)])
+    np.testing.assert_allclose(c, c_mean, rtol=1e-12, atol=1e-12)  # converged
+    w, _, v = o.mixture_from_clusters(X, c, 1e-9)
+    for k in range(4):
+        rows = X[a == k].astype(np.float64)
+        np.testing.assert_allclose(w[k], rows.shape[0] / X.shape[0], rtol=1e-15)
+        np.testing.assert_allclose(v[k], np.var(rows, axis=0), rtol=1e-10)
 
 
 CHECKS = [check_sklearn_lloyd, check_bruteforce, check_ties_and_empty, check_mixture_from_clusters]
@@ -108,6 +119,12 @@ MUTATIONS = [
      "new = np.where(counts[:, None] > 0, sums / np.maximum(counts, 1.0)[:, None], _f64(centres))",
      "new = sums / np.maximum(counts, 1.0)[:, None]", check_ties_and_empty),
     ("variance about the origin", "np.add.at(dev, a, (x - c[a]) ** 2)", "np.add.at(dev, a, x ** 2)",
+     check_mixture_from_clusters),
+    ("sample variance of a cluster", "dev / np.maximum(counts, 1.0)[:, None]",
+     "dev / np.maximum(counts - 1.0, 1.0)[:, None]", check_mixture_from_clusters),
+    ("isotropic variance summed over dimensions", "var = np.mean(var, axis=1)", "var = np.sum(var, axis=1)",
+     check_mixture_from_clusters),
+    ("empty cluster gets the floor", "glob = np.var(x, axis=0)", "glob = np.zeros(D)",
      check_mixture_from_clusters),
 ]
 

@@ -65,6 +65,18 @@ MUTATIONS = [
      pins.check_two_component_logistic),
     ("gemm form sign slip", "- 2.0 * (X @ (mu * inv).T)", "+ 2.0 * (X @ (mu * inv).T)",
      pins.check_gemm_matches_direct),
+    ("argmax tested against the threshold", "kept_rank = others[:m]",
+     "kept_rank = np.concatenate(([rn[a]], others[:m]))", pins.check_boundary_rows),
+    ("boundary threshold test ignores rank", "kept_rank = others[:m]", "kept_rank = others",
+     pins.check_boundary_rows),
+    ("no argmax tie", "if rn[a] - others[0] <= eps:", "if False:", pins.check_boundary_rows),
+    ("no rank-cut tie", "and others[m - 1] - others[m] <= eps:", "and False:", pins.check_boundary_rows),
+    ("rank cut without the threshold", "others[m] >= threshold - eps and ", "", pins.check_boundary_rows),
+    ("threshold tested with no extras", """        if m == 0:
+            continue
+        kept_rank""", """        kept_rank""", pins.check_boundary_rows),
+    ("CSR list loses its last row", "for n in ids[offsets[k]:offsets[k + 1]]:",
+     "for n in ids[offsets[k]:offsets[k + 1] - 1]:", pins.check_csr_to_lists),
 ]
 
 
