@@ -233,8 +233,13 @@ def test_bit_identical_reruns_and_paths_agree(name):
     if len(res) == 2:
         ms, rms = data_scales(Xn)
         x, y = res[PATH_TWO_SWEEP], res[PATH_FUSED]
+        # each path is held to the float64 oracle at the per-iteration 1e-4
+        # (test_estep_parity), so the two may differ by up to 2e-4; they are
+        # checked against each other at that same 1e-4 (the D=768 case, with
+        # diffuse responsibilities and fp32 contractions on both paths,
+        # differs by 2.7e-5 of S2)
         errs = check_stats((y[0], y[1], y[2], y[3][0]), (x[0], x[1], x[2], x[3][0]), ms, rms,
-                           np.sqrt(params[2].astype(np.float64)), 5e-5)
+                           np.sqrt(params[2].astype(np.float64)), 1e-4)
         assert not errs, "\n".join(errs)
 
 
@@ -324,4 +329,9 @@ def test_workspace_is_independent_of_n():
     assert free1 - free2 <= (64 << 20), "the E-step allocated device memory"
     assert ws < N * K * 4 / 10, "workspace must be far below one N x K float matrix"
     g.check()
-    assert abs(out[0].sum().item() - N) <= 1e-6 * N
+    dev_rel = abs(out[0].sum().item() - N) / N
+    log(f"[workspace] sum_k N_k = N to relative {dev_rel:.3e}")
+    # sum_k r_nk = 1 holds per row to the float32 rounding of log Z and of
+    # the exponentials (a few ulps, 2^-22 = 2.4e-7 relative); in the worst
+    # case those errors share a sign over all N rows
+    assert dev_rel <= 4.0 * 2.0 ** -22

@@ -10,18 +10,28 @@ per quantity, with a scale that keeps it meaningful where a value is near 0:
   S1   |d| <= tol * (|S1| + N_k sigma_kd + rms_d)
   S2   |d| <= tol * (|S2| + ms_d)            (ms_d = mean x_d^2: one point)
   mu   |d| <= tol * (|mu| + sigma)           components with oracle N_k >= 1
-  s^2  |d| <= tol * s^2 + U * (s^2 + mu^2)  components with oracle N_k >= 1
+  s^2  |d| <= tol * s^2                       components with oracle N_k >= 1,
+       |d| <= tol * s^2 + U * (s^2 + mu^2)  collapsed ones (below)
 Components whose oracle N_k < 1 are held to the N_k / pi_k rules only: their
 means and variances come from fractional mass at far-away points.
 
-The variance term U * (s^2 + mu^2), U = 1e-6 (16 float32 ulps): Eq. (3) of
-the Flash-GMM paper is evaluated from S1 and S2 as s^2 = S2/N_k - mu^2, and
-S2 is accumulated from float32 x^2 (the paper's 4-byte storage).  For a
-component that has collapsed onto a few points (s^2 at the floor, s^2 <<
-mu^2) that difference cancels to the rounding of x^2 itself, about
-2^-24 mu^2, whatever the accumulation precision; the float64 oracle has no
-such floor.  For well-conditioned components (mu^2 / s^2 up to about 100) U
-adds at most about 1e-4 * s^2, so the tolerance stays near relative 1e-4.
+Collapsed components.  Eq. (3) of the Flash-GMM pages is evaluated from the
+statistics as s^2 = S2/N_k - mu^2, and the library's statistics are
+float32-grade (x^2 formed in float32, the statistics contraction exact to
+float32 rounding, float32 partial sums over at most 2048 rows before each
+float64 flush).  Their error is a few float32 ulps of the second moment
+S2/N_k = s^2 + mu^2, whatever s^2 is.  For a component whose mass sits on a
+few rows the worst case counts: x^2 rounded (1 ulp), the split product's
+omitted third-order parts (2), one accumulator rounding per bfloat16 pass
+(6), the same again for the S1 that gives mu^2 (twice: 18), the float64
+M-step and the float32 store (< 1), so U = 32 * 2^-24.  Where s^2 is more
+than 2^-10 of s^2 + mu^2 the tests hold the plain relative tolerance: the
+measured error there is below 5e-6 s^2 (many rows' rounding errors do not
+add up to the worst case), although U * (s^2 + mu^2) could reach 2^-9 s^2.
+Where s^2 <= 2^-10 (s^2 + mu^2) (a component that has collapsed onto a few
+points, s^2 often at the floor, s^2 << mu^2) the difference cancels more
+than ten of the 24 bits of S2/N_k, and the slack U * (s^2 + mu^2) is added;
+the float64 oracle has no such limit.
 """
 from __future__ import annotations
 
@@ -54,7 +64,8 @@ def check_stats(got, want, X_ms, X_rms, sigma, tol):
     return [m for m in out if m]
 
 
-VAR_ULP = 1e-6  # float32 cancellation floor of s^2 = S2/N_k - mu^2, relative to S2/N_k
+VAR_ULP = 32.0 * 2.0 ** -24    # float32 resolution of S2/N_k (see the module text)
+COLLAPSED = 2.0 ** -10          # s^2 / (s^2 + mu^2) at or below which a component counts as collapsed
 
 
 def check_params(got, want, Nk_ref, N, tol):
@@ -65,7 +76,10 @@ def check_params(got, want, Nk_ref, N, tol):
     out = [_viol("pi", w_g, w, tol * np.maximum(w, 1.0 / N))]
     sd = np.sqrt(v)
     out.append(_viol("mu", mu_g[live], mu[live], tol * (np.abs(mu[live]) + sd[live])))
-    out.append(_viol("var", v_g[live], v[live], tol * v[live] + VAR_ULP * (v[live] + mu[live] ** 2)))
+    vl, ml = v[live], mu[live]
+    m2 = vl + ml ** 2
+    slack = np.where(vl <= COLLAPSED * m2, VAR_ULP * m2, 0.0)
+    out.append(_viol("var", v_g[live], vl, tol * vl + slack))
     return [m for m in out if m]
 
 
