@@ -27,7 +27,9 @@
  *     gmm_last_error().  A failed call leaves caller arrays unspecified only
  *     when the status is GMM_ERR_HIP or GMM_ERR_NUMERIC.
  *   - The same inputs on the same device and build give bit-identical
- *     outputs: no floating-point atomics, fixed reduction trees.
+ *     outputs: fixed reduction trees, and floating-point atomic adds only
+ *     into words that a single lane of a single workgroup writes (their
+ *     order is that lane's program order), never a contended one.
  *   - A context is not thread-safe; distinct contexts are independent.
  */
 #ifndef FLASHGMM_H
@@ -111,7 +113,10 @@ typedef enum {
 /* Create a context for K components of dimension D on the current HIP device.
  * hip_stream is a hipStream_t (NULL = the null stream).  Allocates the
  * workspace, whose size depends on K, D and the device but not on N (see
- * gmm_workspace_bytes); nothing else is allocated later.
+ * gmm_workspace_bytes).  The only later allocations are those of the
+ * out-of-core calls (gmm_estep_stats_host, gmm_fit_host): a copy stream and
+ * two device staging buffers, made on their first use and grown when a call
+ * asks for larger chunks; every other entry point allocates nothing.
  * 1 <= K <= 65536, 1 <= D <= 1024. */
 gmm_status gmm_create(gmm_ctx **out /*[host]*/, int32_t K, int32_t D, void *hip_stream);
 
@@ -172,7 +177,10 @@ gmm_status gmm_mstep(gmm_ctx *ctx, const double *Nk, const double *S1, const dou
                      double n_total, float var_floor,
                      float *weights, float *means, float *vars /*[dev], in/out*/);
 
-/* T EM iterations from the parameters passed in (updated in place).
+/* T EM iterations from the parameters passed in (updated in place): each is
+ * the E-step above followed by the M-step above (Section 2: the E-step's
+ * responsibilities, then Eqs. (1)-(3)), the loop of Algorithm 1 run for a
+ * fixed number of iterations (Section 3.4 times 30 of them).
  * loglik_hist [dev] float64[T]: entry t is the log-likelihood of the
  * parameters entering iteration t.  No host synchronisation inside. */
 gmm_status gmm_fit(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_t ldx, int32_t T,

@@ -7,8 +7,11 @@ is no fallback of any kind, and a missing library raises at import.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import sys
+import weakref
 
 import numpy as np
 import torch
@@ -114,8 +117,28 @@ def _rows(X, D, device):
     return X.shape[0], X.stride(0) if X.shape[0] > 1 else ((D + 3) // 4) * 4
 
 
+_LIVE: "weakref.WeakSet[GMM]" = weakref.WeakSet()
+
+
+@atexit.register
+def _close_all():
+    """Destroy every live context while the HIP runtime is still up: torch
+    registers its own exit handlers when it is imported, before this module,
+    and exit handlers run last-registered first, so this runs ahead of them.
+    Afterwards no library call is left for a finaliser to make during
+    interpreter teardown."""
+    for g in list(_LIVE):
+        try:
+            g.close()
+        except Exception:
+            pass
+
+
 class GMM:
-    """A context for K components of dimension D on the current HIP device."""
+    """A context for K components of dimension D on the current HIP device.
+
+    Release it with close() (or use it as a context manager); contexts still
+    open when the interpreter exits are closed by an exit handler."""
 
     def __init__(self, K: int, D: int, device=None):
         if not torch.cuda.is_available():
@@ -131,16 +154,29 @@ class GMM:
             if st != GMM_OK:
                 raise GMMError(st, _lib.gmm_last_error(None).decode())
         self._h = h
+        _LIVE.add(self)
 
     def close(self):
+        """Synchronise the context's stream and release its workspace."""
         h = getattr(self, "_h", None)
         self._h = None
         if h:
-            _lib.gmm_destroy(h)
+            with torch.cuda.device(self.device):
+                _lib.gmm_destroy(h)
+        _LIVE.discard(self)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+        return False
 
     def __del__(self):
-        # at interpreter shutdown the module globals may already be gone; the
-        # driver releases device memory with the process then
+        # never call into the library while the interpreter is finalising
+        # (the exit handler above has closed every context by then)
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:

@@ -1,7 +1,9 @@
 """Builds libflashgmm.so (gfx950) in-tree with hipcc.
 
-Usage: python soft_clustering_amd/build.py [--verbose] [--resource-usage]
-(loaded by path, so a stale library is never imported while building)
+Usage: python soft_clustering_amd/build.py [--verbose] [--resource-usage] [--incremental]
+(loaded by path, so a stale library is never imported while building).
+--incremental recompiles only objects older than their source or a header;
+the default recompiles everything.
 """
 from __future__ import annotations
 
@@ -35,8 +37,21 @@ def hipcc() -> str:
     return p
 
 
-def _compile(src: str, verbose: bool, resource: bool) -> str:
+HEADERS = [os.path.join(CSRC, "gmm_device.h"), os.path.join(CSRC, "gmm_internal.h"),
+           os.path.join(ROOT, "include", "flashgmm.h")]
+
+
+def _stale(src: str, obj: str) -> bool:
+    if not os.path.exists(obj):
+        return True
+    newest = max(os.path.getmtime(p) for p in [os.path.join(CSRC, src), *HEADERS] if os.path.exists(p))
+    return os.path.getmtime(obj) < newest
+
+
+def _compile(src: str, verbose: bool, resource: bool, incremental: bool = False) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if incremental and not resource and not _stale(src, obj):
+        return obj
     cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     if resource:
         cmd += ["-Rpass-analysis=kernel-resource-usage"]
@@ -52,11 +67,11 @@ def _compile(src: str, verbose: bool, resource: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, resource: bool = False) -> str:
+def build(verbose: bool = False, resource: bool = False, incremental: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
     with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, resource), srcs))
+        objs = list(ex.map(lambda s: _compile(s, verbose, resource, incremental), srcs))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
@@ -69,4 +84,5 @@ def build(verbose: bool = False, resource: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv, resource="--resource-usage" in sys.argv))
+    print(build(verbose="--verbose" in sys.argv, resource="--resource-usage" in sys.argv,
+                incremental="--incremental" in sys.argv))

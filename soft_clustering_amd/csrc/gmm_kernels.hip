@@ -7,13 +7,18 @@
 // M-step Eqs. (1)-(3).  The covariance here is diagonal.
 //
 // Design for CDNA4, not a port of the paper's Triton kernel:
-//  * Both contractions run on v_mfma_f32_16x16x4_f32.  The logit contraction
-//    L[pt][comp] = sum_f A[pt][f] W[f][comp] + c[comp] uses features
-//    A = [x^2 | x] and weights W = [-1/(2 s^2) | mu/s^2] (the expanded
-//    quadratic); its accumulator layout (lane = component, register = point)
-//    is exactly the A-operand layout of the statistics contraction
+//  * The logit contraction L[pt][comp] = sum_f A[pt][f] W[f][comp] + c[comp]
+//    uses features A = [x^2 | x] and weights W = [-1/(2 s^2) | mu/s^2] (the
+//    expanded quadratic).  By default it runs on the bfloat16 matrix units as
+//    a split product (x = x_hi + x_lo, W likewise; three passes of
+//    v_mfma_f32_16x16x32_bf16), and every logit that can carry
+//    responsibility is recomputed in float64; v_mfma_f32_16x16x4_f32 and
+//    v_mfma_f64_16x16x4_f64 variants exist for the other settings.  The
+//    accumulator layout (lane = component, register = point) is exactly the
+//    A-operand layout of the statistics contraction
 //    S[comp][phi] += sum_pt r[comp][pt] F[pt][phi], F = [x^2 | x], so
-//    responsibilities go from registers straight into the second MFMA.
+//    responsibilities go from registers straight into the second MFMA
+//    (three-part split bfloat16, six passes, or fp32).
 //  * A workgroup owns 32*WC components and a strided set of row tiles; its
 //    statistics stay in registers (fp32) and are flushed into a private
 //    float64 slot every few tiles; a fixed-order pairwise tree over the slots
@@ -24,8 +29,10 @@
 //    workgroups that share a row tile exchanging their per-row partial
 //    log-sum-exp through tagged 64-bit words in device memory (cooperative
 //    launch guarantees they are co-resident), so each logit is computed once.
-//  * X tiles are staged in LDS as [x^2_lo | x_lo | x^2_hi | x_hi] per row so
-//    one ds_read_b128 gives a lane four consecutive MFMA k-steps.
+//  * X tiles are staged in LDS as raw float32 rows (a 4-float pad per row
+//    keeps the 16 rows of an MFMA operand load on distinct banks), by LDS DMA
+//    where rows need no padding; the split-bfloat16 operand tiles are built
+//    from them in LDS once per tile and shared by every wave.
 #include "gmm_device.h"
 
 #include <math.h>
