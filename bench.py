@@ -25,18 +25,24 @@ MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, AMD published figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, AMD published figure
 HBM_PEAK_GBS = 8000.0
 
+# The configured workloads; the timed iterations are --steps (after --warmup
+# untimed ones), and the line reports what 30 iterations (the configured run
+# of the large and mid workloads) take at the measured rate.
 WORKLOAD_TEXT = {
-    "large": "large EM: N=100,000,000, D=128, K=1024, fp32, diagonal covariance, 30 EM iterations",
-    "mid": "mid EM: N=1,000,000, D=128, K=1024, fp32, diagonal covariance, 30 EM iterations",
-    "tiny": "tiny EM: N=10,000, D=8, K=16, fp32, diagonal covariance, 10 EM iterations",
-    "embed": "embedding-like EM: N=10,000,000, D=768, K=4096, fp32, diagonal covariance, 20 EM iterations",
-    "iso": "isotropic EM (sigma_k^2 I): N=100,000,000, D=128, K=1024, fp32, 30 EM iterations",
+    "large": "large EM: N=100,000,000, D=128, K=1024, fp32, diagonal covariance (configured run: 30 EM iterations)",
+    "mid": "mid EM: N=1,000,000, D=128, K=1024, fp32, diagonal covariance (configured run: 30 EM iterations)",
+    "tiny": "tiny EM: N=10,000, D=8, K=16, fp32, diagonal covariance (configured run: 10 EM iterations)",
+    "embed": "embedding-like EM: N=10,000,000, D=768, K=4096, fp32, diagonal covariance "
+             "(configured run: 20 EM iterations)",
+    "iso": "isotropic EM (sigma_k^2 I): N=100,000,000, D=128, K=1024, fp32 (30 EM iterations as the large run)",
     "stream": "out-of-core EM: the large data (N=100,000,000, D=128, K=1024) in pinned host memory, streamed in "
-              "2^24-row chunks, 30 EM iterations",
+              "2^24-row chunks",
     "kmeans": "k-means warm start: Lloyd iterations at N=100,000,000, D=128, K=1024 (the large data), fp32",
-    "ivf": "IVF: EM on a 1,000,000-row sample, D=128, K=16384, integer values 0..255, 10 EM iterations; "
-           "then soft assignment (argmax + up to 3 with r >= 0.1) of 10,000,000 base rows into CSR lists",
+    "ivf": "IVF: EM on a 1,000,000-row sample, D=128, K=16384, integer values 0..255 (configured run: 10 EM "
+           "iterations); soft assignment (argmax + up to 3 with r >= 0.1) of 10,000,000 base rows into CSR lists; "
+           "10,000 queries probed at nprobe 8, 16, 32, 64 with recall@10 against exact search",
 }
+CONFIGURED_ITERS = {"large": 30, "mid": 30, "tiny": 10, "embed": 20, "iso": 30, "ivf": 10}
 
 
 def useful_flops(N, K, D, iso=False):
@@ -109,10 +115,36 @@ def measured_traffic():
     return float(fields["traffic_bytes_per_launch"])
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(O, X, w, mu, var, n, floor, budget_s, max_iters):
+    """Seconds per EM iteration of the oracle on X (at least one iteration)."""
+    t0 = time.perf_counter()
+    iters = 0
+    while True:
+        Nk, S1, S2, ll = O.estep_stats(X, w, mu, var, method="gemm")  # S2: Q for the isotropic model
+        w, mu, var = O.mstep(Nk, S1, S2, n, floor, mu, var)
+        iters += 1
+        if time.perf_counter() - t0 > budget_s or iters >= max_iters:
+            break
+    return (time.perf_counter() - t0) / iters, iters
+
+
 def cpu_baseline(workload, sample_rows, budget_s):
-    """Time the oracle as it stands on a prefix of the same data, scaled to
-    ms per EM iteration at the full N (EM cost is linear in N)."""
+    """Time the oracle as it stands on a prefix of the same data with every
+    host core, then once more on one thread on a tenth of that prefix,
+    each scaled to ms per EM iteration at the full N (EM cost is linear in N)."""
     import torch
+    from threadpoolctl import threadpool_limits
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from soft_clustering_amd import datagen
     iso = workload == "iso"
@@ -126,24 +158,27 @@ def cpu_baseline(workload, sample_rows, budget_s):
     X = datagen.sample(mix, n, seed=wl.seed).numpy()
     rows = datagen.init_rows(n, wl.K, seed=wl.init_seed)
     w, mu, var = O.init(X, rows, wl.var_floor)
-    cores = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    iters = 0
-    while True:
-        Nk, S1, S2, ll = O.estep_stats(X, w, mu, var, method="gemm")  # S2: Q for the isotropic model
-        w, mu, var = O.mstep(Nk, S1, S2, n, wl.var_floor, mu, var)
-        iters += 1
-        if time.perf_counter() - t0 > budget_s or iters >= 3:
-            break
-    dt = (time.perf_counter() - t0) / iters
+    from threadpoolctl import threadpool_info
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    cores = max(blas) if blas else 1  # the threads the oracle's BLAS calls use
+    dt, iters = _oracle_rate(O, X, w, mu, var, n, wl.var_floor, budget_s, 3)
+    n1 = max(wl.K, n // 10)
+    with threadpool_limits(limits=1):
+        dt1, iters1 = _oracle_rate(O, X[:n1], w, mu, var, n1, wl.var_floor, budget_s / 2, 1)
     n_full = wl.extra.get("train_rows", wl.N)  # EM runs on the training sample for ivf
     ms_full = dt * 1e3 * (n_full / n)
     return {"value": ms_full, "unit": "ms per EM iteration (extrapolated linearly in N)", "cores": cores,
             "kind": "oracle",
             "sample": f"{iters} EM iteration(s) of the float64 numpy oracle on the first {n} rows of the "
-                      f"{workload} workload ({dt:.2f} s each), scaled by {n_full}/{n}",
+                      f"{workload} workload ({dt:.2f} s each, BLAS on {cores} threads of "
+                      f"{len(os.sched_getaffinity(0))} host CPUs), scaled by {n_full}/{n}",
             "gflops": useful_flops(n, wl.K, wl.D, iso) / dt / 1e9,
-            "torch_threads": torch.get_num_threads()}
+            "cpu_model": cpu_model(),
+            "torch_threads": torch.get_num_threads(),
+            "one_thread": {"value": dt1 * 1e3 * (n_full / n1), "unit": "ms per EM iteration (extrapolated)",
+                           "cores": 1, "sample": f"{iters1} EM iteration(s) on the first {n1} rows "
+                                                 f"({dt1:.2f} s each) on one BLAS thread",
+                           "gflops": useful_flops(n1, wl.K, wl.D, iso) / dt1 / 1e9}}
 
 
 def bench_stream(args):
@@ -183,6 +218,7 @@ def bench_stream(args):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     g.check()
+    g.close()
     ms = dt * 1e3 / args.steps
     F = useful_flops(N, K, D)
     line = {"metric": "ms per EM iteration with X streamed from pinned host memory (PCIe-inclusive)",
@@ -225,6 +261,7 @@ def bench_kmeans(args):
     _, counts, _, _ = g.kmeans(X, c, args.steps, lists=lists)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    g.close()
     ms = dt * 1e3 / args.steps
     useful = 2.0 * N * K * D  # the x.c products of the distances
     line = {"metric": "ms per Lloyd iteration (k-means warm start)", "value": round(ms, 3), "unit": "ms",
@@ -261,6 +298,7 @@ def main():
                          "split-bf16 logits only, or fp32")
     ap.add_argument("--rows", type=int, default=0, help="override N (testing only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-recall", action="store_true", help="ivf: skip the probe / recall@10 evaluation")
     ap.add_argument("--cpu-sample-rows", type=int, default=250_000)
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -376,6 +414,10 @@ def main():
                      "kernel_ms_per_iteration": round(kern_ms, 3),
                      "avg_launch_ms": round(avg_ms, 3), "launches": stats_n + logz_n},
         "loglik_first_last": [float(hl[0]), float(hl[-1])],
+        "configured_iterations": CONFIGURED_ITERS.get(args.workload),
+        "configured_run_ms": (round(ms_step * CONFIGURED_ITERS[args.workload], 1)
+                              if args.workload in CONFIGURED_ITERS else None),
+        "configured_run_ms_basis": "configured iterations x the measured ms per timed iteration",
         "refined_logit_fraction": n_ref / max(n_logits, 1.0),
         "x_hbm_gbs_once": round(N * D * 4 / (avg_ms * 1e-3) / 1e9, 1),
     }
@@ -411,11 +453,49 @@ def main():
             top2.append({"tau_times_K": f, "ms": round(dt_t * 1e3, 1), "lists_per_row": round(ids.shape[0] / nb, 4)})
             del offsets, ids
         line["soft_assign_top2"] = top2
+        if not args.no_recall:
+            line["ivf_search"] = ivf_recall(g, Xb, w, mu, var, mix, wl, dev)
         del Xb
         torch.cuda.empty_cache()
+    g.close()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_rows, args.cpu_budget_s)
     print(json.dumps(line), flush=True)
+
+
+def ivf_recall(g, Xb, w, mu, var, mix, wl, dev):
+    """Recall@10 and distance computations of IVF search over the lists of
+    each assignment rule: argmax only, the configured multi-assignment
+    (argmax + up to 3 with r >= 0.1) and the pages' top-2 rule at tau in
+    {0.5, 1, 2}/K; queries probe nprobe in {8, 16, 32, 64} nearest means."""
+    import torch
+    from soft_clustering_amd import datagen, ivf_probe
+    K = wl.K
+    Q = datagen.query_rows(mix, wl.extra["queries"], seed=wl.seed, device=dev)
+    t0 = time.perf_counter()
+    truth, _ = ivf_probe.exact_topk(Q, Xb, 10)
+    torch.cuda.synchronize()
+    out = {"queries": int(Q.shape[0]), "exact_topk_s": round(time.perf_counter() - t0, 2), "rules": []}
+    rules = [("argmax", 1.0, 0), (f"argmax+{wl.extra['max_extra']}@r>={wl.extra['threshold']}",
+                                  wl.extra["threshold"], wl.extra["max_extra"])]
+    rules += [(f"top2@tau={f}/K", f / K, 1) for f in (0.5, 1.0, 2.0)]
+    nb = Xb.shape[0]
+    for name, thr, m in rules:
+        offsets, ids = g.soft_assign(Xb, w, mu, var, thr, m)
+        mbar = ids.shape[0] / nb
+        pts = []
+        for nprobe in wl.extra["nprobe"]:
+            t0 = time.perf_counter()
+            found, _, dco = ivf_probe.search(Q, Xb, offsets, ids, mu, nprobe)
+            torch.cuda.synchronize()
+            r10, r1 = ivf_probe.recall(found, truth)
+            pts.append({"nprobe": nprobe, "recall@10": round(r10, 4), "1-recall@10": round(r1, 4),
+                        "dco_mean": round(float(dco.to(torch.float64).mean()), 1),
+                        "dco_identity": round(ivf_probe.dco_identity(offsets, nb, nprobe), 1),
+                        "search_s": round(time.perf_counter() - t0, 2)})
+        out["rules"].append({"rule": name, "lists_per_row": round(mbar, 4), "points": pts})
+        del offsets, ids
+    return out
 
 
 if __name__ == "__main__":

@@ -172,6 +172,32 @@ def sample(mix: Mixture, rows: int, start: int = 0, seed: int = 0, stream: int =
     return buf[:, :D]
 
 
+def sample_portable(mix: Mixture, rows: int, seed: int = 0) -> np.ndarray:
+    """Rows of the law drawn with numpy's PCG64 stream alone (labels by
+    inverse CDF of uniforms, then standard normals; elementwise float64
+    arithmetic, one rounding to float32).  Unlike ``sample`` (torch
+    generators, whose CPU kernels differ between instruction sets), the
+    result is the same bytes on any x86-64 host running the same numpy, so
+    expected values computed once from it can be stored and checked later
+    on another machine.  Returns a (rows, D) float32 array."""
+    rng = np.random.default_rng([seed, 0x5EED])
+    cdf = np.cumsum(mix.weights)
+    cdf[-1] = 1.0
+    labels = np.minimum(np.searchsorted(cdf, rng.random(rows), side="right"), mix.K - 1)
+    noise = rng.standard_normal((rows, mix.D))
+    x = mix.means[labels] + mix.stds[labels] * noise
+    if mix.law == "embed":
+        # squared norms summed column by column: elementwise operations only,
+        # so the order of the additions cannot depend on the host's SIMD width
+        ss = x[:, 0] * x[:, 0]
+        for d in range(1, mix.D):
+            ss = ss + x[:, d] * x[:, d]
+        x = x / np.sqrt(ss)[:, None]
+    elif mix.law == "ivf":
+        x = np.clip(np.round(x), 0.0, 255.0)
+    return x.astype(np.float32)
+
+
 def init_rows(N: int, K: int, seed: int = 1) -> np.ndarray:
     """K distinct row indices drawn without replacement (int64, host)."""
     if K > N:
@@ -197,5 +223,5 @@ def random_params(K: int, D: int, seed: int, scale: float = 1.0, var_lo: float =
     return w, mu, var
 
 
-__all__ = ["CHUNK", "WORKLOADS", "Workload", "Mixture", "mixture", "sample", "sample_into",
+__all__ = ["CHUNK", "WORKLOADS", "Workload", "Mixture", "mixture", "sample", "sample_into", "sample_portable",
            "init_rows", "query_rows", "random_params"]
