@@ -40,34 +40,33 @@ struct AArgs {
   unsigned long long* counts;    // K list sizes (pass A) or nullptr
   float log_thr;                 // log(threshold)
   float delta;                   // float64 window below the row's largest logit
+  float cand_off;                // candidate bound offset: min(log(threshold), 0) with extras, 0 without
   int m;                         // max_extra
 };
 
-// Insert (val, k) into a list sorted by value descending, index ascending.
-// FULL = false: k is larger than every index already in the list (one wave's
-// own stream), so an equal value ranks after the existing entries.
-template <bool FULL>
+constexpr float kLag = 20.f;     // lag of the log-sum-exp reference (e^20 * K stays finite)
+
+// Insert (val, k) into a list sorted by value descending, index ascending:
+// the carried entry walks down the list and trades places with every entry
+// it ranks before, so the list stays sorted and the last entry falls off.
+// Branch-free: the same instructions for every lane and any input.
 __device__ __forceinline__ void top_insert(float (&tv)[kTopN], int (&tk)[kTopN], float val, int k) {
-  auto better = [&](float v2, int k2) { return FULL ? (val > v2 || (val == v2 && k < k2)) : (val > v2); };
-  if (!better(tv[kTopN - 1], tk[kTopN - 1])) return;
 #pragma unroll
-  for (int i = kTopN - 1; i > 0; --i) {
-    if (better(tv[i - 1], tk[i - 1])) {
-      tv[i] = tv[i - 1];
-      tk[i] = tk[i - 1];
-    } else if (better(tv[i], tk[i])) {
-      tv[i] = val;
-      tk[i] = k;
-    }
-  }
-  if (better(tv[0], tk[0])) {
-    tv[0] = val;
-    tk[0] = k;
+  for (int i = 0; i < kTopN; ++i) {
+    const bool b = (val > tv[i]) || (val == tv[i] && k < tk[i]);
+    const float ov = tv[i];
+    const int ok = tk[i];
+    tv[i] = b ? val : ov;
+    tk[i] = b ? k : ok;
+    val = b ? ov : val;
+    k = b ? ok : k;
   }
 }
 
+// Orders a wave's LDS writes before its later reads by other lanes of the
+// same wave (the fence waits for the wave's outstanding LDS operations).
 __device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   __builtin_amdgcn_wave_barrier();
 }
 
@@ -183,31 +182,79 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
         refine_tile<SH, WD, DPW>(acc, thrw[wc], nrm, co, xt, rows, a, C, compbase, rlist[SH::COOP ? wc : w], elist[SH::COOP ? wc : w], lane,
                                  wd, nsel);
       }
+      // online log-sum-exp with a lagging reference: the running reference
+      // M moves only when a logit exceeds it by more than kLag nats, so the
+      // rescaling exponential is rare; S then holds terms up to e^kLag
 #pragma unroll
       for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float mn = fmaxf(M[pb][v], fmaxf(acc[pb][0][v], acc[pb][1][v]));
-          const float ms = (mn == kNegInf) ? 0.f : mn;
-          S[pb][v] = S[pb][v] * __expf(M[pb][v] - ms) + __expf(acc[pb][0][v] - ms) +
-                     __expf(acc[pb][1][v] - ms);
-          M[pb][v] = mn;
-        }
-      // per-row top lists: transpose each 16-component block through LDS so
-      // lane p sees row p's values, components in ascending order
-      if (wd == 0) {
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-#pragma unroll
-          for (int pb = 0; pb < NPB; ++pb)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) tl[r16 * (BN + 1) + pb * 16 + 4 * g + v] = acc[pb][cb][v];
-          wave_sync();
-          if (lane < BN) {
-#pragma unroll 4
-            for (int j = 0; j < 16; ++j) top_insert<false>(tv, tk, tl[j * (BN + 1) + lane], compbase + cb * 16 + j);
+          const float mn = fmaxf(acc[pb][0][v], acc[pb][1][v]);
+          if (mn > M[pb][v] + kLag) {
+            S[pb][v] = (M[pb][v] == kNegInf) ? 0.f : S[pb][v] * __expf(M[pb][v] - mn);
+            M[pb][v] = mn;
           }
-          wave_sync();
+          const float ms = (M[pb][v] == kNegInf) ? 0.f : M[pb][v];
+          S[pb][v] += __expf(acc[pb][0][v] - ms) + __expf(acc[pb][1][v] - ms);
+        }
+      // per-row top lists.  Only a logit at or above the row's candidate bound
+      // can be selected: the argmax is at least the largest lower bound Rlb of
+      // the row's logits seen so far (less one float32 rounding of a refined
+      // value), and an extra needs l - log Z >= log(threshold) with
+      // log Z >= that maximum.  The wave's candidates are compacted into a
+      // list (lane-major); lane p then inserts the entries of row p.
+      if (wd == 0) {
+        unsigned cbits = 0;
+#pragma unroll
+        for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            if constexpr (!REFINE) Rlb[pb][v] = fmaxf(Rlb[pb][v], row16_max(fmaxf(acc[pb][0][v], acc[pb][1][v])));
+            const float rb = Rlb[pb][v];
+            const float bound = rb + s.cand_off - (fabsf(rb) * 2.4e-7f + 1e-6f);
+            const bool rok = pb * 16 + 4 * g + v < rows;
+            cbits |= (rok && acc[pb][0][v] >= bound ? 1u : 0u) << (pb * 8 + v);
+            cbits |= (rok && acc[pb][1][v] >= bound ? 1u : 0u) << (pb * 8 + 4 + v);
+          }
+        const int c = __popc(cbits);
+        int pre = 0, total = 0;
+#pragma unroll
+        for (int b = 0; b < 6; ++b) {
+          const unsigned long long m = __ballot((c >> b) & 1);
+          pre += (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u)) << b;
+          total += __popcll(m) << b;
+        }
+        if (total > 0) {
+          // tl[0, CAPC): candidate values; tl[CAPC, 2 CAPC): their codes
+          // (register << 6 | lane) as float bit patterns
+          constexpr int CAPC = TBW / 2;
+          for (int b0 = 0; b0 < total; b0 += CAPC) {
+            const int n = min(CAPC, total - b0);
+            {
+              int idx = pre - b0;
+#pragma unroll
+              for (int r = 0; r < NPB * 8; ++r)
+                if ((cbits >> r) & 1u) {
+                  if (idx >= 0 && idx < CAPC) {
+                    tl[idx] = acc[r >> 3][(r >> 2) & 1][r & 3];
+                    tl[CAPC + idx] = __int_as_float((r << 6) | lane);
+                  }
+                  ++idx;
+                }
+            }
+            wave_sync();
+            if (lane < BN) {
+#pragma unroll 1
+              for (int e = 0; e < n; ++e) {
+                const int code = __float_as_int(tl[CAPC + e]);
+                const float cvv = tl[e];
+                const int r = code >> 6, ln = code & 63;
+                if ((r >> 3) * 16 + 4 * (ln >> 4) + (r & 3) == lane)
+                  top_insert(tv, tk, cvv, compbase + ((r >> 2) & 1) * 16 + (ln & 15));
+              }
+            }
+            wave_sync();
+          }
         }
       }
     }
@@ -239,7 +286,7 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
         for (int i = 0; i < kTopN; ++i) {
           const float v = o[i * BN + tid];
           if (v == kNegInf) break;
-          top_insert<true>(tv, tk, v, __float_as_int(o[(kTopN + i) * BN + tid]));
+          top_insert(tv, tk, v, __float_as_int(o[(kTopN + i) * BN + tid]));
         }
       }
       if (tid < rows) {
@@ -476,6 +523,7 @@ hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* 
   const double lt = log((double)threshold);
   sa.log_thr = (float)lt;
   sa.delta = (float)(1.0 - lt > 16.0 ? 1.0 - lt : 16.0);
+  sa.cand_off = max_extra > 0 ? (float)(lt < 0.0 ? lt : 0.0) : 0.f;
   sa.m = max_extra;
   void* args[] = {&a, &sa};
   const int64_t tiles = (rows + p.BN - 1) / p.BN;

@@ -142,6 +142,48 @@ def test_soft_assign_parity(name, mfma):
         assert ids.shape[0] == N  # argmax only
 
 
+@pytest.mark.parametrize("mfma", ["split", "fp32"])
+def test_soft_assign_exact_duplicate_components(mfma):
+    """Components given identical parameters have bit-identical logits on both
+    sides, so every row near them holds exact responsibility ties, which the
+    rule breaks by the lower index: a row that lists the higher index of a
+    duplicated pair must list the lower one too, no row may list a component
+    twice, and rows clear of other near-ties match the oracle exactly.  The
+    pairs sit in different waves' component groups (k and k + 32, k + 96),
+    in one group's two 16-component blocks (k and k + 16), and side by side
+    (k and k + 1)."""
+    from soft_clustering_amd import MFMA_FP32
+    K, D, N = 1024, 128, 30_011
+    thr, m = 0.1, 3
+    mix = datagen.mixture("ivf", D, K, seed=5)
+    pairs = [(7, 39), (300, 396), (512, 528), (700, 701), (900, 932)]
+    means, stds = mix.means.copy(), mix.stds.copy()
+    for a, b in pairs:
+        means[b], stds[b] = means[a], stds[a]
+    mix = datagen.Mixture(np.full(K, 1.0 / K), means, stds, "ivf")
+    Xc = datagen.sample(mix, N, seed=5)
+    Xg = Xc.to(DEV)
+    w = np.full(K, 1.0 / K, np.float32)
+    mu, var = means.astype(np.float32), (stds ** 2).astype(np.float32)
+    g = GMM(K, D, DEV)
+    if mfma == "fp32":
+        g.set_mfma(MFMA_FP32)
+    offsets, ids = g.soft_assign(Xg, *(torch.as_tensor(a).to(DEV) for a in (w, mu, var)), thr, m)
+    gpu = csr_rows(offsets, ids, N, 1 + m)  # also: no row twice in a list
+    for a, b in pairs:
+        has_b = np.any(gpu == b, axis=1)
+        assert np.all(np.any(gpu[has_b] == a, axis=1)), f"rows list {b} without its twin {a}"
+        assert has_b.sum() > 0, f"no row near the pair ({a}, {b})"
+    _, _, lists, boundary = O.soft_assign(Xc.numpy(), w, mu, var, thr, m, method="gemm", chunk_rows=2048)
+    # exempt only near-ties other than the exact ones: rank the oracle's r
+    # with each duplicate folded into its twin
+    r, _ = O.responsibilities(Xc.numpy(), w, mu, var, method="gemm")
+    for a, b in pairs:
+        r[:, b] = 0.0
+    other = O.boundary_rows(r, thr, m)
+    compare(gpu, lists, other, f"duplicates ({mfma})")
+
+
 def test_soft_assign_chunks_compose():
     """Rows past the first 2^19-row chunk go through the second selection
     pass and the list cursors: the lists of X equal the lists of its two
