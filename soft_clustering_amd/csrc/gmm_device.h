@@ -340,8 +340,12 @@ struct SplitRow {
 // LDS-DMA row assignment with one instruction per row) from float32 in xt
 // to split bfloat16 operands in xsb.  Called after this wave's dma_wait, so
 // the rows it reads are its own DMA's; the next barrier publishes xsb.
+// With nrm given (DPW = 128: one row per 16-lane DPP row and pass), the
+// rows' ||x||^2 and ||x||_1 are formed on the way (slightly rounded up, as
+// row_norms2) and written to nrm, published by the same barrier.
 template <class SH, int DPW, bool ISO>
-__device__ __forceinline__ void split_rows(const float* __restrict__ xt, __bf16* __restrict__ xsb, int w) {
+__device__ __forceinline__ void split_rows(const float* __restrict__ xt, __bf16* __restrict__ xsb, int w,
+                                           float2* __restrict__ nrm = nullptr) {
   using SR = SplitRow<DPW, ISO>;
   constexpr int BN = SH::TILE / SH::RS;
   constexpr int NW = SH::NT / kWave;
@@ -349,10 +353,28 @@ __device__ __forceinline__ void split_rows(const float* __restrict__ xt, __bf16*
   constexpr int RPW = (BN + NW - 1) / NW;     // rows per wave
   constexpr int HS = DPW / 16;                // chunks per half (= S)
   const int lane = threadIdx.x & 63;
+  static_assert(CH == 16 || CH == 8 || CH == 4 || CH == 2, "8-dim chunks per row");
 #pragma unroll 1  // one item at a time (registers, as in split_stats)
   for (int it = lane; it < RPW * CH; it += kWave) {
     const int rl = it / CH, c = it - rl * CH;
     const int pt = w + rl * NW;
+    if (nrm) {
+      // CH == 16: the 16 chunks of row rl sit in one DPP row of the wave
+      // (uniform trip count: RPW * CH is a multiple of 64 for DPW = 128)
+      float n2 = 0.f, n1 = 0.f;
+      if (pt < BN) {
+        const float* src = xt + pt * SH::RS + c * 8;
+        const f4 u0 = *reinterpret_cast<const f4*>(src);
+        const f4 u1 = *reinterpret_cast<const f4*>(src + 4);
+        n2 = ((u0[0] * u0[0] + u0[1] * u0[1]) + (u0[2] * u0[2] + u0[3] * u0[3])) +
+             ((u1[0] * u1[0] + u1[1] * u1[1]) + (u1[2] * u1[2] + u1[3] * u1[3]));
+        n1 = ((fabsf(u0[0]) + fabsf(u0[1])) + (fabsf(u0[2]) + fabsf(u0[3]))) +
+             ((fabsf(u1[0]) + fabsf(u1[1])) + (fabsf(u1[2]) + fabsf(u1[3])));
+      }
+      n2 = row16_sum(n2);
+      n1 = row16_sum(n1);
+      if (pt < BN && c == 0) nrm[pt] = make_float2(n2 * (1.f + 1e-6f), n1 * (1.f + 1e-6f));
+    }
     if (pt < BN) {
       const float* src = xt + pt * SH::RS + c * 8;
       const f4 u0 = *reinterpret_cast<const f4*>(src);
@@ -834,6 +856,127 @@ __device__ __forceinline__ void refine_tile(f4 (&acc)[SH::NPB][2], const float* 
     }
     if constexpr (SH::COOP) __syncthreads();
     else { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); __builtin_amdgcn_wave_barrier(); }
+  }
+}
+
+// The same refinement with the selected logits of all NW waves of a
+// workgroup (WD = 1) pooled into one list: every wave then takes four
+// entries per pass, so one pass serves up to 4 * NW logits of the
+// workgroup and no wave waits on another's longer list.  Entry codes carry
+// the owning wave (w << 11 | register << 6 | lane); comp0 is the first
+// component of the workgroup (wave w owns comp0 + 32 w ...).  wtot: NW + 1
+// ints of LDS.  Same float64 arithmetic and order per logit as refine_tile,
+// so the refined values are bit-identical.
+template <class SH, int DPW>
+__device__ __forceinline__ void refine_pooled(f4 (&acc)[SH::NPB][2], const float* __restrict__ thr,
+                                              const float2* __restrict__ nrm, const float (&co)[6],
+                                              const float* __restrict__ xt, int rows, const EArgs& a, double C,
+                                              int comp0, int compbase, float* __restrict__ rlist,
+                                              unsigned short* __restrict__ elist, int* __restrict__ wtot, int cap,
+                                              int lane, int w, unsigned& nsel) {
+  constexpr int NREG = SH::NPB * 8;
+  constexpr int NW = SH::NT / kWave;
+  constexpr int DPT = DPW / 16;
+  constexpr int DCH = DPT < 4 ? DPT : 4;
+  static_assert(NW <= 32 && NREG <= 32, "entry code: 5 bits of wave, 5 of register, 6 of lane");
+  const int g = lane >> 4, r16 = lane & 15;
+  unsigned sel = 0;
+  const bool cok0 = compbase + r16 < a.K, cok1 = compbase + 16 + r16 < a.K;
+#pragma unroll
+  for (int pb = 0; pb < SH::NPB; ++pb) {
+    const f4 t4 = *reinterpret_cast<const f4*>(thr + pb * 16 + 4 * g);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int pt = pb * 16 + 4 * g + v;
+      const bool rok = pt < rows;
+      const float2 nn = nrm[pt];
+      const float L0 = acc[pb][0][v], L1 = acc[pb][1][v];
+      const float E0 = err_bound(a.kappa, co[0], co[1], co[2], nn);
+      const float E1 = err_bound(a.kappa, co[3], co[4], co[5], nn);
+      const bool b0 = rok && cok0 && (L0 != kNegInf) && (L0 + E0 >= t4[v]);
+      const bool b1 = rok && cok1 && (L1 != kNegInf) && (L1 + E1 >= t4[v]);
+      sel |= (b0 ? 1u : 0u) << (pb * 8 + v);
+      sel |= (b1 ? 1u : 0u) << (pb * 8 + 4 + v);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int c = __popc(sel);
+  int pre = 0, total = 0;
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const unsigned long long m = __ballot((c >> b) & 1);
+    pre += (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u)) << b;
+    total += __popcll(m) << b;
+  }
+  if (lane == 0) wtot[w] = total;
+  __syncthreads();
+  int base = 0, T = 0;
+#pragma unroll
+  for (int q = 0; q < NW; ++q) {
+    const int tq = wtot[q];
+    base += (q < w) ? tq : 0;
+    T += tq;
+  }
+  if (T == 0) return;  // uniform over the workgroup
+  nsel += (unsigned)total;
+  for (int b0 = 0; b0 < T; b0 += cap) {
+    const int count = min(cap, T - b0);
+    {
+      unsigned bits = sel;
+      int idx = base + pre - b0;
+      while (bits) {
+        const int r = __ffs(bits) - 1;
+        bits &= bits - 1u;
+        if (idx >= 0 && idx < cap) elist[idx] = (unsigned short)((w << 11) | (r << 6) | lane);
+        ++idx;
+      }
+    }
+    __syncthreads();
+    for (int e0 = w * 4; e0 < count; e0 += NW * 4) {
+      const int e = e0 + g;
+      const bool live = e < count;
+      const int code = live ? (int)elist[e] : 0;
+      const int wo = code >> 11, r = (code >> 6) & 31, ln = code & 63;
+      const int pt = (r >> 3) * 16 + 4 * (ln >> 4) + (r & 3);
+      const int comp = comp0 + wo * 32 + ((r >> 2) & 1) * 16 + (ln & 15);
+      const double2* wr = a.w64 + (size_t)comp * a.Dp;
+      const double cf = (live && r16 == 0) ? a.cfull[comp] : 0.0;
+      double t = 0.0;
+      if (live) {
+#pragma unroll
+        for (int j0 = 0; j0 < DPT; j0 += DCH) {
+          double2 ab[DCH];
+          float xv[DCH];
+#pragma unroll
+          for (int j = 0; j < DCH; ++j) {
+            const int d = r16 + 16 * (j0 + j);
+            ab[j] = wr[d];
+            xv[j] = xt[pt * SH::RS + d];
+          }
+#pragma unroll
+          for (int j = 0; j < DCH; ++j) {
+            const double x = (double)xv[j];
+            t = fma(ab[j].x, x * x, fma(ab[j].y, x, t));
+          }
+        }
+      }
+      t += __shfl_xor(t, 8);
+      t += __shfl_xor(t, 4);
+      t += __shfl_xor(t, 2);
+      t += __shfl_xor(t, 1);
+      if (live && r16 == 0) rlist[e] = (float)((cf - C) + t);
+    }
+    __syncthreads();
+    {
+      int idx = base + pre - b0;
+#pragma unroll
+      for (int r = 0; r < NREG; ++r)
+        if ((sel >> r) & 1u) {
+          if (idx >= 0 && idx < cap) acc[r >> 3][(r >> 2) & 1][r & 3] = rlist[idx];
+          ++idx;
+        }
+    }
+    __syncthreads();
   }
 }
 

@@ -231,6 +231,10 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   __shared__ float vtmp[BN];
   __shared__ float rlist[SH::COOP ? WC : WC * WD][kRefineCap];  // refinement lists (per group or wave)
   __shared__ unsigned short elist[SH::COOP ? WC : WC * WD][kRefineCap];
+  // the diagonal split-statistics kernel pools the refinement lists of its
+  // waves into one (rlist / elist as one array of WC * kRefineCap entries)
+  constexpr bool POOL = SPLIT == 2 && !ISO && REFINE && FUSED && WD == 1;
+  __shared__ int wtot[POOL ? WC + 1 : 1];
   __shared__ __attribute__((aligned(16))) float xn2[ISO ? BN : 4];  // ISO: ||x||^2 of the tile's rows
   __shared__ int lidx[HARD ? WC : 1][BN];                             // HARD: per-wave argmax
   __shared__ int exk[HARD ? QP : 1][BN];
@@ -347,10 +351,12 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   };
   // split operands of a freshly staged tile: each wave converts the rows its
   // own DMA brought in (register staging: after a barrier, the same rows)
+  // the diagonal split-statistics kernel forms the rows' norms there too
+  constexpr bool NORMS_IN_SPLIT = SPLIT == 2 && !ISO && REFINE && DPW == 128;
   auto split_now = [&](const float* buf) {
     if constexpr (SPLIT) {
       if (!a.dma) __syncthreads();
-      split_rows<SH, DPW, ISO>(buf, xsb, w);
+      split_rows<SH, DPW, ISO>(buf, xsb, w, NORMS_IN_SPLIT ? nrm : nullptr);
     }
   };
   int j = 0;
@@ -421,7 +427,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
       lane_coefs(a, cbo, r16, co);
     }
     if constexpr (REFINE) {
-      if constexpr (!ISO) {
+      if constexpr (!ISO && !NORMS_IN_SPLIT) {
         row_norms2<SH, DPW>(xt[cur], nrm, a.Dp);
         __syncthreads();
       }
@@ -464,7 +470,12 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
         if (tid < BN) thrs[tid] = ((tid < rows) ? a.logz[trow + tid] : kPosInf) - kDelta;
       }
       __syncthreads();
-      refine_tile<SH, WD, DPW>(acc, thrs, nrm, co, xt[cur], rows, a, C, compbase, rlist[SH::COOP ? wc : w], elist[SH::COOP ? wc : w], lane, wd, nsel);
+      if constexpr (POOL)
+        refine_pooled<SH, DPW>(acc, thrs, nrm, co, xt[cur], rows, a, C, p * 32 * WC, compbase, &rlist[0][0],
+                               &elist[0][0], wtot, WC * WD * kRefineCap, lane, w, nsel);
+      else
+        refine_tile<SH, WD, DPW>(acc, thrs, nrm, co, xt[cur], rows, a, C, compbase, rlist[SH::COOP ? wc : w],
+                                 elist[SH::COOP ? wc : w], lane, wd, nsel);
     }
 
     // ---- per-row log Z (HARD: the row's argmax)
@@ -620,7 +631,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
       if ((j + 1 + fphase) % FLUSH == 0) flush();
       __syncthreads();  // statistics operands released, next rows visible
       if (has_next) {
-        split_rows<SH, DPW, ISO>(xt[0], xsb, w);
+        split_rows<SH, DPW, ISO>(xt[0], xsb, w, NORMS_IN_SPLIT ? nrm : nullptr);
         __syncthreads();
       }
       continue;
