@@ -124,7 +124,8 @@ gmm_status gmm_create(gmm_ctx **out /*[host]*/, int32_t K, int32_t D, void *hip_
 void gmm_destroy(gmm_ctx *ctx);
 
 /* Message of the last failed call on ctx (a context-owned string), or of the
- * last failed gmm_create when ctx is NULL. */
+ * last failed context-free call (gmm_create, gmm_estep_stats_noalloc) when
+ * ctx is NULL. */
 const char *gmm_last_error(const gmm_ctx *ctx);
 
 /* Workspace bytes a context for (K, D) allocates on the current device. */
@@ -317,6 +318,32 @@ gmm_status gmm_profile_read(gmm_ctx *ctx, double *stats_ms, int64_t *stats_launc
  * logits recomputed in float64 and the number of logits the E-step sweeps
  * evaluated (N*K per sweep) since the previous call, then resets both. */
 gmm_status gmm_refine_stats(gmm_ctx *ctx, int64_t *refined, double *logits);
+
+/* Scratch of gmm_estep_stats_noalloc: 160 MiB of device memory, one array per
+ * device, held from the first call on a device until the process ends. */
+#define GMM_NOALLOC_SCRATCH_BYTES ((size_t)160 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * E-step statistics of gmm_estep_stats (same definition, same arguments
+ * from X on, same kernels and default settings: refined logits, split
+ * bfloat16 contractions, the fused path where it applies) without a
+ * context, on the given HIP stream (NULL = the null stream) of the current
+ * device.  It calls no allocating routine: its workspace lives in a
+ * fixed-size file-scope device array of GMM_NOALLOC_SCRATCH_BYTES.  With as
+ * many statistics slots as the context's workspace has (true for K=1024,
+ * D=128) the results equal gmm_estep_stats's bit for bit; shapes whose
+ * workspace is larger get fewer slots (the same statistics up to the
+ * rounding order of the partial sums), and shapes whose smallest workspace
+ * does not fit return GMM_ERR_CAPACITY.  Every call on a device shares that
+ * device's array: calls that overlap on one device (two streams, two host
+ * threads) race and must be serialised by the caller.  Errors: as
+ * gmm_estep_stats (launch errors only; device-side faults are not reported);
+ * gmm_last_error(NULL) returns the message of a failed call. */
+gmm_status gmm_estep_stats_noalloc(int32_t K, int32_t D, const float *X /*[dev]*/, int64_t N, int64_t ldx,
+                                   const float *weights, const float *means, const float *vars /*[dev]*/,
+                                   double *Nk /*[dev] K*/, double *S1 /*[dev] K*D*/, double *S2 /*[dev] K*D*/,
+                                   double *loglik /*[dev] 1*/, int32_t accumulate, void *hip_stream);
 
 #ifdef __cplusplus
 }

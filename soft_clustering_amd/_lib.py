@@ -31,7 +31,7 @@ EXPORTS = ["gmm_create", "gmm_destroy", "gmm_last_error", "gmm_workspace_bytes",
            "gmm_init", "gmm_estep_stats", "gmm_mstep", "gmm_fit", "gmm_soft_assign", "gmm_check",
            "gmm_init_iso", "gmm_estep_stats_iso", "gmm_mstep_iso", "gmm_fit_iso", "gmm_kmeans", "gmm_init_kmeans",
            "gmm_estep_stats_host", "gmm_fit_host",
-           "gmm_profile", "gmm_profile_read", "gmm_refine_stats"]
+           "gmm_profile", "gmm_profile_read", "gmm_refine_stats", "gmm_estep_stats_noalloc"]
 
 
 class GMMError(RuntimeError):
@@ -72,6 +72,7 @@ def _load():
         "gmm_refine_stats": (i32, [vp, ctypes.POINTER(i64), ctypes.POINTER(f64)]),
         "gmm_profile_read": (i32, [vp, ctypes.POINTER(f64), ctypes.POINTER(i64), ctypes.POINTER(f64),
                                    ctypes.POINTER(i64)]),
+        "gmm_estep_stats_noalloc": (i32, [i32, i32, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -434,6 +435,26 @@ class GMM:
     def check(self):
         with torch.cuda.device(self.device):
             self._check(_lib.gmm_check(self._h))
+
+
+def estep_stats_noalloc(X, w, mu, var, out, accumulate=False):
+    """gmm_estep_stats_noalloc: the E-step statistics without a context, into
+    the caller's out = (Nk, S1, S2, loglik) on torch's current stream; the
+    library allocates nothing (its workspace is a fixed device array)."""
+    K, D = mu.shape
+    N, ldx = _rows(X, D, X.device)
+    for t, dt, shape, name in ((w, torch.float32, (K,), "weights"), (mu, torch.float32, (K, D), "means"),
+                               (var, torch.float32, (K, D), "vars")):
+        _need(t, dt, shape, name, X.device)
+    Nk, S1, S2, ll = out
+    for t, shape, name in ((Nk, (K,), "Nk"), (S1, (K, D), "S1"), (S2, (K, D), "S2"), (ll, (1,), "loglik")):
+        _need(t, torch.float64, shape, name, X.device)
+    with torch.cuda.device(X.device):
+        st = _lib.gmm_estep_stats_noalloc(int(K), int(D), _ptr(X), N, ldx, _ptr(w), _ptr(mu), _ptr(var), _ptr(Nk),
+                                          _ptr(S1), _ptr(S2), _ptr(ll), int(bool(accumulate)), _stream())
+    if st != GMM_OK:
+        raise GMMError(st, _lib.gmm_last_error(None).decode())
+    return out
 
 
 def raw_library():

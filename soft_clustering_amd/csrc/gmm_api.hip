@@ -820,3 +820,116 @@ gmm_status gmm_check(gmm_ctx* ctx) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Entry point that allocates nothing (gmm_estep_stats_noalloc).  Its
+// workspace is carved from `scratch`, a file-scope device array of
+// GMM_NOALLOC_SCRATCH_BYTES that each device holds from the first call on
+// it until the process ends.  In host code the array's name is only a
+// host-side stand-in, so the device address is taken once per device with
+// hipGetSymbolAddress and only that address is used afterwards.
+static __device__ __align__(256) unsigned char scratch[GMM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices] = {};
+
+// Workspace of the E-step alone (precomputed operands, statistics slots,
+// exchange words, flags), carved in order from base; returns the bytes used.
+size_t carve_estep(const gmm::Plan& p, char* base, gmm::Workspace& ws) {
+  char* q = base;
+  ws = gmm::Workspace{};
+  ws.wop = carve<float>(q, (size_t)p.Kpad * 2 * p.Dp);
+  ws.cvec = carve<float>(q, p.Kpad);
+  ws.cfull = carve<double>(q, p.Kpad);
+  ws.cpeak = carve<double>(q, p.Kpad);
+  ws.cshift = carve<double>(q, 1);
+  ws.w64 = carve<double2>(q, (size_t)p.Kpad * p.Dp);
+  ws.abmax = carve<float2>(q, p.Kpad);
+  ws.wsplit = carve<__bf16>(q, (size_t)p.Kpad * 2 * p.Dp * 2);
+  ws.cvec64 = carve<double>(q, p.Kpad);  // written by the shift kernel whatever the precision
+  // flags (4 ints) and the refined-logit counter share one cleared block
+  ws.flags = carve<int>(q, 16);
+  ws.nrefined = reinterpret_cast<unsigned long long*>(ws.flags + 8);
+  ws.llslots = carve<double>(q, p.R > p.Glogz ? p.R : p.Glogz);
+  ws.logz = carve<float>(q, (size_t)p.chunk);
+  ws.xbuf = carve<unsigned long long>(q, (size_t)p.R * 4 * p.P * p.BN);
+  ws.slots = carve<double>(q, (size_t)p.R * p.Kpad * p.SR);
+  ws.refine = 1;
+  ws.f64 = 0;
+  ws.split = 2;
+  return (size_t)(q - base);
+}
+
+}  // namespace
+
+extern "C" gmm_status gmm_estep_stats_noalloc(int32_t K, int32_t D, const float* X, int64_t N, int64_t ldx,
+                                              const float* weights, const float* means, const float* vars,
+                                              double* Nk, double* S1, double* S2, double* loglik,
+                                              int32_t accumulate, void* hip_stream) {
+  g_create_err.clear();
+  if (K < 1 || K > 65536) return fail(nullptr, GMM_ERR_INVALID_ARG, "K must be in [1, 65536] (got %d)", K);
+  if (D < 1 || D > 1024) return fail(nullptr, GMM_ERR_INVALID_ARG, "D must be in [1, 1024] (got %d)", D);
+  if (!X || !aligned16(X)) return fail(nullptr, GMM_ERR_INVALID_ARG, "X must be non-NULL and 16-byte aligned");
+  if (N < 1 || N > ((int64_t)1 << 40)) return fail(nullptr, GMM_ERR_INVALID_ARG, "N out of range (got %lld)", (long long)N);
+  if (ldx < D || (ldx & 3))
+    return fail(nullptr, GMM_ERR_INVALID_ARG, "ldx must be >= D and a multiple of 4 (got %lld)", (long long)ldx);
+  if (!weights || !means || !vars || !aligned16(weights) || !aligned16(means) || !aligned16(vars))
+    return fail(nullptr, GMM_ERR_INVALID_ARG, "weights/means/vars must be non-NULL and 16-byte aligned");
+  if (!Nk || !S1 || !S2 || !loglik) return fail(nullptr, GMM_ERR_INVALID_ARG, "statistics outputs must be non-NULL");
+  if (accumulate != 0 && accumulate != 1) return fail(nullptr, GMM_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(nullptr, GMM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(nullptr, GMM_ERR_UNSUPPORTED, "device index %d", dev);
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(nullptr, GMM_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(nullptr, GMM_ERR_UNSUPPORTED, "built for gfx950, device is %s", prop.gcnArchName);
+  if (!g_scratch[dev]) {  // once per device, with that device current
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(nullptr, GMM_ERR_HIP, "scratch address: %s", hipGetErrorString(e));
+    g_scratch[dev] = ptr;
+  }
+  gmm::Plan p0 = gmm::make_plan(K, D, prop.multiProcessorCount, 1, 1);
+  if (!gmm::plan_shape_ok(p0)) return fail(nullptr, GMM_ERR_UNSUPPORTED, "no kernel for K=%d D=%d", K, D);
+  int o1 = 1, o2 = 1;
+  e = gmm::occupancy(p0, &o1, &o2);
+  if (e != hipSuccess) return fail(nullptr, GMM_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
+  gmm::Plan p = gmm::make_plan(K, D, prop.multiProcessorCount, o1, o2);
+  p.chunk = (int64_t)1 << 18;  // two-sweep log Z chunk
+  // as many row groups (statistics slots) as the scratch holds, up to the plan's
+  char* base = (char*)g_scratch[dev];
+  gmm::Workspace ws;
+  const int Rmax = p.R;
+  for (; p.R >= 1; --p.R) {
+    p.G = p.R * p.P;
+    if (carve_estep(p, base, ws) <= (size_t)GMM_NOALLOC_SCRATCH_BYTES) break;
+  }
+  if (p.R < 1) {
+    p.R = 1;
+    p.G = p.P;
+    return fail(nullptr, GMM_ERR_CAPACITY, "K=%d D=%d needs %zu bytes of scratch, the maximum is %zu", K, D,
+                carve_estep(p, base, ws), (size_t)GMM_NOALLOC_SCRATCH_BYTES);
+  }
+  (void)Rmax;
+  if (!ws.wop || !ws.cvec || !ws.cfull || !ws.cpeak || !ws.cshift || !ws.w64 || !ws.abmax || !ws.wsplit ||
+      !ws.cvec64 || !ws.flags || !ws.llslots || !ws.logz || !ws.xbuf || !ws.slots)
+    return fail(nullptr, GMM_ERR_HIP, "scratch workspace incomplete");
+  hipStream_t s = (hipStream_t)hip_stream;
+  // the array keeps the last call's contents: flags and counter start at zero
+  e = gmm::launch_fill_zero(reinterpret_cast<double*>(ws.flags), 8, s);
+  if (e == hipSuccess) e = gmm::launch_precompute(p, ws, weights, means, vars, s);
+  if (e != hipSuccess) return fail(nullptr, GMM_ERR_HIP, "precompute launch: %s", hipGetErrorString(e));
+  const bool fused = p.fusedOK != 0 && p.P <= 64;
+  int nslots = 0;
+  e = gmm::launch_estep(p, ws, X, N, ldx, fused, s, nullptr, &nslots, 0);
+  if (e != hipSuccess) return fail(nullptr, GMM_ERR_HIP, "E-step launch: %s", hipGetErrorString(e));
+  e = gmm::launch_reduce(p, ws, Nk, S1, S2, loglik, accumulate, nslots, fused ? nslots : p.Glogz, N, s);
+  if (e != hipSuccess) return fail(nullptr, GMM_ERR_HIP, "reduce launch: %s", hipGetErrorString(e));
+  return GMM_OK;
+}

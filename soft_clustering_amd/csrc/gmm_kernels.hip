@@ -992,7 +992,7 @@ __global__ void k_precompute_shift(const double* __restrict__ cfull, const doubl
   if (!isfinite(C)) C = 0.0;
   for (int k = threadIdx.x; k < Kpad; k += blockDim.x) {
     cvec[k] = (float)(cfull[k] - C);
-    cvec64[k] = cfull[k] - C;
+    if (cvec64) cvec64[k] = cfull[k] - C;  // only the float64-logit mode reads it
   }
   if (threadIdx.x == 0) *cshift = C;
 }
