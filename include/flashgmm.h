@@ -116,7 +116,10 @@ typedef enum {
  * gmm_workspace_bytes).  The only later allocations are those of the
  * out-of-core calls (gmm_estep_stats_host, gmm_fit_host): a copy stream and
  * two device staging buffers, made on their first use and grown when a call
- * asks for larger chunks; every other entry point allocates nothing.
+ * asks for larger chunks; and of gmm_soft_assign over more than 2^19 rows:
+ * one buffer of N * (1 + max_extra) int32 (kept when it is at most 4 GiB,
+ * grown on demand).  Every other entry point allocates nothing; all of it
+ * is freed by gmm_destroy.
  * 1 <= K <= 65536, 1 <= D <= 1024. */
 gmm_status gmm_create(gmm_ctx **out /*[host]*/, int32_t K, int32_t D, void *hip_stream);
 
@@ -291,7 +294,11 @@ gmm_status gmm_init_kmeans(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, in
  * threshold) nats of a row's largest are evaluated in float64 (under
  * GMM_PREC_REFINED), so ranks and the threshold test are float64-accurate.
  * The result is deterministic.  0 < threshold <= 1, 0 <= max_extra <= 8,
- * N < 2^31.  Synchronises the stream. */
+ * N < 2^31.  Rows are processed in chunks of 2^19: a counting sweep, then
+ * the scatter into the lists; the selections of the first sweep are kept for
+ * the second in a context buffer of N * (1 + max_extra) int32 when that is at
+ * most 4 GiB and can be allocated, otherwise the rows are selected again.
+ * Synchronises the stream. */
 gmm_status gmm_soft_assign(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_t ldx,
                            const float *weights, const float *means, const float *vars /*[dev]*/,
                            float threshold, int32_t max_extra,

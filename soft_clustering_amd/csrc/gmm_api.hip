@@ -14,6 +14,9 @@
 #include "flashgmm.h"
 #include "gmm_internal.h"
 
+// largest buffer the soft assignment holds for the selections of all rows
+constexpr size_t kSelKeepBytes = (size_t)4 << 30;
+
 struct gmm_ctx {
   int device = 0;
   hipStream_t stream = nullptr;
@@ -36,6 +39,11 @@ struct gmm_ctx {
   int64_t stage_rows = 0;
   hipEvent_t ev_copied[2] = {nullptr, nullptr};
   hipEvent_t ev_used[2] = {nullptr, nullptr};
+  // soft assignment over several chunks: every row's selections, kept from
+  // the counting sweep for the scatter (grown on demand, at most
+  // kSelKeepBytes)
+  int32_t* selkeep = nullptr;
+  size_t selkeep_bytes = 0;
 };
 
 namespace {
@@ -247,6 +255,7 @@ gmm_status gmm_create(gmm_ctx** out, int32_t K, int32_t D, void* hip_stream) {
   c->ws.flags = carve<int>(q, 4);
   c->ws.colG = 1024;
   c->ws.asel = carve<int32_t>(q, (size_t)p.assignChunk * 9);
+  c->ws.agco = carve<float4>(q, (size_t)p.Kpad / 32);
   c->ws.acounts = carve<unsigned long long>(q, p.Kpad);
   c->ws.acnt = carve<unsigned>(q, (size_t)p.assignBlocks * p.Kpad);
   c->ws.atot = carve<unsigned>(q, p.Kpad);
@@ -286,6 +295,7 @@ void gmm_destroy(gmm_ctx* ctx) {
     if (ctx->ev_used[b]) hipEventDestroy(ctx->ev_used[b]);
   }
   if (ctx->copy_stream) hipStreamDestroy(ctx->copy_stream);
+  if (ctx->selkeep) hipFree(ctx->selkeep);
   delete ctx;
 }
 
@@ -556,11 +566,37 @@ gmm_status soft_assign_run(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx,
   if (e == hipSuccess) e = gmm::launch_assign_begin(p, ctx->ws, s);
   if (e != hipSuccess) return hip_fail(ctx, e, "soft assignment set-up");
   const int64_t CH = p.assignChunk;
-  const bool one = N <= CH;
+  // Where the input spans several chunks, the selections of all rows are
+  // kept from the counting sweep (N x (1 + max_extra) ints, up to
+  // kSelKeepBytes) so that the scatter needs no second logit sweep; if that
+  // buffer cannot be had, every chunk is selected again before its scatter.
+  const size_t keep_bytes = (size_t)N * (size_t)(1 + max_extra) * sizeof(int32_t);
+  bool keep = N <= CH;
+  if (!keep && keep_bytes <= kSelKeepBytes) {
+    if (ctx->selkeep_bytes < keep_bytes) {
+      e = hipStreamSynchronize(s);  // the old buffer may still be read
+      if (e != hipSuccess) return hip_fail(ctx, e, "soft assignment set-up");
+      if (ctx->selkeep) hipFree(ctx->selkeep);
+      ctx->selkeep = nullptr;
+      ctx->selkeep_bytes = 0;
+      void* q = nullptr;
+      if (hipMalloc(&q, keep_bytes) == hipSuccess) {
+        ctx->selkeep = static_cast<int32_t*>(q);
+        ctx->selkeep_bytes = keep_bytes;
+      } else {
+        (void)hipGetLastError();  // not fatal: fall back to selecting twice
+      }
+    }
+    keep = ctx->selkeep != nullptr && ctx->selkeep_bytes >= keep_bytes;
+  }
+  const int stride = 1 + max_extra;
+  auto chunk_sel = [&](int64_t r0) -> int32_t* {
+    return (N <= CH || !keep) ? ctx->ws.asel : ctx->selkeep + r0 * stride;
+  };
   // pass A: select every row and count list sizes
   for (int64_t r0 = 0; r0 < N; r0 += CH) {
     const int64_t rows = (N - r0 < CH) ? N - r0 : CH;
-    e = gmm::launch_assign_select(p, ctx->ws, X, r0, rows, ldx, threshold, max_extra, true, s);
+    e = gmm::launch_assign_select(p, ctx->ws, X, r0, rows, ldx, threshold, max_extra, true, chunk_sel(r0), s);
     if (e != hipSuccess) return hip_fail(ctx, e, "assignment selection");
   }
   e = gmm::launch_assign_offsets(p, ctx->ws, list_offsets, s);
@@ -576,11 +612,11 @@ gmm_status soft_assign_run(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx,
   // pass B: place rows into the lists in row order
   for (int64_t r0 = 0; r0 < N; r0 += CH) {
     const int64_t rows = (N - r0 < CH) ? N - r0 : CH;
-    if (!one) {
-      e = gmm::launch_assign_select(p, ctx->ws, X, r0, rows, ldx, threshold, max_extra, false, s);
+    if (!keep) {
+      e = gmm::launch_assign_select(p, ctx->ws, X, r0, rows, ldx, threshold, max_extra, false, chunk_sel(r0), s);
       if (e != hipSuccess) return hip_fail(ctx, e, "assignment selection");
     }
-    e = gmm::launch_assign_scatter(p, ctx->ws, r0, rows, max_extra, list_offsets, list_ids, s);
+    e = gmm::launch_assign_scatter(p, ctx->ws, chunk_sel(r0), r0, rows, max_extra, list_offsets, list_ids, s);
     if (e != hipSuccess) return hip_fail(ctx, e, "list scatter");
   }
   e = hipStreamSynchronize(s);

@@ -42,6 +42,7 @@ struct AArgs {
   float delta;                   // float64 window below the row's largest logit
   float cand_off;                // candidate bound offset: min(log(threshold), 0) with extras, 0 without
   int m;                         // max_extra
+  const float4* gco;             // Kpad / 32 per-group error-bound coefficients (k_assign_ct)
 };
 
 constexpr float kLag = 20.f;     // lag of the log-sum-exp reference (e^20 * K stays finite)
@@ -70,14 +71,13 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// SPLIT: split-bfloat16 first-pass logits (refined mode, WD = 1); the tile's
-// split operands are built once and serve every component group.
-template <int WC, int WD, int DPW, int BN, int MODE, bool SPLIT = false>
+// Row-major accumulators (lane (g, r16), register v: row 4 g + v of a
+// 16-row block, component r16 of a 16-component block) with float32 or
+// float64 MFMA logits; the split-bf16 variant is k_assign_ct below.
+template <int WC, int WD, int DPW, int BN, int MODE>
 __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
   using SH = Shape<WC, WD, DPW, BN>;
   constexpr bool REFINE = MODE == MODE_REFINE, F64 = MODE == MODE_FP64;
-  static_assert(!SPLIT || (REFINE && WD == 1), "split-bf16 logits: refined mode, WD = 1");
-  using SPR = SplitRow<DPW, false>;
   constexpr int NPB = SH::NPB;
   constexpr int TLW = 16 * (BN + 1);        // one wave's transposed 16-component block
   constexpr int LSTW = 2 * kTopN * BN;      // one wave's lists (values, indices)
@@ -91,7 +91,6 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
   __shared__ __attribute__((aligned(16))) float thrw[WC][BN];
   __shared__ float rlist[SH::COOP ? WC : WC * WD][kRefineCap];  // refinement lists (per group or wave)
   __shared__ unsigned short elist[SH::COOP ? WC : WC * WD][kRefineCap];
-  __shared__ __attribute__((aligned(16))) __bf16 xsb[SPLIT ? BN * SPR::XSR : 8];  // split operands
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wc = w % WC, wd = w / WC;
@@ -114,7 +113,6 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
       stg.store(xt);
     }
     __syncthreads();
-    if constexpr (SPLIT) split_rows<SH, DPW, false>(xt, xsb, w);  // published by the barrier below
     if constexpr (REFINE) {
       row_norms2<SH, DPW>(xt, nrm, a.Dp);
       __syncthreads();
@@ -152,14 +150,9 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
           acc[pb][0] = f4{c0, c0, c0, c0};
           acc[pb][1] = f4{c1, c1, c1, c1};
         }
-        if constexpr (SPLIT) {
-          logit_tile_split<SH, DPW, false>(xsb, a.wsp + (size_t)(compbase >> 4) * SPR::WBLK,
-                                           a.wsp + (size_t)((compbase >> 4) + 1) * SPR::WBLK, acc, lane);
-        } else {
-          logit_tile<SH, DPW>(xt, wop_block(a.wop, compbase >> 4, WD, wd, DPW),
-                              wop_block(a.wop, (compbase >> 4) + 1, WD, wd, DPW), acc, lane, wd);
-          reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
-        }
+        logit_tile<SH, DPW>(xt, wop_block(a.wop, compbase >> 4, WD, wd, DPW),
+                            wop_block(a.wop, (compbase >> 4) + 1, WD, wd, DPW), acc, lane, wd);
+        reduce_partial_logits<SH, WC, WD>(red, acc, lane, wc, wd);
       }
       if constexpr (REFINE) {
         // running maximum of guaranteed lower bounds L - E of the row's
@@ -320,6 +313,393 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
 }
 
 // ---------------------------------------------------------------------------
+// Component-major soft assignment: split-bf16 first-pass logits, float64
+// refinement, one dim segment per wave.  The logit MFMA takes W as its A
+// operand, so lane (g, r16) holds, for 16-row block pb, the logits of row
+// pb * 16 + r16 against components 4 g .. 4 g + 3 of both 16-component
+// blocks of the group: a row's 32 logits sit in the four lanes r16 + 16 g',
+// eight per lane.  A row's per-group maximum is then an in-lane maximum and
+// two cross-lane steps (lanes 32 and 16 apart), and its log-sum-exp,
+// running bound and thresholds are per-lane registers.  The fp32 error
+// bound uses the group's coefficient maxima (gco), at least every
+// component's own bound, so every logit the per-component test would refine
+// is refined.
+
+// max / sum of v over lanes l and l ^ 32 (permlane32 swap: the two halves of
+// the wave trade places), and over lanes l and l ^ 16 (permlane16 swap).
+__device__ __forceinline__ float xmax32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xmax16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xsum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xsum16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float max8(const f4& p, const f4& q) {
+  return fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])), fmaxf(fmaxf(q[0], q[1]), fmaxf(q[2], q[3])));
+}
+
+// Float64 recomputation of the logits L >= tq[pb] of one wave's group
+// (component-major registers: bit pb * 8 + cb * 4 + v of a lane is row
+// pb * 16 + r16, component compbase + cb * 16 + 4 g + v).  Lane-major list,
+// 16 lanes per logit, four logits per pass, the same float64 arithmetic and
+// order per logit as the row-major refine_tile.
+template <class SH, int DPW>
+__device__ __forceinline__ void refine_ct(f4 (&acc)[SH::NPB][2], const float (&tq)[SH::NPB],
+                                          const float* __restrict__ xt, const EArgs& a, double C, int compbase,
+                                          float* __restrict__ rlist, unsigned short* __restrict__ elist, int lane,
+                                          unsigned& nsel) {
+  constexpr int NREG = SH::NPB * 8;
+  constexpr int DPT = DPW / 16;            // dims per lane (16 lanes per logit)
+  constexpr int DCH = DPT < 4 ? DPT : 4;   // dims with loads in flight together
+  const int g = lane >> 4, r16 = lane & 15;
+  unsigned sel = 0;
+#pragma unroll
+  for (int pb = 0; pb < SH::NPB; ++pb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float L = acc[pb][cb][v];
+        const bool b = (L >= tq[pb]) && (L != kNegInf) && (compbase + cb * 16 + 4 * g + v < a.K);
+        sel |= (b ? 1u : 0u) << (pb * 8 + cb * 4 + v);
+      }
+  const int c = __popc(sel);
+  int pre = 0, total = 0;
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const unsigned long long m = __ballot((c >> b) & 1);
+    pre += (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u)) << b;
+    total += __popcll(m) << b;
+  }
+  if (total == 0) return;  // uniform over the wave
+  nsel += (unsigned)total;
+  for (int b0 = 0; b0 < total; b0 += kRefineCap) {
+    const int count = min(kRefineCap, total - b0);
+    {
+      unsigned bits = sel;
+      int idx = pre - b0;
+      while (bits) {
+        const int r = __ffs(bits) - 1;
+        bits &= bits - 1u;
+        if (idx >= 0 && idx < kRefineCap) elist[idx] = (unsigned short)((r << 6) | lane);
+        ++idx;
+      }
+    }
+    wave_sync();
+    for (int base = 0; base < count; base += 4) {
+      const int e = base + g;
+      const bool live = e < count;
+      const int code = live ? (int)elist[e] : 0;
+      const int r = code >> 6, ln = code & 63;
+      const int pt = (r >> 3) * 16 + (ln & 15);
+      const int comp = compbase + ((r >> 2) & 1) * 16 + 4 * (ln >> 4) + (r & 3);
+      const double2* wr = a.w64 + (size_t)comp * a.Dp;
+      const double cf = (live && r16 == 0) ? a.cfull[comp] : 0.0;
+      double t = 0.0;
+      if (live) {
+#pragma unroll
+        for (int j0 = 0; j0 < DPT; j0 += DCH) {
+          double2 ab[DCH];
+          float xv[DCH];
+#pragma unroll
+          for (int j = 0; j < DCH; ++j) {
+            const int d = r16 + 16 * (j0 + j);  // < Dp: padded dims have a = b = 0
+            ab[j] = wr[d];
+            xv[j] = xt[pt * SH::RS + d];
+          }
+#pragma unroll
+          for (int j = 0; j < DCH; ++j) {
+            const double x = (double)xv[j];
+            t = fma(ab[j].x, x * x, fma(ab[j].y, x, t));
+          }
+        }
+      }
+      t += __shfl_xor(t, 8);
+      t += __shfl_xor(t, 4);
+      t += __shfl_xor(t, 2);
+      t += __shfl_xor(t, 1);
+      if (live && r16 == 0) rlist[e] = (float)((cf - C) + t);
+    }
+    wave_sync();
+    {
+      int idx = pre - b0;
+#pragma unroll
+      for (int r = 0; r < NREG; ++r)
+        if ((sel >> r) & 1u) {
+          if (idx >= 0 && idx < kRefineCap) acc[r >> 3][(r >> 2) & 1][r & 3] = rlist[idx];
+          ++idx;
+        }
+    }
+    wave_sync();
+  }
+}
+
+template <int WC, int DPW, int BN>
+__global__ void __launch_bounds__(kWave* WC) k_assign_ct(EArgs a, AArgs s) {
+  using SH = Shape<WC, 1, DPW, BN>;
+  using SPR = SplitRow<DPW, false>;
+  constexpr int NPB = SH::NPB;
+  constexpr bool NIS = DPW == 128;       // row norms formed while splitting the rows
+  constexpr int LSTW = 2 * kTopN * BN;   // one wave's lists (values, indices)
+  constexpr int CAPC = LSTW / 2;         // candidates per compaction batch
+  __shared__ __attribute__((aligned(16))) float xt[SH::TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 xsb[BN * SPR::XSR];
+  __shared__ float tbuf[WC][LSTW];
+  __shared__ float lpart[WC][BN];
+  __shared__ float2 nrm[BN];
+  __shared__ float rlist[WC][kRefineCap];
+  __shared__ unsigned short elist[WC][kRefineCap];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int ncg = a.Kpad / 32;
+  const double C = *a.cshift;
+  const int nt = (int)((a.nrows + BN - 1) / BN);
+  const int stride = 1 + s.m;
+  unsigned nsel = 0;  // refined logits of this wave (counted once at the end)
+  float* tl = tbuf[w];
+
+  for (int t = blockIdx.x; t < nt; t += gridDim.x) {
+    const int64_t trow = (int64_t)t * BN;
+    const int rows = (int)min((int64_t)BN, a.nrows - trow);
+    if (a.dma) {
+      stage_dma<SH>(xt, a.X, a.ldx, a.row0 + trow, rows);
+      dma_wait();
+    } else {
+      Stage<SH, DPW> stg;
+      stg.load(a.X, a.ldx, a.row0 + trow, rows, a.D);
+      stg.store(xt);
+    }
+    __syncthreads();
+    split_rows<SH, DPW, false>(xt, xsb, w, NIS ? nrm : nullptr);
+    if constexpr (!NIS) row_norms2<SH, DPW>(xt, nrm, a.Dp);
+    __syncthreads();
+    float2 nn[NPB];
+    bool rok[NPB];
+    float M[NPB], S[NPB], Rlb[NPB];
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb) {
+      nn[pb] = nrm[pb * 16 + r16];
+      rok[pb] = pb * 16 + r16 < rows;
+      M[pb] = kNegInf;
+      S[pb] = 0.f;
+      Rlb[pb] = kNegInf;
+    }
+    float tv[kTopN];
+    int tk[kTopN];
+#pragma unroll
+    for (int i = 0; i < kTopN; ++i) {
+      tv[i] = kNegInf;
+      tk[i] = INT_MAX;
+    }
+    for (int cg = w; cg < ncg; cg += WC) {
+      const int compbase = cg * 32;
+      f4 acc[NPB][2];
+      {
+        const f4 c0 = *reinterpret_cast<const f4*>(a.cvec + compbase + 4 * g);
+        const f4 c1 = *reinterpret_cast<const f4*>(a.cvec + compbase + 16 + 4 * g);
+#pragma unroll
+        for (int pb = 0; pb < NPB; ++pb) {
+          acc[pb][0] = c0;
+          acc[pb][1] = c1;
+        }
+      }
+      logit_tile_split<SH, DPW, false, true>(xsb, a.wsp + (size_t)(compbase >> 4) * SPR::WBLK,
+                                             a.wsp + (size_t)((compbase >> 4) + 1) * SPR::WBLK, acc, lane);
+      // 1. running lower bound Rlb of the row's largest logit (the largest
+      //    L - E seen so far) and the refinement test: L + E_k >= Rlb - delta
+      //    implies L >= tq, since E_k <= Eg (the margin covers the roundings
+      //    of both forms)
+      const float4 gc = s.gco[cg];
+      float tq[NPB];
+      unsigned long long anyr = 0;
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) {
+        const float Eg = a.kappa * (gc.x * nn[pb].x + gc.y * nn[pb].y + gc.z);
+        const float lb = xmax16(xmax32(max8(acc[pb][0], acc[pb][1]) - Eg));
+        Rlb[pb] = fmaxf(Rlb[pb], lb);
+        const float thr = Rlb[pb] - s.delta;
+        tq[pb] = rok[pb] ? (thr - Eg) - (fabsf(thr) + Eg) * 0x1p-21f : kPosInf;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) anyr |= __ballot(acc[pb][cb][v] >= tq[pb]);
+      }
+      if (anyr) refine_ct<SH, DPW>(acc, tq, xt, a, C, compbase, rlist[w], elist[w], lane, nsel);
+      // 2. online log-sum-exp with a lagging reference: M moves only when a
+      //    logit exceeds it by more than kLag nats
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) {
+        const float mn = max8(acc[pb][0], acc[pb][1]);
+        if (mn > M[pb] + kLag) {
+          S[pb] = (M[pb] == kNegInf) ? 0.f : S[pb] * __expf(M[pb] - mn);
+          M[pb] = mn;
+        }
+        const float ms = (M[pb] == kNegInf) ? 0.f : M[pb];
+        float sm = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sm += __expf(acc[pb][cb][v] - ms);
+        S[pb] += sm;
+      }
+      // 3. top-list candidates: only a logit at or above the row's bound can
+      //    be selected (the argmax is at least Rlb, less one float32 rounding
+      //    of a refined value, and an extra needs l - log Z >= log(threshold)
+      //    with log Z at least that); they are compacted into a lane-major
+      //    list and lane p inserts the entries of row p
+      float bnd[NPB];
+      unsigned long long anyc = 0;
+#pragma unroll
+      for (int pb = 0; pb < NPB; ++pb) {
+        const float rb = Rlb[pb];
+        bnd[pb] = rok[pb] ? rb + s.cand_off - (fabsf(rb) * 2.4e-7f + 1e-6f) : kPosInf;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) anyc |= __ballot(acc[pb][cb][v] >= bnd[pb]);
+      }
+      if (anyc) {
+        unsigned cbits = 0;
+#pragma unroll
+        for (int pb = 0; pb < NPB; ++pb)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) cbits |= (acc[pb][cb][v] >= bnd[pb] ? 1u : 0u) << (pb * 8 + cb * 4 + v);
+        const int c = __popc(cbits);
+        int pre = 0, total = 0;
+#pragma unroll
+        for (int b = 0; b < 6; ++b) {
+          const unsigned long long m = __ballot((c >> b) & 1);
+          pre += (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u)) << b;
+          total += __popcll(m) << b;
+        }
+        // tl[0, CAPC): candidate values; tl[CAPC, 2 CAPC): their codes
+        // (register << 6 | lane) as float bit patterns
+        for (int b0 = 0; b0 < total; b0 += CAPC) {
+          const int n = min(CAPC, total - b0);
+          {
+            int idx = pre - b0;
+#pragma unroll
+            for (int r = 0; r < NPB * 8; ++r)
+              if ((cbits >> r) & 1u) {
+                if (idx >= 0 && idx < CAPC) {
+                  tl[idx] = acc[r >> 3][(r >> 2) & 1][r & 3];
+                  tl[CAPC + idx] = __int_as_float((r << 6) | lane);
+                }
+                ++idx;
+              }
+          }
+          wave_sync();
+          if (lane < BN) {
+#pragma unroll 1
+            for (int e = 0; e < n; ++e) {
+              const int code = __float_as_int(tl[CAPC + e]);
+              const float cvv = tl[e];
+              const int r = code >> 6, ln = code & 63;
+              if ((r >> 3) * 16 + (ln & 15) == lane)
+                top_insert(tv, tk, cvv, compbase + ((r >> 2) & 1) * 16 + 4 * (ln >> 4) + (r & 3));
+            }
+          }
+          wave_sync();
+        }
+      }
+    }
+    // merge the four lanes of each row, then the WC waves
+#pragma unroll
+    for (int pb = 0; pb < NPB; ++pb) {
+      const float mr = xmax16(xmax32(M[pb]));
+      const float ms = (mr == kNegInf) ? 0.f : mr;
+      const float sm = xsum16(xsum32(S[pb] * __expf(M[pb] - ms)));
+      if (g == 0) lpart[w][pb * 16 + r16] = (sm > 0.f) ? ms + __logf(sm) : kNegInf;
+    }
+    if (w > 0 && lane < BN) {
+#pragma unroll
+      for (int i = 0; i < kTopN; ++i) {
+        tl[i * BN + lane] = tv[i];
+        tl[(kTopN + i) * BN + lane] = __int_as_float(tk[i]);
+      }
+    }
+    __syncthreads();
+    if (tid < BN) {  // wave 0: lane = row
+#pragma unroll 1
+      for (int q = 1; q < WC; ++q) {
+        const float* o = tbuf[q];
+#pragma unroll 1
+        for (int i = 0; i < kTopN; ++i) {
+          const float v = o[i * BN + tid];
+          if (v == kNegInf) break;
+          top_insert(tv, tk, v, __float_as_int(o[(kTopN + i) * BN + tid]));
+        }
+      }
+      if (tid < rows) {
+        float Mx = kNegInf, Sx = 0.f;
+#pragma unroll
+        for (int k = 0; k < WC; ++k) lse_merge(Mx, Sx, lpart[k][tid], 1.f);
+        const float lz = lse_of(Mx, Sx);
+        int32_t* out = s.sel + (trow + tid) * stride;
+        const bool ok = (tv[0] != kNegInf) && (tv[0] == tv[0]) && (lz == lz) && (lz != kNegInf);
+        if (!ok) {
+          __hip_atomic_store(&a.flags[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int j = 0; j < stride; ++j) out[j] = -1;
+        } else {
+          out[0] = tk[0];
+          if (s.counts) atomicAdd(&s.counts[tk[0]], 1ull);
+          int n = 1;
+#pragma unroll
+          for (int i = 1; i < kTopN; ++i) {
+            if (i <= s.m && tv[i] != kNegInf && tv[i] - lz >= s.log_thr) {
+              out[n++] = tk[i];
+              if (s.counts) atomicAdd(&s.counts[tk[i]], 1ull);
+            }
+          }
+          for (; n < stride; ++n) out[n] = -1;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  count_refined(a, nsel);
+}
+
+// Per-group error-bound coefficients of k_assign_ct: for each 32-component
+// group, the maxima over its components of max|a|, max|b| and |c - C|
+// (padding contributes 0).  One wave per group.
+__global__ void k_group_coefs(const float2* __restrict__ abmax, const float* __restrict__ cvec,
+                              float4* __restrict__ gco, int ngroups) {
+  const int grp = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int lane = threadIdx.x & 63;
+  if (grp >= ngroups) return;
+  float ma = 0.f, mb = 0.f, mc = 0.f;
+  if (lane < 32) {
+    const int k = grp * 32 + lane;
+    const float2 ab = abmax[k];
+    const float c = cvec[k];
+    ma = ab.x;
+    mb = ab.y;
+    mc = (c == kNegInf) ? 0.f : fabsf(c);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    ma = fmaxf(ma, __shfl_xor(ma, o));
+    mb = fmaxf(mb, __shfl_xor(mb, o));
+    mc = fmaxf(mc, __shfl_xor(mc, o));
+  }
+  if (lane == 0) gco[grp] = make_float4(ma, mb, mc, 0.f);
+}
+
+// ---------------------------------------------------------------------------
 // Inverted-list construction.
 
 // offsets[0..K] = exclusive scan of counts; cursor = offsets[0..K-1];
@@ -438,7 +818,7 @@ struct AKern {
   template <int M>
   static void* assign() { return (void*)&k_assign<WC, WD, DPW, BN, M>; }
   static void* assign_split() {
-    if constexpr (WD == 1) return (void*)&k_assign<WC, WD, DPW, BN, MODE_REFINE, true>;
+    if constexpr (WD == 1) return (void*)&k_assign_ct<WC, DPW, BN>;
     else return nullptr;
   }
 };
@@ -489,7 +869,8 @@ hipError_t assign_occupancy(const Plan& p, int* occ) {
 }
 
 hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* X, int64_t row0, int64_t rows,
-                                int64_t ldx, float threshold, int max_extra, bool count, hipStream_t s) {
+                                int64_t ldx, float threshold, int max_extra, bool count, int32_t* sel,
+                                hipStream_t s) {
   void* t[4];
   const int wc = assign_wc(p);
   if (!alookup(wc, p.WD, p.DPW, t)) return hipErrorInvalidValue;
@@ -518,13 +899,14 @@ hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* 
   a.wop64 = w.wop64;
   a.cvec64 = w.cvec64;
   AArgs sa{};
-  sa.sel = w.asel;
+  sa.sel = sel;
   sa.counts = count ? w.acounts : nullptr;
   const double lt = log((double)threshold);
   sa.log_thr = (float)lt;
   sa.delta = (float)(1.0 - lt > 16.0 ? 1.0 - lt : 16.0);
   sa.cand_off = max_extra > 0 ? (float)(lt < 0.0 ? lt : 0.0) : 0.f;
   sa.m = max_extra;
+  sa.gco = w.agco;
   void* args[] = {&a, &sa};
   const int64_t tiles = (rows + p.BN - 1) / p.BN;
   const int64_t gmax = (int64_t)p.numCU * (p.occAssign > 0 ? p.occAssign : 1);
@@ -541,6 +923,8 @@ hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* 
 
 hipError_t launch_assign_begin(const Plan& p, const Workspace& w, hipStream_t s) {
   hipLaunchKernelGGL(k_fill_u64a, dim3((p.Kpad + 255) / 256), dim3(256), 0, s, w.acounts, (size_t)p.Kpad);
+  const int ng = p.Kpad / 32;
+  hipLaunchKernelGGL(k_group_coefs, dim3((ng + 3) / 4), dim3(256), 0, s, w.abmax, w.cvec, w.agco, ng);
   return hipGetLastError();
 }
 
@@ -549,17 +933,17 @@ hipError_t launch_assign_offsets(const Plan& p, const Workspace& w, int64_t* off
   return hipGetLastError();
 }
 
-hipError_t launch_assign_scatter(const Plan& p, const Workspace& w, int64_t row0, int64_t rows, int max_extra,
-                                 const int64_t* offsets, int32_t* ids, hipStream_t s) {
+hipError_t launch_assign_scatter(const Plan& p, const Workspace& w, const int32_t* sel, int64_t row0, int64_t rows,
+                                 int max_extra, const int64_t* offsets, int32_t* ids, hipStream_t s) {
   const int NB = p.assignBlocks;
   const int BR = (int)((p.assignChunk + NB - 1) / NB);
   const int stride = 1 + max_extra;
   const size_t n = (size_t)NB * p.Kpad;
   hipLaunchKernelGGL(k_fill_u32, dim3(grid_n(n)), dim3(256), 0, s, w.acnt, n);
-  hipLaunchKernelGGL(k_block_count, dim3((NB + 63) / 64), dim3(64), 0, s, w.asel, rows, stride, BR, NB, w.acnt,
+  hipLaunchKernelGGL(k_block_count, dim3((NB + 63) / 64), dim3(64), 0, s, sel, rows, stride, BR, NB, w.acnt,
                      p.Kpad);
   hipLaunchKernelGGL(k_block_scan, dim3((p.K + 255) / 256), dim3(256), 0, s, w.acnt, NB, p.K, p.Kpad, w.atot);
-  hipLaunchKernelGGL(k_block_scatter, dim3((NB + 63) / 64), dim3(64), 0, s, w.asel, rows, stride, BR, NB, w.acnt,
+  hipLaunchKernelGGL(k_block_scatter, dim3((NB + 63) / 64), dim3(64), 0, s, sel, rows, stride, BR, NB, w.acnt,
                      p.Kpad, w.acursor, offsets, row0, ids, w.flags);
   hipLaunchKernelGGL(k_cursor_advance, dim3((p.K + 255) / 256), dim3(256), 0, s, w.acursor, w.atot, p.K);
   return hipGetLastError();

@@ -72,6 +72,7 @@ struct Workspace {
   int colG;
   // soft assignment
   int32_t* asel;                 // assignChunk * 9  per-row selections
+  float4* agco;                  // Kpad / 32  per-group error-bound coefficients
   unsigned long long* acounts;   // Kpad  list sizes
   unsigned* acnt;                // assignBlocks * Kpad  per-(block, list) counts / ranks
   unsigned* atot;                // Kpad  per-chunk list totals
@@ -130,13 +131,15 @@ hipError_t launch_mstep(const Plan& p, const Workspace& w, const double* Nk, con
 hipError_t launch_init(const Plan& p, const Workspace& w, const float* X, int64_t N, int64_t ldx,
                        float var_floor, float* weights, float* means, float* vars, hipStream_t s);
 // Soft assignment (gmm_assign.hip).  Pass A: select + count each chunk, then
-// offsets; pass B: select again (unless one chunk) and scatter.
+// offsets; pass B: scatter each chunk's selections, selected again unless
+// they were kept.  sel receives rows x (1 + max_extra) selections.
 hipError_t assign_occupancy(const Plan& p, int* occ);
 hipError_t launch_assign_begin(const Plan& p, const Workspace& w, hipStream_t s);
 hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* X, int64_t row0, int64_t rows,
-                                int64_t ldx, float threshold, int max_extra, bool count, hipStream_t s);
+                                int64_t ldx, float threshold, int max_extra, bool count, int32_t* sel,
+                                hipStream_t s);
 hipError_t launch_assign_offsets(const Plan& p, const Workspace& w, int64_t* offsets, hipStream_t s);
-hipError_t launch_assign_scatter(const Plan& p, const Workspace& w, int64_t row0, int64_t rows, int max_extra,
-                                 const int64_t* offsets, int32_t* ids, hipStream_t s);
+hipError_t launch_assign_scatter(const Plan& p, const Workspace& w, const int32_t* sel, int64_t row0, int64_t rows,
+                                 int max_extra, const int64_t* offsets, int32_t* ids, hipStream_t s);
 
 }  // namespace gmm

@@ -1489,6 +1489,7 @@ size_t workspace_bytes(const Plan& p) {
   b += up((size_t)p.K * 8);
   b += up(16);
   b += up((size_t)p.assignChunk * 9 * 4);
+  b += up((size_t)p.Kpad / 32 * 16);
   b += up((size_t)p.Kpad * 8);
   b += up((size_t)p.assignBlocks * p.Kpad * 4);
   b += up((size_t)p.Kpad * 4);
