@@ -344,45 +344,229 @@ __device__ __forceinline__ float xsum16(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Logits of one component group, component-major: W is the MFMA A operand
+// and x the B operand (both have the same per-lane register form), so lane
+// (g, r16), register v of block cb accumulates component cb * 16 + 4 g + v
+// for row pb * 16 + r16.  Split-bf16, three passes per block as in
+// logit_tile_split.  The W operands of each step are fetched one step ahead
+// (two register sets, steps taken in pairs), and the last step fetches the
+// first step of the next group (wn0, wn1; the current group's again when
+// there is none), so the L2 latency of W overlaps MFMA work or the previous
+// group's epilogue.  wf holds the step-0 operands on entry and the next
+// group's on exit; cf, likewise, the starting values c of the next group's
+// accumulators (cvn: its first component's c).
+template <class SH, int DPW>
+__device__ __forceinline__ void logit_group_ct(const __bf16* __restrict__ xsb, const __bf16* __restrict__ ws0,
+                                               const __bf16* __restrict__ ws1, const __bf16* __restrict__ wn0,
+                                               const __bf16* __restrict__ wn1, const float* __restrict__ cvn,
+                                               bf16x8 (&wf)[4], f4 (&cf)[2], f4 (&acc)[SH::NPB][2], int lane) {
+  using SR = SplitRow<DPW, false>;
+  constexpr int S = SR::S;
+  const int g = lane >> 4, r16 = lane & 15;
+  const __bf16* arow = xsb + r16 * SR::XSR + g * 8;
+  // W operands of step st of the blocks b0, b1 into wd (issued, not waited for)
+  auto fetch = [&](bf16x8 (&wd)[4], const __bf16* b0, const __bf16* b1, int st) {
+    wd[0] = *reinterpret_cast<const bf16x8*>(b0 + ((st * 2 + 0) * kWave + lane) * 8);
+    wd[1] = *reinterpret_cast<const bf16x8*>(b0 + ((st * 2 + 1) * kWave + lane) * 8);
+    wd[2] = *reinterpret_cast<const bf16x8*>(b1 + ((st * 2 + 0) * kWave + lane) * 8);
+    wd[3] = *reinterpret_cast<const bf16x8*>(b1 + ((st * 2 + 1) * kWave + lane) * 8);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMA work
+  };
+  auto step = [&](const bf16x8 (&wc)[4], int st) {
+    auto ld = [&](int pb, int off) {
+      return *reinterpret_cast<const bf16x8*>(arow + pb * 16 * SR::XSR + off + st * 32);
+    };
+    bf16x8 ahn = ld(0, 0), aln = ld(0, SR::LO);
+#pragma unroll
+    for (int pb = 0; pb < SH::NPB; ++pb) {
+      const bf16x8 ah = ahn, al = aln;
+      if (pb + 1 < SH::NPB) {
+        ahn = ld(pb + 1, 0);
+        aln = ld(pb + 1, SR::LO);
+      }
+      // small terms first
+      acc[pb][0] = mfma_bf16(wc[0], al, acc[pb][0]);
+      acc[pb][1] = mfma_bf16(wc[2], al, acc[pb][1]);
+      acc[pb][0] = mfma_bf16(wc[1], ah, acc[pb][0]);
+      acc[pb][1] = mfma_bf16(wc[3], ah, acc[pb][1]);
+      acc[pb][0] = mfma_bf16(wc[0], ah, acc[pb][0]);
+      acc[pb][1] = mfma_bf16(wc[2], ah, acc[pb][1]);
+    }
+  };
+  if constexpr (S % 2 == 0) {
+    bf16x8 wb[4];
+#pragma unroll 1
+    for (int st = 0; st < S; st += 2) {
+      fetch(wb, ws0, ws1, st + 1);
+      step(wf, st);
+      const bool last = st + 2 == S;  // uniform: pointer selects, no branch
+      fetch(wf, last ? wn0 : ws0, last ? wn1 : ws1, last ? 0 : st + 2);
+      step(wb, st + 1);
+    }
+  } else {
+    static_assert(S == 1, "odd step count: one step");
+    bf16x8 wb[4];
+    fetch(wb, wn0, wn1, 0);
+    step(wf, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wf[i] = wb[i];
+  }
+  cf[0] = *reinterpret_cast<const f4*>(cvn + 4 * g);
+  cf[1] = *reinterpret_cast<const f4*>(cvn + 16 + 4 * g);
+}
+
 __device__ __forceinline__ float max8(const f4& p, const f4& q) {
   return fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])), fmaxf(fmaxf(q[0], q[1]), fmaxf(q[2], q[3])));
 }
 
-// Float64 recomputation of the logits L >= tq[pb] of one wave's group
-// (component-major registers: bit pb * 8 + cb * 4 + v of a lane is row
-// pb * 16 + r16, component compbase + cb * 16 + 4 g + v).  Lane-major list,
-// 16 lanes per logit, four logits per pass, the same float64 arithmetic and
-// order per logit as the row-major refine_tile.
+// Order-preserving map of float32 onto int32 (LDS integer max of floats):
+// non-negative floats keep their bits, negative ones have the magnitude
+// bits flipped, so a < b as floats iff fkey(a) < fkey(b) as ints.
+__device__ __forceinline__ int fkey(float f) {
+  const int b = __float_as_int(f);
+  return b >= 0 ? b : b ^ 0x7FFFFFFF;
+}
+__device__ __forceinline__ float funkey(int k) { return __int_as_float(k >= 0 ? k : k ^ 0x7FFFFFFF); }
+
+// Float64 logits of the list entries [0, count) of one wave: entry codes
+// (register << 6 | lane) in elist, component-major registers (register
+// pb * 8 + cb * 4 + v of lane (g, r16): row pb * 16 + r16, component
+// compbase + cb * 16 + 4 g + v); 16 lanes per logit, four logits per pass,
+// results in rlist.  The same float64 arithmetic and order per logit as the
+// row-major refine_tile.
 template <class SH, int DPW>
-__device__ __forceinline__ void refine_ct(f4 (&acc)[SH::NPB][2], const float (&tq)[SH::NPB],
-                                          const float* __restrict__ xt, const EArgs& a, double C, int compbase,
-                                          float* __restrict__ rlist, unsigned short* __restrict__ elist, int lane,
-                                          unsigned& nsel) {
-  constexpr int NREG = SH::NPB * 8;
+__device__ __forceinline__ void refine_entries_ct(const unsigned short* __restrict__ elist, float* __restrict__ rlist,
+                                                  int count, const float* __restrict__ xt, const EArgs& a, double C,
+                                                  int compbase, int lane) {
   constexpr int DPT = DPW / 16;            // dims per lane (16 lanes per logit)
   constexpr int DCH = DPT < 4 ? DPT : 4;   // dims with loads in flight together
   const int g = lane >> 4, r16 = lane & 15;
-  unsigned sel = 0;
+  for (int base = 0; base < count; base += 4) {
+    const int e = base + g;
+    const bool live = e < count;
+    const int code = live ? (int)elist[e] : 0;
+    const int r = code >> 6, ln = code & 63;
+    const int pt = (r >> 3) * 16 + (ln & 15);
+    const int comp = compbase + ((r >> 2) & 1) * 16 + 4 * (ln >> 4) + (r & 3);
+    const double2* wr = a.w64 + (size_t)comp * a.Dp;
+    const double cf = (live && r16 == 0) ? a.cfull[comp] : 0.0;
+    double t = 0.0;
+    if (live) {
 #pragma unroll
-  for (int pb = 0; pb < SH::NPB; ++pb)
+      for (int j0 = 0; j0 < DPT; j0 += DCH) {
+        double2 ab[DCH];
+        float xv[DCH];
+#pragma unroll
+        for (int j = 0; j < DCH; ++j) {
+          const int d = r16 + 16 * (j0 + j);  // < Dp: padded dims have a = b = 0
+          ab[j] = wr[d];
+          xv[j] = xt[pt * SH::RS + d];
+        }
+#pragma unroll
+        for (int j = 0; j < DCH; ++j) {
+          const double x = (double)xv[j];
+          t = fma(ab[j].x, x * x, fma(ab[j].y, x, t));
+        }
+      }
+    }
+    t += __shfl_xor(t, 8);
+    t += __shfl_xor(t, 4);
+    t += __shfl_xor(t, 2);
+    t += __shfl_xor(t, 1);
+    if (live && r16 == 0) rlist[e] = (float)((cf - C) + t);
+  }
+}
+
+// Mask of the lanes whose register e = pb * 8 + cb * 4 + v is >= lim[pb].
+template <int NPB>
+__device__ __forceinline__ unsigned long long sel_mask(const f4 (&acc)[NPB][2], const float (&lim)[NPB], int e) {
+  return __ballot(acc[e >> 3][(e >> 2) & 1][e & 3] >= lim[e >> 3]);
+}
+
+// Lanes below this one in mask m.
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+}
+
+// List of the registers >= lim, register by register (register order, then
+// lane order), one ballot per register: entry codes (register << 6 | lane)
+// go to codes16[i], or, with vals given, the value to vals[i] and the code
+// (as float bits) to codesf[i], for the first cap entries.  Returns the
+// count over the wave (also past cap).
+template <int NPB>
+__device__ __forceinline__ int list_ge(const f4 (&acc)[NPB][2], const float (&lim)[NPB], int lane, int cap,
+                                       unsigned short* __restrict__ codes16, float* __restrict__ vals,
+                                       float* __restrict__ codesf) {
+  int n = 0;
+#pragma unroll
+  for (int e = 0; e < NPB * 8; ++e) {
+    const unsigned long long m = sel_mask(acc, lim, e);
+    if (m) {
+      if ((m >> lane) & 1ull) {
+        const int i = n + lanes_below(m);
+        if (i < cap) {
+          if (codes16) codes16[i] = (unsigned short)((e << 6) | lane);
+          if (vals) {
+            vals[i] = acc[e >> 3][(e >> 2) & 1][e & 3];
+            codesf[i] = __int_as_float((e << 6) | lane);
+          }
+        }
+      }
+      n += __popcll(m);
+    }
+  }
+  return n;
+}
+
+// Marks the accumulators as changed (no instruction): later selection masks
+// are recomputed from them instead of being kept in scalar registers.
+template <int NPB>
+__device__ __forceinline__ void opaque(f4 (&acc)[NPB][2]) {
+#pragma unroll
+  for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float L = acc[pb][cb][v];
-        const bool b = (L >= tq[pb]) && (L != kNegInf) && (compbase + cb * 16 + 4 * g + v < a.K);
-        sel |= (b ? 1u : 0u) << (pb * 8 + cb * 4 + v);
-      }
-  const int c = __popc(sel);
-  int pre = 0, total = 0;
+      for (int v = 0; v < 4; ++v) asm volatile("" : "+v"(acc[pb][cb][v]));
+}
+
+// Float64 recomputation of the logits L >= tq[pb] of one wave's group
+// (tq > -inf, so -inf logits, padding included, never qualify).  Up to
+// kRefineCap of them: one list, built and taken back register by register;
+// more: lane-major batches from per-lane bit masks.  Returns their number.
+template <class SH, int DPW>
+__device__ __forceinline__ int refine_ct(f4 (&acc)[SH::NPB][2], const float (&tq)[SH::NPB],
+                                         const float* __restrict__ xt, const EArgs& a, double C, int compbase,
+                                         float* __restrict__ rlist, unsigned short* __restrict__ elist, int lane) {
+  constexpr int NREG = SH::NPB * 8;
+  const int total = list_ge(acc, tq, lane, kRefineCap, elist, nullptr, nullptr);
+  if (total == 0) return 0;
+  if (total <= kRefineCap) {
+    wave_sync();
+    refine_entries_ct<SH, DPW>(elist, rlist, total, xt, a, C, compbase, lane);
+    wave_sync();
+    opaque(acc);
+    int n = 0;
 #pragma unroll
-  for (int b = 0; b < 6; ++b) {
-    const unsigned long long m = __ballot((c >> b) & 1);
-    pre += (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u)) << b;
-    total += __popcll(m) << b;
+    for (int e = 0; e < NREG; ++e) {
+      const unsigned long long m = sel_mask(acc, tq, e);
+      if (m) {
+        if ((m >> lane) & 1ull) acc[e >> 3][(e >> 2) & 1][e & 3] = rlist[n + lanes_below(m)];
+        n += __popcll(m);
+      }
+    }
+    wave_sync();
+    return total;
   }
-  if (total == 0) return;  // uniform over the wave
-  nsel += (unsigned)total;
+  unsigned sel = 0;
+#pragma unroll
+  for (int e = 0; e < NREG; ++e)
+    sel |= (acc[e >> 3][(e >> 2) & 1][e & 3] >= tq[e >> 3] ? 1u : 0u) << e;
+  const int c = __popc(sel);
+  int pre = 0;
+#pragma unroll
+  for (int b = 0; b < 6; ++b) pre += lanes_below(__ballot((c >> b) & 1)) << b;
+  wave_sync();  // the register-order list above is overwritten
   for (int b0 = 0; b0 < total; b0 += kRefineCap) {
     const int count = min(kRefineCap, total - b0);
     {
@@ -396,40 +580,7 @@ __device__ __forceinline__ void refine_ct(f4 (&acc)[SH::NPB][2], const float (&t
       }
     }
     wave_sync();
-    for (int base = 0; base < count; base += 4) {
-      const int e = base + g;
-      const bool live = e < count;
-      const int code = live ? (int)elist[e] : 0;
-      const int r = code >> 6, ln = code & 63;
-      const int pt = (r >> 3) * 16 + (ln & 15);
-      const int comp = compbase + ((r >> 2) & 1) * 16 + 4 * (ln >> 4) + (r & 3);
-      const double2* wr = a.w64 + (size_t)comp * a.Dp;
-      const double cf = (live && r16 == 0) ? a.cfull[comp] : 0.0;
-      double t = 0.0;
-      if (live) {
-#pragma unroll
-        for (int j0 = 0; j0 < DPT; j0 += DCH) {
-          double2 ab[DCH];
-          float xv[DCH];
-#pragma unroll
-          for (int j = 0; j < DCH; ++j) {
-            const int d = r16 + 16 * (j0 + j);  // < Dp: padded dims have a = b = 0
-            ab[j] = wr[d];
-            xv[j] = xt[pt * SH::RS + d];
-          }
-#pragma unroll
-          for (int j = 0; j < DCH; ++j) {
-            const double x = (double)xv[j];
-            t = fma(ab[j].x, x * x, fma(ab[j].y, x, t));
-          }
-        }
-      }
-      t += __shfl_xor(t, 8);
-      t += __shfl_xor(t, 4);
-      t += __shfl_xor(t, 2);
-      t += __shfl_xor(t, 1);
-      if (live && r16 == 0) rlist[e] = (float)((cf - C) + t);
-    }
+    refine_entries_ct<SH, DPW>(elist, rlist, count, xt, a, C, compbase, lane);
     wave_sync();
     {
       int idx = pre - b0;
@@ -442,21 +593,40 @@ __device__ __forceinline__ void refine_ct(f4 (&acc)[SH::NPB][2], const float (&t
     }
     wave_sync();
   }
+  return total;
 }
 
-template <int WC, int DPW, int BN>
+// Insert (val, k) into a list of N entries sorted by value descending,
+// index ascending (as top_insert).
+template <int N>
+__device__ __forceinline__ void top_insert_n(float (&tv)[N], int (&tk)[N], float val, int k) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bool b = (val > tv[i]) || (val == tv[i] && k < tk[i]);
+    const float ov = tv[i];
+    const int ok = tk[i];
+    tv[i] = b ? val : ov;
+    tk[i] = b ? k : ok;
+    val = b ? ov : val;
+    k = b ? ok : k;
+  }
+}
+
+// TOPN: list entries per row (1 + the largest max_extra it serves).
+template <int WC, int DPW, int BN, int TOPN>
 __global__ void __launch_bounds__(kWave* WC) k_assign_ct(EArgs a, AArgs s) {
   using SH = Shape<WC, 1, DPW, BN>;
   using SPR = SplitRow<DPW, false>;
   constexpr int NPB = SH::NPB;
   constexpr bool NIS = DPW == 128;       // row norms formed while splitting the rows
-  constexpr int LSTW = 2 * kTopN * BN;   // one wave's lists (values, indices)
+  constexpr int LSTW = 2 * TOPN * BN > 512 ? 2 * TOPN * BN : 512;  // per wave: lists, or candidates
   constexpr int CAPC = LSTW / 2;         // candidates per compaction batch
   __shared__ __attribute__((aligned(16))) float xt[SH::TILE];
   __shared__ __attribute__((aligned(16))) __bf16 xsb[BN * SPR::XSR];
   __shared__ float tbuf[WC][LSTW];
   __shared__ float lpart[WC][BN];
   __shared__ float2 nrm[BN];
+  __shared__ int cbnd[BN];  // shared candidate bound per row (fkey), the largest any wave has shown
   __shared__ float rlist[WC][kRefineCap];
   __shared__ unsigned short elist[WC][kRefineCap];
 
@@ -480,6 +650,7 @@ __global__ void __launch_bounds__(kWave* WC) k_assign_ct(EArgs a, AArgs s) {
       stg.load(a.X, a.ldx, a.row0 + trow, rows, a.D);
       stg.store(xt);
     }
+    if (tid < BN) cbnd[tid] = fkey(kNegInf);  // published by the second barrier
     __syncthreads();
     split_rows<SH, DPW, false>(xt, xsb, w, NIS ? nrm : nullptr);
     if constexpr (!NIS) row_norms2<SH, DPW>(xt, nrm, a.Dp);
@@ -495,47 +666,53 @@ __global__ void __launch_bounds__(kWave* WC) k_assign_ct(EArgs a, AArgs s) {
       S[pb] = 0.f;
       Rlb[pb] = kNegInf;
     }
-    float tv[kTopN];
-    int tk[kTopN];
+    float tv[TOPN];
+    int tk[TOPN];
 #pragma unroll
-    for (int i = 0; i < kTopN; ++i) {
+    for (int i = 0; i < TOPN; ++i) {
       tv[i] = kNegInf;
       tk[i] = INT_MAX;
     }
+    auto wblk = [&](int cb16) { return a.wsp + (size_t)cb16 * SPR::WBLK; };
+    // the first step's W operands and the c values of this wave's next group
+    bf16x8 wf[4];
+    f4 cf[2];
+    if (w < ncg) {
+      const __bf16* b0 = wblk(2 * w);
+      const __bf16* b1 = wblk(2 * w + 1);
+      wf[0] = *reinterpret_cast<const bf16x8*>(b0 + lane * 8);
+      wf[1] = *reinterpret_cast<const bf16x8*>(b0 + (kWave + lane) * 8);
+      wf[2] = *reinterpret_cast<const bf16x8*>(b1 + lane * 8);
+      wf[3] = *reinterpret_cast<const bf16x8*>(b1 + (kWave + lane) * 8);
+      cf[0] = *reinterpret_cast<const f4*>(a.cvec + w * 32 + 4 * g);
+      cf[1] = *reinterpret_cast<const f4*>(a.cvec + w * 32 + 16 + 4 * g);
+    }
     for (int cg = w; cg < ncg; cg += WC) {
       const int compbase = cg * 32;
+      const int cgn = (cg + WC < ncg) ? cg + WC : cg;
+      const float4 gc = s.gco[cg];  // used after the contraction
       f4 acc[NPB][2];
-      {
-        const f4 c0 = *reinterpret_cast<const f4*>(a.cvec + compbase + 4 * g);
-        const f4 c1 = *reinterpret_cast<const f4*>(a.cvec + compbase + 16 + 4 * g);
 #pragma unroll
-        for (int pb = 0; pb < NPB; ++pb) {
-          acc[pb][0] = c0;
-          acc[pb][1] = c1;
-        }
+      for (int pb = 0; pb < NPB; ++pb) {
+        acc[pb][0] = cf[0];
+        acc[pb][1] = cf[1];
       }
-      logit_tile_split<SH, DPW, false, true>(xsb, a.wsp + (size_t)(compbase >> 4) * SPR::WBLK,
-                                             a.wsp + (size_t)((compbase >> 4) + 1) * SPR::WBLK, acc, lane);
+      logit_group_ct<SH, DPW>(xsb, wblk(2 * cg), wblk(2 * cg + 1), wblk(2 * cgn), wblk(2 * cgn + 1),
+                              a.cvec + cgn * 32, wf, cf, acc, lane);
       // 1. running lower bound Rlb of the row's largest logit (the largest
       //    L - E seen so far) and the refinement test: L + E_k >= Rlb - delta
       //    implies L >= tq, since E_k <= Eg (the margin covers the roundings
-      //    of both forms)
-      const float4 gc = s.gco[cg];
+      //    of both forms); tq > -inf keeps -inf logits (padding) out
       float tq[NPB];
-      unsigned long long anyr = 0;
 #pragma unroll
       for (int pb = 0; pb < NPB; ++pb) {
         const float Eg = a.kappa * (gc.x * nn[pb].x + gc.y * nn[pb].y + gc.z);
         const float lb = xmax16(xmax32(max8(acc[pb][0], acc[pb][1]) - Eg));
         Rlb[pb] = fmaxf(Rlb[pb], lb);
         const float thr = Rlb[pb] - s.delta;
-        tq[pb] = rok[pb] ? (thr - Eg) - (fabsf(thr) + Eg) * 0x1p-21f : kPosInf;
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) anyr |= __ballot(acc[pb][cb][v] >= tq[pb]);
+        tq[pb] = rok[pb] ? fmaxf((thr - Eg) - (fabsf(thr) + Eg) * 0x1p-21f, -__FLT_MAX__) : kPosInf;
       }
-      if (anyr) refine_ct<SH, DPW>(acc, tq, xt, a, C, compbase, rlist[w], elist[w], lane, nsel);
+      nsel += (unsigned)refine_ct<SH, DPW>(acc, tq, xt, a, C, compbase, rlist[w], elist[w], lane);
       // 2. online log-sum-exp with a lagging reference: M moves only when a
       //    logit exceeds it by more than kLag nats
 #pragma unroll
@@ -553,43 +730,38 @@ __global__ void __launch_bounds__(kWave* WC) k_assign_ct(EArgs a, AArgs s) {
           for (int v = 0; v < 4; ++v) sm += __expf(acc[pb][cb][v] - ms);
         S[pb] += sm;
       }
-      // 3. top-list candidates: only a logit at or above the row's bound can
-      //    be selected (the argmax is at least Rlb, less one float32 rounding
-      //    of a refined value, and an extra needs l - log Z >= log(threshold)
-      //    with log Z at least that); they are compacted into a lane-major
-      //    list and lane p inserts the entries of row p
+      // 3. top-list candidates.  A logit can be selected only if it is at
+      //    least (a) the row's argmax lower bound Rlb (less one float32
+      //    rounding of a refined value) plus min(log threshold, 0), since an
+      //    extra needs l - log Z >= log threshold and log Z >= Rlb, and
+      //    (b) the TOPN-th value of any wave's list of the row.  Every wave
+      //    shows its bounds in cbnd (LDS integer max), so each filters with
+      //    the largest bound shown so far; which bound a wave sees changes
+      //    only which non-selectable logits it inserts, not the lists'
+      //    selectable entries.  Candidates are listed register by register
+      //    and lane p inserts the entries of row p.
       float bnd[NPB];
-      unsigned long long anyc = 0;
 #pragma unroll
       for (int pb = 0; pb < NPB; ++pb) {
         const float rb = Rlb[pb];
-        bnd[pb] = rok[pb] ? rb + s.cand_off - (fabsf(rb) * 2.4e-7f + 1e-6f) : kPosInf;
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) anyc |= __ballot(acc[pb][cb][v] >= bnd[pb]);
+        const float own = rb + s.cand_off - (fabsf(rb) * 2.4e-7f + 1e-6f);
+        const int seen = atomicMax(&cbnd[pb * 16 + r16], fkey(own));
+        bnd[pb] = rok[pb] ? fmaxf(own, funkey(seen)) : kPosInf;
       }
-      if (anyc) {
-        unsigned cbits = 0;
+      const int ncand = list_ge(acc, bnd, lane, CAPC, nullptr, tl, tl + CAPC);
+      if (ncand) {
+        for (int b0 = 0; b0 < ncand; b0 += CAPC) {
+          const int n = min(CAPC, ncand - b0);
+          if (ncand > CAPC) {
+            // more than one batch: lane-major order from per-lane bit masks
+            unsigned cbits = 0;
 #pragma unroll
-        for (int pb = 0; pb < NPB; ++pb)
+            for (int e = 0; e < NPB * 8; ++e)
+              cbits |= (acc[e >> 3][(e >> 2) & 1][e & 3] >= bnd[e >> 3] ? 1u : 0u) << e;
+            const int c = __popc(cbits);
+            int pre = 0;
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) cbits |= (acc[pb][cb][v] >= bnd[pb] ? 1u : 0u) << (pb * 8 + cb * 4 + v);
-        const int c = __popc(cbits);
-        int pre = 0, total = 0;
-#pragma unroll
-        for (int b = 0; b < 6; ++b) {
-          const unsigned long long m = __ballot((c >> b) & 1);
-          pre += (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u)) << b;
-          total += __popcll(m) << b;
-        }
-        // tl[0, CAPC): candidate values; tl[CAPC, 2 CAPC): their codes
-        // (register << 6 | lane) as float bit patterns
-        for (int b0 = 0; b0 < total; b0 += CAPC) {
-          const int n = min(CAPC, total - b0);
-          {
+            for (int b = 0; b < 6; ++b) pre += lanes_below(__ballot((c >> b) & 1)) << b;
             int idx = pre - b0;
 #pragma unroll
             for (int r = 0; r < NPB * 8; ++r)
@@ -609,8 +781,9 @@ __global__ void __launch_bounds__(kWave* WC) k_assign_ct(EArgs a, AArgs s) {
               const float cvv = tl[e];
               const int r = code >> 6, ln = code & 63;
               if ((r >> 3) * 16 + (ln & 15) == lane)
-                top_insert(tv, tk, cvv, compbase + ((r >> 2) & 1) * 16 + 4 * (ln >> 4) + (r & 3));
+                top_insert_n<TOPN>(tv, tk, cvv, compbase + ((r >> 2) & 1) * 16 + 4 * (ln >> 4) + (r & 3));
             }
+            atomicMax(&cbnd[lane], fkey(tv[TOPN - 1]));
           }
           wave_sync();
         }
@@ -626,9 +799,9 @@ __global__ void __launch_bounds__(kWave* WC) k_assign_ct(EArgs a, AArgs s) {
     }
     if (w > 0 && lane < BN) {
 #pragma unroll
-      for (int i = 0; i < kTopN; ++i) {
+      for (int i = 0; i < TOPN; ++i) {
         tl[i * BN + lane] = tv[i];
-        tl[(kTopN + i) * BN + lane] = __int_as_float(tk[i]);
+        tl[(TOPN + i) * BN + lane] = __int_as_float(tk[i]);
       }
     }
     __syncthreads();
@@ -637,10 +810,10 @@ __global__ void __launch_bounds__(kWave* WC) k_assign_ct(EArgs a, AArgs s) {
       for (int q = 1; q < WC; ++q) {
         const float* o = tbuf[q];
 #pragma unroll 1
-        for (int i = 0; i < kTopN; ++i) {
+        for (int i = 0; i < TOPN; ++i) {
           const float v = o[i * BN + tid];
           if (v == kNegInf) break;
-          top_insert(tv, tk, v, __float_as_int(o[(kTopN + i) * BN + tid]));
+          top_insert_n<TOPN>(tv, tk, v, __float_as_int(o[(TOPN + i) * BN + tid]));
         }
       }
       if (tid < rows) {
@@ -658,7 +831,7 @@ __global__ void __launch_bounds__(kWave* WC) k_assign_ct(EArgs a, AArgs s) {
           if (s.counts) atomicAdd(&s.counts[tk[0]], 1ull);
           int n = 1;
 #pragma unroll
-          for (int i = 1; i < kTopN; ++i) {
+          for (int i = 1; i < TOPN; ++i) {
             if (i <= s.m && tv[i] != kNegInf && tv[i] - lz >= s.log_thr) {
               out[n++] = tk[i];
               if (s.counts) atomicAdd(&s.counts[tk[i]], 1ull);
@@ -817,21 +990,24 @@ struct AKern {
   static constexpr int BN = bn_for(WD, DPW);
   template <int M>
   static void* assign() { return (void*)&k_assign<WC, WD, DPW, BN, M>; }
+  template <int TOPN>
   static void* assign_split() {
-    if constexpr (WD == 1) return (void*)&k_assign_ct<WC, DPW, BN>;
+    if constexpr (WD == 1) return (void*)&k_assign_ct<WC, DPW, BN, TOPN>;
     else return nullptr;
   }
 };
 
-// t[0..2]: float32, refined, float64 logits; t[3]: refined with split-bf16
+// t[0..2]: float32, refined, float64 logits; t[3..5]: refined with split-bf16
 // first-pass logits (nullptr where not built)
-static bool alookup(int WC, int WD, int DPW, void* (&t)[4]) {
+static bool alookup(int WC, int WD, int DPW, void* (&t)[6]) {
 #define GMM_A(wc, wd, dpw)                                           \
   if (WC == wc && WD == wd && DPW == dpw) {                          \
     t[0] = AKern<wc, wd, dpw>::assign<0>();                          \
     t[1] = AKern<wc, wd, dpw>::assign<1>();                          \
     t[2] = AKern<wc, wd, dpw>::assign<2>();                          \
-    t[3] = AKern<wc, wd, dpw>::assign_split();                       \
+    t[3] = AKern<wc, wd, dpw>::assign_split<2>();                    \
+    t[4] = AKern<wc, wd, dpw>::assign_split<4>();                    \
+    t[5] = AKern<wc, wd, dpw>::assign_split<kTopN>();                \
     return true;                                                     \
   }
   GMM_A(1, 1, 16) GMM_A(1, 1, 32) GMM_A(1, 1, 64) GMM_A(1, 1, 128)
@@ -853,25 +1029,26 @@ static int assign_wc(const Plan& p) {
 }
 
 hipError_t assign_occupancy(const Plan& p, int* occ) {
-  void* t[4];
+  void* t[6];
   const int wc = assign_wc(p);
   *occ = 0;
   if (!alookup(wc, p.WD, p.DPW, t)) return hipSuccess;  // no assignment kernel for this shape
-  int o0 = 0, o1 = 0, o3 = 1 << 30;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o0, (const void*)t[0], 64 * wc * p.WD, 0);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1, (const void*)t[1], 64 * wc * p.WD, 0);
-  if (e == hipSuccess && t[3])
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o3, (const void*)t[3], 64 * wc * p.WD, 0);
-  if (e != hipSuccess) return e;
-  *occ = o0 < o1 ? o0 : o1;
-  if (o3 < *occ) *occ = o3;
+  int o = 1 << 30;
+  for (int i = 0; i < 6; ++i) {
+    if (i == 2 || !t[i]) continue;  // the float64 variant has its own LDS; it takes the same grid
+    int oi = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&oi, (const void*)t[i], 64 * wc * p.WD, 0);
+    if (e != hipSuccess) return e;
+    if (oi < o) o = oi;
+  }
+  *occ = o;
   return hipSuccess;
 }
 
 hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* X, int64_t row0, int64_t rows,
                                 int64_t ldx, float threshold, int max_extra, bool count, int32_t* sel,
                                 hipStream_t s) {
-  void* t[4];
+  void* t[6];
   const int wc = assign_wc(p);
   if (!alookup(wc, p.WD, p.DPW, t)) return hipErrorInvalidValue;
   EArgs a{};
@@ -912,9 +1089,10 @@ hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* 
   const int64_t gmax = (int64_t)p.numCU * (p.occAssign > 0 ? p.occAssign : 1);
   const int grid = (int)(tiles < gmax ? tiles : gmax);
   void* kern = t[w.f64 ? 2 : (w.refine ? 1 : 0)];
-  if (!w.f64 && w.refine && w.split && t[3]) {
+  void* ct = t[max_extra <= 1 ? 3 : (max_extra <= 3 ? 4 : 5)];  // list length 2, 4 or 9
+  if (!w.f64 && w.refine && w.split && ct) {
     // split-bf16 first-pass logits, the refinement bound widened to match
-    kern = t[3];
+    kern = ct;
     a.wsp = w.wsplit;
     a.kappa = (float)((6.0 * p.Dp + 8.0) * 5.9604644775390625e-08 * (1.0 + 1.0 / 64.0) + 3.1 * 1.52587890625e-05);
   }

@@ -419,11 +419,8 @@ __device__ __forceinline__ void split_rows(const float* __restrict__ xt, __bf16*
 // take cost more in spills of the whole kernel than the exposed load latency
 // (measured 748 against 813 ms per EM iteration at N=1e8, K=1024).
 // ws0/ws1: the two component blocks' split W, [step][hi, lo][lane][8].
-// acc must hold the starting value.  CT: W is the A operand and x the B
-// operand (the two have the same per-lane register form), so lane (g, r16),
-// register v accumulates component 4 g + v of the block for row r16 instead
-// of row 4 g + v for component r16; the products are the same.
-template <class SH, int DPW, bool ISO, bool CT = false>
+// acc must hold the starting value.
+template <class SH, int DPW, bool ISO>
 __device__ __forceinline__ void logit_tile_split(const __bf16* __restrict__ xsb, const __bf16* __restrict__ ws0,
                                                  const __bf16* __restrict__ ws1, f4 (&acc)[SH::NPB][2], int lane) {
   using SR = SplitRow<DPW, ISO>;
@@ -447,21 +444,12 @@ __device__ __forceinline__ void logit_tile_split(const __bf16* __restrict__ xsb,
         aln = ld(pb + 1, SR::LO);
       }
       // small terms first
-      if constexpr (CT) {
-        acc[pb][0] = mfma_bf16(h0, al, acc[pb][0]);
-        acc[pb][1] = mfma_bf16(h1, al, acc[pb][1]);
-        acc[pb][0] = mfma_bf16(l0, ah, acc[pb][0]);
-        acc[pb][1] = mfma_bf16(l1, ah, acc[pb][1]);
-        acc[pb][0] = mfma_bf16(h0, ah, acc[pb][0]);
-        acc[pb][1] = mfma_bf16(h1, ah, acc[pb][1]);
-      } else {
-        acc[pb][0] = mfma_bf16(al, h0, acc[pb][0]);
-        acc[pb][1] = mfma_bf16(al, h1, acc[pb][1]);
-        acc[pb][0] = mfma_bf16(ah, l0, acc[pb][0]);
-        acc[pb][1] = mfma_bf16(ah, l1, acc[pb][1]);
-        acc[pb][0] = mfma_bf16(ah, h0, acc[pb][0]);
-        acc[pb][1] = mfma_bf16(ah, h1, acc[pb][1]);
-      }
+      acc[pb][0] = mfma_bf16(al, h0, acc[pb][0]);
+      acc[pb][1] = mfma_bf16(al, h1, acc[pb][1]);
+      acc[pb][0] = mfma_bf16(ah, l0, acc[pb][0]);
+      acc[pb][1] = mfma_bf16(ah, l1, acc[pb][1]);
+      acc[pb][0] = mfma_bf16(ah, h0, acc[pb][0]);
+      acc[pb][1] = mfma_bf16(ah, h1, acc[pb][1]);
     }
   }
 }

@@ -184,6 +184,41 @@ def test_soft_assign_exact_duplicate_components(mfma):
     compare(gpu, lists, other, f"duplicates ({mfma})")
 
 
+@pytest.mark.parametrize("mfma", ["split", "fp32"])
+@pytest.mark.parametrize("D,m", [(16, 3), (128, 1), (128, 8), (96, 2)])
+def test_soft_assign_all_components_tied(D, m, mfma):
+    """Every component has the same parameters, so each row's K logits are
+    bit-identical on the GPU and every responsibility is exactly 1/K: the
+    rule's tie-break by the lower index makes the lists {0, ..., m} for every
+    row (threshold 0.5/K).  All of a row's logits then sit inside the float64
+    window and clear the candidate bound, so every component group of every
+    wave overflows the one-pass refinement and candidate lists (256 entries
+    each) and runs the batched branches.  The oracle's lists on the same
+    input agree (its responsibilities are also exactly tied)."""
+    from soft_clustering_amd import MFMA_FP32
+    K, N = 512, 3_001
+    thr = 0.5 / K
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((N, D)).astype(np.float32)
+    mu = np.broadcast_to(rng.standard_normal(D).astype(np.float32), (K, D)).copy()
+    var = np.full((K, D), 1.5, np.float32)
+    w = np.full(K, 1.0 / K, np.float32)
+    log(f"soft_assign all tied ({mfma}): N={N} D={D} K={K} m={m}")
+    g = GMM(K, D, DEV)
+    if mfma == "fp32":
+        g.set_mfma(MFMA_FP32)
+    offsets, ids = g.soft_assign(torch.as_tensor(X).to(DEV), *(torch.as_tensor(a).to(DEV) for a in (w, mu, var)),
+                                 thr, m)
+    gpu = csr_rows(offsets, ids, N, 1 + m)
+    want = np.broadcast_to(np.arange(m + 1), (N, m + 1))
+    assert np.array_equal(gpu, want), f"rows differ from {{0..{m}}}, e.g. {gpu[np.any(gpu != want, axis=1)][:1]}"
+    # the oracle's plain per-component log-densities tie exactly too (its
+    # BLAS path need not: a GEMM may round columns differently)
+    _, _, lists, _ = O.soft_assign(X[:64], w, mu, var, thr, m, method="direct", chunk_rows=64)
+    assert np.array_equal(oracle_rows(lists, 1 + m), want[:64])
+    g.close()
+
+
 def test_soft_assign_chunks_compose():
     """Rows past the first 2^19-row chunk go through the second selection
     pass and the list cursors: the lists of X equal the lists of its two
