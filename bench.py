@@ -80,6 +80,12 @@ def mfma_roofline(N, K, D, split, iso=False):
 
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                "k_stats_fused_large_traffic.md")
+COUNTER_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "k_stats_fused_large_counters.md")
+SIMDS = 1024          # 256 CUs x 4 SIMDs
+CLOCK_HZ = 2.4e9      # MI355X peak engine clock
+
+
 def kernel_source_hash(root=None):
     """sha256 prefix of the fused E-step's source: the text of k_stats (from its
     heading comment to the next kernel's) and the device code it includes."""
@@ -100,19 +106,26 @@ def measured_traffic():
     committed FETCH_SIZE + WRITE_SIZE counter summary (each counter scaled by
     what it reads for a copy of known size), or None when the kernel sources
     have changed since those counters were taken."""
+    return profile_field(TRAFFIC_PROFILE, "traffic_bytes_per_launch")
+
+
+def profile_field(path, name):
+    """A numeric field ("name: value" line) of a committed profile summary,
+    or None when the file is missing or the fused E-step's source has changed
+    since the counters in it were taken (its source_hash no longer matches)."""
     try:
-        with open(TRAFFIC_PROFILE) as fh:
+        with open(path) as fh:
             text = fh.read()
     except OSError:
         return None
     fields = {}
     for ln in text.splitlines():
-        if ":" in ln and ln.split(":", 1)[0] in ("traffic_bytes_per_launch", "source_hash"):
+        if ":" in ln and ln.split(":", 1)[0] in (name, "source_hash"):
             k, v = ln.split(":", 1)
             fields[k] = v.strip()
-    if fields.get("source_hash") != kernel_source_hash() or "traffic_bytes_per_launch" not in fields:
+    if fields.get("source_hash") != kernel_source_hash() or name not in fields:
         return None
-    return float(fields["traffic_bytes_per_launch"])
+    return float(fields[name])
 
 
 def cpu_model():
@@ -387,8 +400,11 @@ def main():
     hl = hist.cpu().numpy()
     peak, peak_basis = mfma_roofline(N, K, D, split, iso)
     traffic = None
+    busy_cycles = None
     if fused and split == 2 and args.workload == "large" and args.precision == "refined" and not args.rows:
-        traffic = measured_traffic()  # taken on the default kernel (split-bf16 logits and statistics)
+        # taken on the default kernel (split-bf16 logits and statistics)
+        traffic = measured_traffic()
+        busy_cycles = profile_field(COUNTER_PROFILE, "mfma_busy_cycles_per_launch")
     line = {
         "metric": "ms per EM iteration and GFLOP/s at N=100M,K=1024,D=128 fp32; % MFMA peak",
         "value": round(gflops, 1),
@@ -407,6 +423,11 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "peak_basis": peak_basis,
                      "fp32_peak_frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4),
                      "traffic": traffic,
+                     # matrix-pipe busy cycles per launch from the committed
+                     # counter summary (SQ_VALU_MFMA_BUSY_CYCLES) over this
+                     # run's launch time x 1024 SIMDs x 2.4 GHz
+                     "mfma_busy_from_counters": (round(busy_cycles / (avg_ms * 1e-3 * CLOCK_HZ * SIMDS), 4)
+                                                 if busy_cycles else None),
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "kernel": ("k_stats (fused E-step" + ["", ", split-bf16 logits", ", split-bf16 logits and statistics"][split]
                                 + ")") if fused
