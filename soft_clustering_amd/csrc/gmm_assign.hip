@@ -12,21 +12,27 @@
 // int32, ids ascending within each list.
 //
 // GPU design:
-//  * k_assign walks all component groups of a row tile with the same MFMA
-//    logit contraction, float64 refinement and online log-sum-exp as the
-//    E-step's first sweep.  After each 16-component block the wave transposes
-//    its logits through LDS so that lane p holds row p's 16 values, and keeps
-//    a sorted top-9 list (value descending, index ascending) per row in
-//    registers.  Because r is increasing in l, the extras are the list's
-//    entries 2..m+1 that clear log(threshold) against the row's log Z.
+//  * k_assign_ct (split-bf16 first-pass logits, D <= 128) is component-major:
+//    W is the MFMA A operand, so each lane holds one row's logits against
+//    four components of each 16-component block, and a row's maximum,
+//    log-sum-exp and thresholds are per-lane registers with two permlane
+//    steps per group.  Top lists (2, 4 or 9 entries, by max_extra) are kept
+//    per row in the registers of one owner lane, value descending, index
+//    ascending; only logits that can be selected are inserted.  Because r is
+//    increasing in l, the extras are the list's entries 2..m+1 that clear
+//    log(threshold) against the row's log Z.  k_assign (float32 or float64
+//    logits, and the shapes with several dim segments per component group)
+//    has the E-step's row-major layout and merges its lists through LDS.
 //  * Every logit that can be the argmax or clear the threshold lies within
 //    delta = max(16, 1 - log threshold) nats of the row's largest logit, and
-//    exactly those are recomputed in float64, so ranking and threshold tests
+//    each of those is recomputed in float64, so ranking and threshold tests
 //    use float64-accurate values.
-//  * Lists are built deterministically without sorting: pass A counts list
-//    sizes (integer atomics), a scan gives the offsets; pass B re-selects each
-//    chunk of rows, counts per (row block, list), scans those counts per list
-//    and lets one thread per row block place its rows in row order.
+//  * Lists are built deterministically without sorting: the counting sweep
+//    counts list sizes (integer atomics), a scan gives the offsets; per chunk
+//    of rows the selections (kept from the counting sweep, or selected again
+//    when they could not be kept) are counted per (row block, list), those
+//    counts scanned per list, and one thread per row block places its rows in
+//    row order.
 #include "gmm_device.h"
 
 #include <limits.h>
