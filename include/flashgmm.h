@@ -116,10 +116,9 @@ typedef enum {
  * gmm_workspace_bytes).  The only later allocations are those of the
  * out-of-core calls (gmm_estep_stats_host, gmm_fit_host): a copy stream and
  * two device staging buffers, made on their first use and grown when a call
- * asks for larger chunks; and of gmm_soft_assign over more than 2^19 rows:
- * one buffer of N * (1 + max_extra) int32 (kept when it is at most 4 GiB,
- * grown on demand).  Every other entry point allocates nothing; all of it
- * is freed by gmm_destroy.
+ * asks for larger chunks; and of gmm_soft_assign: its own buffers (see
+ * there), within the limit gmm_set_assign_limit sets.  Every other entry
+ * point allocates nothing; all of it is freed by gmm_destroy.
  * 1 <= K <= 65536, 1 <= D <= 1024. */
 gmm_status gmm_create(gmm_ctx **out /*[host]*/, int32_t K, int32_t D, void *hip_stream);
 
@@ -143,6 +142,14 @@ gmm_status gmm_set_precision(gmm_ctx *ctx, int32_t mode);
 
 /* Select the matrix instructions (gmm_mfma_kind) of later E-steps. */
 gmm_status gmm_set_mfma(gmm_ctx *ctx, int32_t kind);
+
+/* Limit, in bytes, of the device memory gmm_soft_assign may hold in the
+ * context beyond its workspace (the kept selections and the list-sort
+ * buffer); default 20 GiB.  0 keeps no selections and sorts nothing: every
+ * chunk is selected twice and the lists are built block by block.  Buffers
+ * already held beyond a new, smaller limit are freed.  bytes >= 0.
+ * Synchronises the stream. */
+gmm_status gmm_set_assign_limit(gmm_ctx *ctx, int64_t bytes);
 
 /* What the E-step of ctx for model (0 diagonal, 1 isotropic, 2 the k-means
  * hard assignment) runs with the context's current path, precision and
@@ -294,10 +301,15 @@ gmm_status gmm_init_kmeans(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, in
  * threshold) nats of a row's largest are evaluated in float64 (under
  * GMM_PREC_REFINED), so ranks and the threshold test are float64-accurate.
  * The result is deterministic.  0 < threshold <= 1, 0 <= max_extra <= 8,
- * N < 2^31.  Rows are processed in chunks of 2^19: a counting sweep, then
- * the scatter into the lists; the selections of the first sweep are kept for
- * the second in a context buffer of N * (1 + max_extra) int32 when that is at
- * most 4 GiB and can be allocated, otherwise the rows are selected again.
+ * N < 2^31.  Rows are selected in chunks of 2^19 by one counting sweep.
+ * Over more than one chunk the selections are kept in a context buffer of
+ * N * (1 + max_extra) int32; with every row's selections at hand the lists
+ * come from one stable radix sort of (list, row) pairs in a second context
+ * buffer (about 16 bytes per selection slot).  Both buffers are allocated on
+ * first need, grown on demand and held until gmm_destroy, within the
+ * context's assignment limit (gmm_set_assign_limit, default 20 GiB); where
+ * they do not fit or cannot be allocated, each chunk is selected again and
+ * its rows placed block by block.  The lists are the same either way.
  * Synchronises the stream. */
 gmm_status gmm_soft_assign(gmm_ctx *ctx, const float *X /*[dev]*/, int64_t N, int64_t ldx,
                            const float *weights, const float *means, const float *vars /*[dev]*/,

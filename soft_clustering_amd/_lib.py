@@ -27,7 +27,7 @@ PREC_REFINED, PREC_FP32, PREC_FP64 = 0, 1, 2
 MFMA_SPLIT_BF16, MFMA_SPLIT_LOGITS, MFMA_FP32 = 0, 1, 2
 
 EXPORTS = ["gmm_create", "gmm_destroy", "gmm_last_error", "gmm_workspace_bytes", "gmm_set_path", "gmm_set_precision",
-           "gmm_set_mfma", "gmm_split_level",
+           "gmm_set_mfma", "gmm_split_level", "gmm_set_assign_limit",
            "gmm_init", "gmm_estep_stats", "gmm_mstep", "gmm_fit", "gmm_soft_assign", "gmm_check",
            "gmm_init_iso", "gmm_estep_stats_iso", "gmm_mstep_iso", "gmm_fit_iso", "gmm_kmeans", "gmm_init_kmeans",
            "gmm_estep_stats_host", "gmm_fit_host",
@@ -53,6 +53,7 @@ def _load():
         "gmm_set_path": (i32, [vp, i32]),
         "gmm_set_precision": (i32, [vp, i32]),
         "gmm_set_mfma": (i32, [vp, i32]),
+        "gmm_set_assign_limit": (i32, [vp, i64]),
         "gmm_split_level": (i32, [vp, i32]),
         "gmm_init": (i32, [vp, vp, i64, i64, vp, f32, vp, vp, vp]),
         "gmm_estep_stats": (i32, [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, i32]),
@@ -199,6 +200,11 @@ class GMM:
 
     def set_mfma(self, kind: int):
         self._check(_lib.gmm_set_mfma(self._h, int(kind)))
+
+    def set_assign_limit(self, nbytes: int):
+        """Device memory soft_assign may hold beyond the workspace (kept
+        selections, list-sort buffer); 0 = none (chunked list building)."""
+        self._check(_lib.gmm_set_assign_limit(self._h, int(nbytes)))
 
     def split_level(self, model: int = 0) -> int:
         """0 fp32 MFMA, 1 split-bf16 logits, 2 split-bf16 logits and

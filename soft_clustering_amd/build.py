@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libflashgmm.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["gmm_kernels.hip", "gmm_assign.hip", "gmm_api.hip"]
+SOURCES = ["gmm_kernels.hip", "gmm_assign.hip", "gmm_lists.hip", "gmm_api.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

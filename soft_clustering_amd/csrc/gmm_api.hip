@@ -14,8 +14,9 @@
 #include "flashgmm.h"
 #include "gmm_internal.h"
 
-// largest buffer the soft assignment holds for the selections of all rows
-constexpr size_t kSelKeepBytes = (size_t)4 << 30;
+// default limit of the soft assignment's own buffers (the selections of all
+// rows and the radix-sort buffer that builds the lists from them)
+constexpr int64_t kAssignLimitDefault = (int64_t)20 << 30;
 
 struct gmm_ctx {
   int device = 0;
@@ -44,6 +45,9 @@ struct gmm_ctx {
   // kSelKeepBytes)
   int32_t* selkeep = nullptr;
   size_t selkeep_bytes = 0;
+  void* sortbuf = nullptr;  // list sort (grown on demand)
+  size_t sortbuf_bytes = 0;
+  int64_t assign_limit = kAssignLimitDefault;  // bytes of selkeep + sortbuf (gmm_set_assign_limit)
 };
 
 namespace {
@@ -296,6 +300,7 @@ void gmm_destroy(gmm_ctx* ctx) {
   }
   if (ctx->copy_stream) hipStreamDestroy(ctx->copy_stream);
   if (ctx->selkeep) hipFree(ctx->selkeep);
+  if (ctx->sortbuf) hipFree(ctx->sortbuf);
   delete ctx;
 }
 
@@ -360,6 +365,25 @@ gmm_status gmm_set_mfma(gmm_ctx* ctx, int32_t kind) {
   if (kind != GMM_MFMA_SPLIT_BF16 && kind != GMM_MFMA_SPLIT_LOGITS && kind != GMM_MFMA_FP32)
     return fail(ctx, GMM_ERR_INVALID_ARG, "unknown matrix instruction kind %d", kind);
   ctx->ws.split = (kind == GMM_MFMA_SPLIT_BF16) ? 2 : (kind == GMM_MFMA_SPLIT_LOGITS) ? 1 : 0;
+  return GMM_OK;
+}
+
+gmm_status gmm_set_assign_limit(gmm_ctx* ctx, int64_t bytes) {
+  if (!ctx) return GMM_ERR_INVALID_ARG;
+  if (bytes < 0) return fail(ctx, GMM_ERR_INVALID_ARG, "bytes must be >= 0");
+  hipError_t e = hipStreamSynchronize(ctx->stream);  // the buffers may still be read
+  if (e != hipSuccess) return hip_fail(ctx, e, "stream synchronize");
+  ctx->assign_limit = bytes;
+  if (ctx->selkeep && (int64_t)ctx->selkeep_bytes > bytes) {
+    hipFree(ctx->selkeep);
+    ctx->selkeep = nullptr;
+    ctx->selkeep_bytes = 0;
+  }
+  if (ctx->sortbuf && (int64_t)ctx->sortbuf_bytes > bytes) {
+    hipFree(ctx->sortbuf);
+    ctx->sortbuf = nullptr;
+    ctx->sortbuf_bytes = 0;
+  }
   return GMM_OK;
 }
 
@@ -567,12 +591,14 @@ gmm_status soft_assign_run(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx,
   if (e != hipSuccess) return hip_fail(ctx, e, "soft assignment set-up");
   const int64_t CH = p.assignChunk;
   // Where the input spans several chunks, the selections of all rows are
-  // kept from the counting sweep (N x (1 + max_extra) ints, up to
-  // kSelKeepBytes) so that the scatter needs no second logit sweep; if that
-  // buffer cannot be had, every chunk is selected again before its scatter.
+  // kept from the counting sweep (N x (1 + max_extra) ints, within the
+  // context's assignment limit) so that the lists need no second logit sweep;
+  // if that buffer cannot be had, every chunk is selected again before its
+  // scatter.
   const size_t keep_bytes = (size_t)N * (size_t)(1 + max_extra) * sizeof(int32_t);
+  const size_t limit = (size_t)ctx->assign_limit;
   bool keep = N <= CH;
-  if (!keep && keep_bytes <= kSelKeepBytes) {
+  if (!keep && keep_bytes <= limit) {
     if (ctx->selkeep_bytes < keep_bytes) {
       e = hipStreamSynchronize(s);  // the old buffer may still be read
       if (e != hipSuccess) return hip_fail(ctx, e, "soft assignment set-up");
@@ -609,7 +635,32 @@ gmm_status soft_assign_run(gmm_ctx* ctx, const float* X, int64_t N, int64_t ldx,
   if (chk != GMM_OK) return chk;
   if (total > ids_capacity)
     return fail(ctx, GMM_ERR_CAPACITY, "ids_capacity %lld < nnz %lld", (long long)ids_capacity, (long long)total);
-  // pass B: place rows into the lists in row order
+  // pass B: place rows into the lists in row order.  With every row's
+  // selections at hand, one stable sort of (list, row) pairs does it;
+  // otherwise (or without the sort buffer) chunk by chunk
+  const size_t held = (N <= CH) ? 0 : keep_bytes;  // the kept selections count against the limit
+  if (keep) {
+    const size_t need = gmm::sort_lists_bytes(N * stride, p.K);
+    const bool fits = need > 0 && held + need <= limit;
+    if (fits && ctx->sortbuf_bytes < need) {
+      e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return hip_fail(ctx, e, "soft assignment");
+      if (ctx->sortbuf) hipFree(ctx->sortbuf);
+      ctx->sortbuf = nullptr;
+      ctx->sortbuf_bytes = 0;
+      if (hipMalloc(&ctx->sortbuf, need) == hipSuccess)
+        ctx->sortbuf_bytes = need;
+      else
+        (void)hipGetLastError();  // not fatal: the chunked scatter runs
+    }
+    if (fits && ctx->sortbuf && ctx->sortbuf_bytes >= need) {
+      e = gmm::sort_lists(chunk_sel(0), N, stride, p.K, list_ids, total, ctx->sortbuf, ctx->sortbuf_bytes, s);
+      if (e != hipSuccess) return hip_fail(ctx, e, "list sort");
+      e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return hip_fail(ctx, e, "soft assignment");
+      return gmm_check(ctx);
+    }
+  }
   for (int64_t r0 = 0; r0 < N; r0 += CH) {
     const int64_t rows = (N - r0 < CH) ? N - r0 : CH;
     if (!keep) {

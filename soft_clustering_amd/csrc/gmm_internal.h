@@ -141,5 +141,11 @@ hipError_t launch_assign_select(const Plan& p, const Workspace& w, const float* 
 hipError_t launch_assign_offsets(const Plan& p, const Workspace& w, int64_t* offsets, hipStream_t s);
 hipError_t launch_assign_scatter(const Plan& p, const Workspace& w, const int32_t* sel, int64_t row0, int64_t rows,
                                  int max_extra, const int64_t* offsets, int32_t* ids, hipStream_t s);
+// The lists from the selections of all rows at once (gmm_lists.hip): a stable
+// radix sort of (list, row) pairs.  sort_lists_bytes: the buffer it needs for
+// n = rows * stride selection slots (0 if the size query fails).
+size_t sort_lists_bytes(int64_t n, int K);
+hipError_t sort_lists(const int32_t* sel, int64_t rows, int stride, int K, int32_t* ids, int64_t nnz, void* buf,
+                      size_t bytes, hipStream_t s);
 
 }  // namespace gmm

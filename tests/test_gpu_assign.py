@@ -194,7 +194,7 @@ def test_soft_assign_all_components_tied(D, m, mfma):
     window and clear the candidate bound, so every component group of every
     wave overflows the one-pass refinement and candidate lists (256 entries
     each) and runs the batched branches.  The oracle's lists on the same
-    input agree (its responsibilities are also exactly tied)."""
+    input agree."""
     from soft_clustering_amd import MFMA_FP32
     K, N = 512, 3_001
     thr = 0.5 / K
@@ -220,9 +220,11 @@ def test_soft_assign_all_components_tied(D, m, mfma):
 
 
 def test_soft_assign_chunks_compose():
-    """Rows past the first 2^19-row chunk go through the second selection
-    pass and the list cursors: the lists of X equal the lists of its two
-    halves, the second's row ids shifted."""
+    """Rows past the first 2^19-row chunk: the lists of X equal the lists of
+    its two halves, the second's row ids shifted, whichever way they are
+    built: the default (selections kept, one stable sort of (list, row)
+    pairs) and, with the assignment limit at 0, chunk by chunk (each chunk
+    selected again, rows placed block by block through the list cursors)."""
     N1, N2, D, K = (1 << 19), 3_001, 16, 64
     log(f"soft_assign chunking: N={N1 + N2} D={D} K={K}")
     mix = datagen.mixture("tiny", D, K, seed=3)
@@ -236,11 +238,18 @@ def test_soft_assign_chunks_compose():
     off, ids = g.soft_assign(X, w, mu, var, 0.1, 3)
     offa, idsa = g.soft_assign(X[:N1], w, mu, var, 0.1, 3)
     offb, idsb = g.soft_assign(X[N1:], w, mu, var, 0.1, 3)
-    off, ids, offa, idsa, offb, idsb = (t.cpu().numpy() for t in (off, ids, offa, idsa, offb, idsb))
+    g.set_assign_limit(0)
+    offc, idsc = g.soft_assign(X, w, mu, var, 0.1, 3)
+    offd, idsd = g.soft_assign(X[:N1], w, mu, var, 0.1, 3)
+    off, ids, offa, idsa, offb, idsb, offc, idsc, offd, idsd = (
+        t.cpu().numpy() for t in (off, ids, offa, idsa, offb, idsb, offc, idsc, offd, idsd))
     assert np.array_equal(off, offa + offb)
     for k in range(K):
         want = np.concatenate((idsa[offa[k]:offa[k + 1]], idsb[offb[k]:offb[k + 1]] + N1))
         assert np.array_equal(ids[off[k]:off[k + 1]], want), f"list {k}"
+    assert np.array_equal(offc, off) and np.array_equal(idsc, ids), "chunked lists differ from the sorted ones"
+    assert np.array_equal(offd, offa) and np.array_equal(idsd, idsa), "one-chunk lists differ without the sort"
+    g.close()
 
 
 def test_soft_assign_deterministic_and_capacity():
