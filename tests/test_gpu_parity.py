@@ -243,6 +243,35 @@ def test_bit_identical_reruns_and_paths_agree(name):
         assert not errs, "\n".join(errs)
 
 
+@pytest.mark.parametrize("name", ["mid_prefix", "tiny"])
+def test_fit_resumes_bit_for_bit(name):
+    """A fit interrupted after T1 iterations and resumed from the float32
+    parameters it returned gives the same parameters and log-likelihood
+    history as T iterations in one call, bit for bit: an iteration depends
+    only on the parameters entering it (checkpoint / resume needs nothing
+    else)."""
+    from soft_clustering_amd import GMM
+    Xn, Xg, params, _, floor = case_data(name)
+    N, D = Xn.shape
+    K = params[1].shape[0]
+    T, T1 = 6, 2
+    log(f"[resume] case={name} T={T} T1={T1}")
+    g = GMM(K, D)
+    w, mu, var = gpu_params(params)
+    _, _, _, hist = g.fit(Xg, w, mu, var, T, floor)
+    g.check()
+    w1, mu1, var1 = gpu_params(params)
+    _, _, _, h1 = g.fit(Xg, w1, mu1, var1, T1, floor)
+    ck = [t.cpu().clone() for t in (w1, mu1, var1)]  # the checkpoint, through host memory
+    w2, mu2, var2 = (t.to(DEV) for t in ck)
+    _, _, _, h2 = g.fit(Xg, w2, mu2, var2, T - T1, floor)
+    g.check()
+    for a, b, what in ((w, w2, "weights"), (mu, mu2, "means"), (var, var2, "variances")):
+        assert torch.equal(a, b), f"{what} differ after resuming"
+    assert torch.equal(hist, torch.cat([h1, h2])), "log-likelihood history differs after resuming"
+    g.close()
+
+
 def test_accumulate_over_row_chunks():
     from soft_clustering_amd import GMM
     Xn, Xg, params, _, _ = case_data("d100_k300")
