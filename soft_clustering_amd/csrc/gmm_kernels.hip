@@ -212,6 +212,9 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   static_assert(!SPLIT || SH::CPR <= kWave, "split rows follow the one-instruction-per-row DMA assignment");
   constexpr int NPB = SH::NPB;
   constexpr int NFB = ISO ? DPW / 16 : SH::NFB;  // statistics feature blocks
+  // row reductions on integer keys except in the soft isotropic kernel
+  // (measured faster there with float maxima)
+  constexpr bool IK = !ISO || HARD;
   constexpr int FLUSH = (BN >= 64) ? 32 : 128;  // tiles between fp64 flushes (2048 rows)
   // row groups flush at staggered tiles, so the float64 atomics of the grid
   // do not all reach L2 at once; the members of a row group flush together
@@ -443,7 +446,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
               const float2 nn = nrm[pb * 16 + 4 * g + v];
               const float lb = fmaxf(acc[pb][0][v] - err_bound(a.kappa, co[0], co[1], co[2], nn),
                                      acc[pb][1][v] - err_bound(a.kappa, co[3], co[4], co[5], nn));
-              const float m = row16_max(lb);
+              const float m = row16_max<IK>(lb);
               if (r16 == 0) lpart[wc][pb * 16 + 4 * g + v] = m;
               if (v == 3) __builtin_amdgcn_sched_barrier(0);
             }
@@ -484,10 +487,10 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
       for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float m = row16_max(fmaxf(acc[pb][0][v], acc[pb][1][v]));
+          const float m = row16_max<IK>(fmaxf(acc[pb][0][v], acc[pb][1][v]));
           // lowest lane of the DPP row holding m, block 0 before block 1
-          const float i0 = row16_min((acc[pb][0][v] == m) ? (float)r16 : 64.f);
-          const float i1 = row16_min((acc[pb][1][v] == m) ? (float)r16 : 64.f);
+          const float i0 = row16_min<IK>((acc[pb][0][v] == m) ? (float)r16 : 64.f);
+          const float i1 = row16_min<IK>((acc[pb][1][v] == m) ? (float)r16 : 64.f);
           if (r16 == 0) {
             lpart[wc][pb * 16 + 4 * g + v] = m;
             lidx[wc][pb * 16 + 4 * g + v] = compbase + (i0 < 16.f ? (int)i0 : (i1 < 16.f ? 16 + (int)i1 : 0));
@@ -514,7 +517,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
         for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float m = row16_max(fmaxf(acc[pb][0][v], acc[pb][1][v]));
+            const float m = row16_max<IK>(fmaxf(acc[pb][0][v], acc[pb][1][v]));
             const float ms = (m == kNegInf) ? 0.f : m;
             float e = __expf(acc[pb][0][v] - ms) + __expf(acc[pb][1][v] - ms);
             e = row16_sum(e);
