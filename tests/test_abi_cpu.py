@@ -66,3 +66,22 @@ def test_gpu_required_without_device():
     from soft_clustering_amd import GMM
     with pytest.raises(RuntimeError):
         GMM(4, 4)
+
+
+def test_sanitizer_exercise_calls_every_entry_point():
+    """tests/native/abi_exercise.cpp, the host program run under AddressSanitizer
+    and UndefinedBehaviorSanitizer, reaches every function the header declares."""
+    src = open(os.path.join(ROOT, "tests", "native", "abi_exercise.cpp")).read()
+    called = set(re.findall(r"\b(gmm_[a-z_]+)\s*\(", src))
+    missing = set(header_symbols()) - called
+    assert not missing, f"not exercised: {sorted(missing)}"
+    build = open(os.path.join(ROOT, "tests", "native", "build_sanitized.sh")).read()
+    for line in build.splitlines():
+        # sanitizers on host code only: outside the host link of objects, each
+        # -fsanitize= sits behind -Xarch_host
+        code = line.split("#")[0]
+        if code.strip().startswith('"$CLANG"'):
+            assert ".hip" not in code, line
+            continue
+        for m in re.finditer(r"(\S+)\s+-fsanitize=", code):
+            assert m.group(1).endswith("-Xarch_host"), line
