@@ -95,6 +95,18 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// max(a, b) in one v_med3_f32 (the median of a, b and +inf), where fmaxf
+// first quiets both operands.  With a NaN operand the result is the other
+// operand or NaN; either way a NaN logit still reaches the row's sum of
+// exponentials and the statistics, where the numeric check reports it.
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, kPosInf); }
+
+// Natural log of a row's sum of exponentials taken relative to its largest
+// term, so s >= 1 (that term is exp(0)), or s = 0 for a row of -inf (giving
+// -inf): the hardware base-2 logarithm times ln 2, without the denormal and
+// range handling of the library logarithm, which such s never needs.
+__device__ __forceinline__ float ln_rowsum(float s) { return __builtin_amdgcn_logf(s) * 0.693147180559945309f; }
+
 // log(exp(a) + exp(b)) merge of two (max, sum) pairs; -inf safe.
 __device__ __forceinline__ void lse_merge(float& M, float& S, float m2, float s2) {
   float mn = fmaxf(M, m2);
@@ -102,9 +114,8 @@ __device__ __forceinline__ void lse_merge(float& M, float& S, float m2, float s2
   S = S * __expf(M - ms) + s2 * __expf(m2 - ms);
   M = mn;
 }
-__device__ __forceinline__ float lse_of(float M, float S) {
-  return (S > 0.f) ? ((M == kNegInf ? 0.f : M) + __logf(S)) : kNegInf;
-}
+// S >= 1 (its largest term is exp(0)) or S = 0 with M = -inf
+__device__ __forceinline__ float lse_of(float M, float S) { return (M == kNegInf ? 0.f : M) + ln_rowsum(S); }
 
 struct EArgs {
   const float* X;
@@ -219,6 +230,9 @@ __device__ __forceinline__ void stage_dma(float* __restrict__ xt, const float* _
   constexpr int IPR = (SH::CPR + 63) / 64;  // instructions per row
   constexpr int NW = SH::NT / kWave;
   const int lane = threadIdx.x & 63;
+  // the wave index is uniform: taken into a scalar register, the row
+  // addresses are scalar arithmetic and only the lane offset is per lane
+  w = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
   for (int i = w; i < BN * IPR; i += NW) {
     const int pt = i / IPR, part = i - pt * IPR;

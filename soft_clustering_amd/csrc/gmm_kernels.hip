@@ -440,16 +440,20 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
         // true logit from below, for every workgroup of the row group alike
         if (wd == 0) {
 #pragma unroll
-          for (int pb = 0; pb < NPB; ++pb)
+          for (int pb = 0; pb < NPB; ++pb) {
+            float m4[4];  // four rows, stored together
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               const float2 nn = nrm[pb * 16 + 4 * g + v];
-              const float lb = fmaxf(acc[pb][0][v] - err_bound(a.kappa, co[0], co[1], co[2], nn),
-                                     acc[pb][1][v] - err_bound(a.kappa, co[3], co[4], co[5], nn));
-              const float m = row16_max<IK>(lb);
-              if (r16 == 0) lpart[wc][pb * 16 + 4 * g + v] = m;
-              if (v == 3) __builtin_amdgcn_sched_barrier(0);
+              const float lb = max2(acc[pb][0][v] - err_bound(a.kappa, co[0], co[1], co[2], nn),
+                                    acc[pb][1][v] - err_bound(a.kappa, co[3], co[4], co[5], nn));
+              m4[v] = row16_max<IK>(lb);
             }
+            if (r16 == 0)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) lpart[wc][pb * 16 + 4 * g + v] = m4[v];
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
         __syncthreads();
         if (tid < BN) {
@@ -487,7 +491,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
       for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float m = row16_max<IK>(fmaxf(acc[pb][0][v], acc[pb][1][v]));
+          const float m = row16_max<IK>(max2(acc[pb][0][v], acc[pb][1][v]));
           // lowest lane of the DPP row holding m, block 0 before block 1
           const float i0 = row16_min<IK>((acc[pb][0][v] == m) ? (float)r16 : 64.f);
           const float i1 = row16_min<IK>((acc[pb][1][v] == m) ? (float)r16 : 64.f);
@@ -514,15 +518,22 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
     } else if constexpr (FUSED) {
       if (wd == 0) {
 #pragma unroll
-        for (int pb = 0; pb < NPB; ++pb)
+        for (int pb = 0; pb < NPB; ++pb) {
+          // four rows at a time, stored together (one branch per four rows,
+          // and the four reductions can interleave)
+          float l4[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float m = row16_max<IK>(fmaxf(acc[pb][0][v], acc[pb][1][v]));
+            const float m = row16_max<IK>(max2(acc[pb][0][v], acc[pb][1][v]));
             const float ms = (m == kNegInf) ? 0.f : m;
             float e = __expf(acc[pb][0][v] - ms) + __expf(acc[pb][1][v] - ms);
             e = row16_sum(e);
-            if (r16 == 0) lpart[wc][pb * 16 + 4 * g + v] = (e > 0.f) ? ms + __logf(e) : kNegInf;
+            l4[v] = ms + ln_rowsum(e);  // e >= 1, or 0 for a row of -inf
           }
+          if (r16 == 0)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) lpart[wc][pb * 16 + 4 * g + v] = l4[v];
+        }
       }
       __syncthreads();
       if (tid < BN) {
@@ -753,8 +764,8 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_logz(
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const float2 nn = nrm[pb * 16 + 4 * g + v];
-            const float lb = fmaxf(acc[pb][0][v] - err_bound(a.kappa, co[0], co[1], co[2], nn),
-                                   acc[pb][1][v] - err_bound(a.kappa, co[3], co[4], co[5], nn));
+            const float lb = max2(acc[pb][0][v] - err_bound(a.kappa, co[0], co[1], co[2], nn),
+                                  acc[pb][1][v] - err_bound(a.kappa, co[3], co[4], co[5], nn));
             Rlb[pb][v] = fmaxf(Rlb[pb][v], row16_max(lb));
             if (r16 == 0 && wd == 0) thrw[wc][pb * 16 + 4 * g + v] = Rlb[pb][v] - kDelta;
           }
@@ -767,7 +778,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_logz(
       for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float mn = fmaxf(M[pb][v], fmaxf(acc[pb][0][v], acc[pb][1][v]));
+          const float mn = max2(M[pb][v], max2(acc[pb][0][v], acc[pb][1][v]));
           const float ms = (mn == kNegInf) ? 0.f : mn;
           S[pb][v] = S[pb][v] * __expf(M[pb][v] - ms) + __expf(acc[pb][0][v] - ms) +
                      __expf(acc[pb][1][v] - ms);
@@ -782,7 +793,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_logz(
           const float mr = row16_max(M[pb][v]);
           const float ms = (mr == kNegInf) ? 0.f : mr;
           const float s = row16_sum(S[pb][v] * __expf(M[pb][v] - ms));
-          if (r16 == 0) lpart[wc][pb * 16 + 4 * g + v] = (s > 0.f) ? ms + __logf(s) : kNegInf;
+          if (r16 == 0) lpart[wc][pb * 16 + 4 * g + v] = ms + ln_rowsum(s);  // s >= 1, or 0
         }
     }
     __syncthreads();
