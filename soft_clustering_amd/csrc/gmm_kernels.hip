@@ -447,7 +447,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
               const float2 nn = nrm[pb * 16 + 4 * g + v];
               const float lb = max2(acc[pb][0][v] - err_bound(a.kappa, co[0], co[1], co[2], nn),
                                     acc[pb][1][v] - err_bound(a.kappa, co[3], co[4], co[5], nn));
-              m4[v] = row16_max<IK>(lb);
+              m4[v] = row16_max<IK, false>(lb);
             }
             if (r16 == 0)
 #pragma unroll
@@ -524,8 +524,9 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
           float l4[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float m = row16_max<IK>(max2(acc[pb][0][v], acc[pb][1][v]));
-            const float ms = (m == kNegInf) ? 0.f : m;
+            const float m = row16_max<IK, false>(max2(acc[pb][0][v], acc[pb][1][v]));
+            // m = -inf (a row of -inf logits) gives ms = -FLT_MAX, e = 0 and -inf
+            const float ms = max2(m, -3.40282347e38f);
             float e = __expf(acc[pb][0][v] - ms) + __expf(acc[pb][1][v] - ms);
             e = row16_sum(e);
             l4[v] = ms + ln_rowsum(e);  // e >= 1, or 0 for a row of -inf
