@@ -23,6 +23,7 @@ import numpy as np
 
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, AMD published figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, AMD published figure
+MFMA_FP64_PEAK_TFLOPS = 78.6  # MI355X dense fp64 matrix, AMD published figure
 HBM_PEAK_GBS = 8000.0
 
 # The configured workloads; the timed iterations are --steps (after --warmup
@@ -53,18 +54,26 @@ def useful_flops(N, K, D, iso=False):
     return float(N) * K * ((4 * D + 6) if iso else (8 * D + 2))
 
 
-def mfma_roofline(N, K, D, split, iso=False):
-    """Peak for the fused E-step: the rate at which the matrix pipes, fully
-    busy with this kernel's MFMA instruction mix, would deliver its useful
-    flops.  split 0: every contraction fp32 MFMA, so the fp32 peak.  The
+def mfma_roofline(N, K, D, split, iso=False, f64=False, sweeps=1):
+    """Peak for the E-step: the rate at which the matrix pipes, fully busy
+    with its MFMA instruction mix, would deliver its useful flops.  The
     logit and statistics contractions take 2*N*K*F flops each over F
-    features (F = 2D diagonal, D isotropic).  split 1: the logits are three
-    bf16 passes at the bf16 peak, the statistics fp32 at the fp32 peak.
-    split 2: the statistics are six bf16 passes too.  The peak is the useful
-    count over that busy time."""
-    if not split:
-        return MFMA_FP32_PEAK_TFLOPS, "fp32 MFMA (all contractions fp32)"
+    features (F = 2D diagonal, D isotropic); the two-sweep path (sweeps = 2)
+    contracts the logits twice.  split 0: every contraction fp32 MFMA.
+    split 1: the logits are three bf16 passes at the bf16 peak, the
+    statistics fp32 at the fp32 peak.  split 2: the statistics are six bf16
+    passes too.  f64: float64 MFMA logits at the fp64 peak, fp32 statistics.
+    The peak is the useful count over that busy time."""
     F = D if iso else 2 * D
+    if f64 or not split:
+        lpeak = MFMA_FP64_PEAK_TFLOPS if f64 else MFMA_FP32_PEAK_TFLOPS
+        t_busy = (sweeps * 2.0 * N * K * F / (lpeak * 1e12)
+                  + 2.0 * N * K * F / (MFMA_FP32_PEAK_TFLOPS * 1e12))
+        peak = useful_flops(N, K, D, iso) / t_busy / 1e12
+        return peak, (f"matrix pipes busy with this mix: logits {sweeps} time(s) over F={'D' if iso else '2D'} "
+                      f"features in {'fp64' if f64 else 'fp32'} (2*N*K*F flops each at {lpeak} TFLOP/s) + "
+                      f"statistics in fp32 (2*N*K*F at 157.3 TFLOP/s); useful N*K*({'4D+6' if iso else '8D+2'}) "
+                      f"over that time")
     bf16_passes = 3 + (6 if split == 2 else 0)
     t_busy = bf16_passes * 2.0 * N * K * F / (MFMA_BF16_PEAK_TFLOPS * 1e12)
     if split == 1:
@@ -398,7 +407,7 @@ def main():
     avg_ms = stats_ms / max(stats_n, 1)
     achieved = F / (kern_ms * 1e-3) / 1e12
     hl = hist.cpu().numpy()
-    peak, peak_basis = mfma_roofline(N, K, D, split, iso)
+    peak, peak_basis = mfma_roofline(N, K, D, split, iso, f64=args.precision == "fp64", sweeps=1 if fused else 2)
     traffic = None
     busy_cycles = None
     if fused and split == 2 and args.workload == "large" and args.precision == "refined" and not args.rows:

@@ -55,7 +55,8 @@ typedef enum {
 } gmm_status;
 
 /* Execution path of the E-step (gmm_set_path).  AUTO picks FUSED when the
- * component groups of one row tile fit the cooperative grid, else TWO_SWEEP. */
+ * component groups of one row tile fit the cooperative grid (at most 64 of
+ * them; under GMM_PREC_FP64 as many as fit), else TWO_SWEEP. */
 typedef enum {
     GMM_PATH_AUTO = 0,
     GMM_PATH_TWO_SWEEP = 1, /* Algorithm 1's two sweeps: log Z first, then
@@ -77,8 +78,7 @@ typedef enum {
  *   1e-4..1e-2 nats on data spread over many cluster widths).
  * FP64: every logit from a float64 MFMA contraction (v_mfma_f64, half the
  *   fp32 matrix rate), rounded once to fp32; for data whose responsibilities
- *   are diffuse, where REFINED would recompute a large share of the logits.
- *   Runs the two-sweep path. */
+ *   are diffuse, where REFINED would recompute a large share of the logits. */
 typedef enum {
     GMM_PREC_REFINED = 0,
     GMM_PREC_FP32 = 1,

@@ -129,7 +129,10 @@ void hook_after(void* user, int which, hipStream_t s) {
 }
 
 bool want_fused(const gmm_ctx* c) {
-  if (c->path == GMM_PATH_TWO_SWEEP || c->ws.f64) return false;  // float64 logits: two-sweep only
+  if (c->path == GMM_PATH_TWO_SWEEP) return false;
+  // float64 logits: one sweep wherever the fused kernel fits (measured 566 against 710 ms per 1e6 rows at
+  // D=768, K=4096, whose 128 component groups exceed the refined kernels' AUTO limit)
+  if (c->ws.f64) return c->plan.fused64OK != 0;
   if (c->path == GMM_PATH_FUSED) return c->plan.fusedOK != 0;
   return c->plan.fusedOK != 0 && c->plan.P <= 64;
 }
@@ -218,6 +221,11 @@ gmm_status gmm_create(gmm_ctx** out, int32_t K, int32_t D, void* hip_stream) {
     return fail(nullptr, GMM_ERR_HIP, "assignment kernel occupancy: %s", hipGetErrorString(e));
   }
   c->plan.occAssign = oa;
+  e = gmm::fused64_fits(c->plan, &c->plan.fused64OK);
+  if (e != hipSuccess) {
+    delete c;
+    return fail(nullptr, GMM_ERR_HIP, "float64 fused kernel occupancy: %s", hipGetErrorString(e));
+  }
   c->bytes = gmm::workspace_bytes(c->plan);
   e = hipMalloc(&c->base, c->bytes);
   if (e != hipSuccess) {

@@ -30,6 +30,7 @@ struct Plan {
   int SR;            // doubles per (slot, component): 2*Dp features + N_k
   int RS;            // LDS floats per tile row
   int fusedOK;       // cooperative grid can hold R*P workgroups
+  int fused64OK;     // ... and so can the float64-logit fused kernel
   int64_t chunk;     // rows per two-sweep chunk (log Z buffer length)
   size_t ldsStats, ldsLogz;
   int numCU;
@@ -81,6 +82,8 @@ struct Workspace {
 };
 
 Plan make_plan(int K, int D, int numCU, int occStats, int occLogz);
+// Whether the float64-logit fused kernel fits the plan's cooperative grid.
+hipError_t fused64_fits(const Plan& p, int* ok);
 bool plan_shape_ok(const Plan& p);
 size_t workspace_bytes(const Plan& p);
 

@@ -1380,10 +1380,10 @@ struct Kern {
   }
 };
 
-// Kernel variants of one shape, indexed by logit precision mode (the fused
-// kernel has no float64-logit variant: that mode runs the two-sweep path).
+// Kernel variants of one shape, indexed by logit precision mode (the
+// isotropic and hard-assignment kernels have no float64-logit variant).
 struct KTab {
-  void* fused[2];
+  void* fused[3];
   void* iso[2];   // fused isotropic kernels (nullptr where not built)
   void* hard[2];  // fused k-means (hard assignment) kernels
   void* split;    // fused diagonal refined kernel with split-bf16 logits (nullptr where not built)
@@ -1400,7 +1400,7 @@ static bool lookup(int WC, int WD, int DPW, KTab& t) {
 #define GMM_K(wc, wd, dpw)                                                                            \
   if (WC == wc && WD == wd && DPW == dpw) {                                                           \
     using KK = Kern<wc, wd, dpw>;                                                                     \
-    t = KTab{{KK::stats_fused<0>(), KK::stats_fused<1>()},                                             \
+    t = KTab{{KK::stats_fused<0>(), KK::stats_fused<1>(), KK::stats_fused<2>()},                       \
              {KK::stats_iso<0>(), KK::stats_iso<1>()},                                                 \
              {KK::stats_hard<0>(), KK::stats_hard<1>()},                                               \
              KK::stats_split(), KK::stats_iso_split(), KK::stats_hard_split(), KK::stats_split2(),    \
@@ -1538,6 +1538,17 @@ hipError_t occupancy(const Plan& p, int* occStats, int* occLogz) {
   return hipSuccess;
 }
 
+hipError_t fused64_fits(const Plan& p, int* ok) {
+  *ok = 0;
+  KTab t;
+  if (!lookup(p.WC, p.WD, p.DPW, t)) return hipErrorInvalidValue;
+  int occ = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)t.fused[2], 64 * p.WC * p.WD, 0);
+  if (e != hipSuccess) return e;
+  *ok = (p.fusedOK && (int64_t)occ * p.numCU >= (int64_t)p.G) ? 1 : 0;
+  return hipSuccess;
+}
+
 static int grid_for(size_t total, int block) {
   size_t g = (total + block - 1) / block;
   if (g > 65535 * 4) g = 65535 * 4;
@@ -1643,7 +1654,7 @@ hipError_t launch_estep(const Plan& p, const Workspace& w, const float* X, int64
   const int nt = 64 * p.WC * p.WD;
   EArgs a = make_args(p, w, X, ldx);
   const int mode = w.f64 ? 2 : (w.refine ? 1 : 0);
-  if (fused && mode == 2) return hipErrorInvalidValue;  // no fused float64-logit kernel
+  if (fused && mode == 2 && variant != 0) return hipErrorInvalidValue;  // diagonal kernel only
   if (fused) {
     a.row0 = 0;
     a.nrows = N;

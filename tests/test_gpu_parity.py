@@ -66,14 +66,14 @@ def gpu_params(params):
 
 
 @pytest.mark.parametrize("path", ["fused", "fused_split_logits", "fused_fp32mfma", "fused_wc4", "two_sweep",
-                                  "two_sweep_fp64"])
+                                  "two_sweep_fp64", "fused_fp64"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_estep_parity(name, path, monkeypatch):
     """fused: the default fused kernel (8-wave workgroups where K allows;
     split-bfloat16 logits and statistics for D <= 128); fused_split_logits:
     split logits, fp32 statistics; fused_fp32mfma: fp32 MFMA for both;
-    fused_wc4: 4-wave workgroups, two per CU; two_sweep_fp64: float64 MFMA
-    logits (GMM_PREC_FP64)."""
+    fused_wc4: 4-wave workgroups, two per CU; two_sweep_fp64 / fused_fp64:
+    float64 MFMA logits (GMM_PREC_FP64) on either path."""
     from soft_clustering_amd import GMM, MFMA_FP32, MFMA_SPLIT_LOGITS, PATH_FUSED, PATH_TWO_SWEEP, PREC_FP64
     if path == "fused_wc4":
         monkeypatch.setenv("FLASHGMM_WC", "4")
@@ -92,11 +92,17 @@ def test_estep_parity(name, path, monkeypatch):
         g.set_mfma(MFMA_FP32)
     if path == "fused_split_logits":
         g.set_mfma(MFMA_SPLIT_LOGITS)
-    want_level = 0 if (path.startswith("two_sweep") or path == "fused_fp32mfma" or D > 128) else \
+    want_level = 0 if (path.startswith("two_sweep") or path in ("fused_fp32mfma", "fused_fp64") or D > 128) else \
         (1 if path == "fused_split_logits" else 2)
     assert g.split_level(0) == want_level
+    if path == "fused_fp64":
+        g.profile(True)
     got = g.estep_stats(Xg, *gpu_params(params))
     g.check()
+    if path == "fused_fp64":
+        _, n_stats, _, n_logz = g.profile_read()
+        g.profile(False)
+        assert (n_stats, n_logz) == (1, 0), "the float64-logit fused kernel did not run"
     got = [t.cpu().numpy() for t in got]
     want = O.estep_stats(Xn, *params, method=method_for(N, D, K))
     ms, rms = data_scales(Xn)
