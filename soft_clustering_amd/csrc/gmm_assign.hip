@@ -144,7 +144,7 @@ __global__ void __launch_bounds__(kWave* WC* WD) k_assign(EArgs a, AArgs s) {
       const int compbase = cg * 32;
       f4 acc[NPB][2];
       if constexpr (F64) {
-        logits_f64<SH, WC, WD, DPW>(xt, wop_block(a.wop64, compbase >> 4, WD, wd, DPW),
+        logits_f64<SH, WC, WD, DPW>(xt + wd * DPW, wop_block(a.wop64, compbase >> 4, WD, wd, DPW),
                                     wop_block(a.wop64, (compbase >> 4) + 1, WD, wd, DPW),
                                     wd == 0 ? a.cvec64[compbase + r16] : 0.0,
                                     wd == 0 ? a.cvec64[compbase + 16 + r16] : 0.0, acc, red64, lane, wc, wd);

@@ -169,7 +169,10 @@ struct Shape {
   // refinement phases then overlap the other workgroup's MFMA work), one
   // otherwise.
   static constexpr int WGS_PER_CU = (WC * WD == 4) ? 2 : 1;
-  static constexpr int RED = (WD > 1) ? WD * WC * NPB * 8 * kWave : 1;  // partial-logit exchange
+  // partial-logit exchange across the dim-segment waves, one 16-row block per
+  // pass (the blocks of a tile go through it in turn): WD partials of 8 values
+  // per lane, then the reduced values of every block (as float32)
+  static constexpr int RED = (WD > 1) ? (WD + NPB) * WC * 8 * kWave : 1;
   static constexpr int NBUF = (TILE * 8 + RED * 4 <= (WGS_PER_CU == 1 ? 140 : 68) * 1024) ? 2 : 1;
   static constexpr int HALF = DPW / 2;
   // refinement: the WD waves of a component group share the float64 passes
@@ -247,6 +250,53 @@ __device__ __forceinline__ void stage_dma(float* __restrict__ xt, const float* _
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)(xt + pt * SH::RS + part * 256), 16,
                                        0, 0);
+    }
+  }
+}
+
+// Segment-major staging: wave wd loads dims [wd * DPW, (wd + 1) * DPW) of rows
+// [r0, r0 + BN) into its own block of LDS, row p of the block at p * SRS
+// (SRS = DPW + 4: the pad keeps 16 rows of an MFMA operand load on distinct
+// banks).  By LDS DMA, 16 bytes per lane, each instruction filling 1 KiB of
+// the block (a pad slot loads the row's first chunk again), rows past `rows`
+// repeating the last row; or through registers (any D: dims past D and rows
+// past `rows` zero).  Only the wave itself reads the block, so its own wait
+// makes it usable.
+template <int DPW, int BN>
+__device__ __forceinline__ void stage_seg(float* __restrict__ blk, const float* __restrict__ X, int64_t ldx,
+                                          int64_t r0, int rows, int D, int wd, bool dma) {
+  constexpr int SRS = DPW + 4;
+  constexpr int CH = SRS / 4;         // 16-byte slots per block row (the last is pad)
+  constexpr int UNITS = BN * CH;      // slots per block
+  const int lane = threadIdx.x & 63;
+  const int d0 = wd * DPW;
+  if (dma) {
+#pragma unroll
+    for (int i = 0; i < (UNITS + 63) / 64; ++i) {
+      const int u = i * 64 + lane;
+      if (u < UNITS) {
+        const int pt = u / CH, c = u - pt * CH;
+        const int row = pt < rows ? pt : rows - 1;
+        const float* src = X + (r0 + row) * ldx + d0 + (c < CH - 1 ? c * 4 : 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(blk + i * 256), 16, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll 4
+    for (int u = lane; u < UNITS; u += 64) {
+      const int pt = u / CH, c = u - pt * CH;
+      const int d = d0 + c * 4;
+      f4 x = {0.f, 0.f, 0.f, 0.f};
+      if (c < CH - 1 && pt < rows && d < D) {
+        const float* src = X + (r0 + pt) * ldx + d;
+        if (d + 4 <= D) {
+          x = __builtin_nontemporal_load(reinterpret_cast<const f4*>(src));
+        } else {
+          for (int q = 0; q < D - d; ++q) x[q] = src[q];
+        }
+      }
+      *reinterpret_cast<f4*>(blk + u * 4) = x;
     }
   }
 }
@@ -639,27 +689,31 @@ template <class SH, int WC, int WD>
 __device__ __forceinline__ void reduce_partial_logits(float* __restrict__ red, f4 (&acc)[SH::NPB][2],
                                                       int lane, int wc, int wd) {
   if constexpr (WD > 1) {
-    constexpr int PER = SH::NPB * 8;  // floats per lane
+    // wave wd sums values e = wd, wd + WD, ... of the 8 per lane over the WD
+    // partials (in wave order) and posts the float32 sum; every wave then
+    // reads the 8 sums it needs
+    constexpr int PER = 8;  // values per lane and 16-row block
     float* mine = red + ((wd * WC + wc) * PER) * kWave + lane;
+    float* sums = red + WD * WC * PER * kWave;
 #pragma unroll
-    for (int pb = 0; pb < SH::NPB; ++pb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) mine[((pb * 2 + cb) * 4 + v) * kWave] = acc[pb][cb][v];
-    __syncthreads();
-#pragma unroll
-    for (int pb = 0; pb < SH::NPB; ++pb)
+    for (int pb = 0; pb < SH::NPB; ++pb) {
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float s = 0.f;
+        for (int v = 0; v < 4; ++v) mine[(cb * 4 + v) * kWave] = acc[pb][cb][v];
+      __syncthreads();
+      for (int e = wd; e < PER; e += WD) {
+        float s = 0.f;
 #pragma unroll
-          for (int k = 0; k < WD; ++k) s += red[((k * WC + wc) * PER + (pb * 2 + cb) * 4 + v) * kWave + lane];
-          acc[pb][cb][v] = s;
-        }
-    __syncthreads();
+        for (int k = 0; k < WD; ++k) s += red[((k * WC + wc) * PER + e) * kWave + lane];
+        sums[((pb * WC + wc) * PER + e) * kWave + lane] = s;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[pb][cb][v] = sums[((pb * WC + wc) * PER + cb * 4 + v) * kWave + lane];
+    }
   }
 }
 
@@ -674,17 +728,18 @@ __device__ __forceinline__ const T* wop_block(const T* wop, int cb16, int WD, in
 // row g + 4v of the 16x16 result in lane g*16 + column, register v (the f32
 // one puts row 4g + v there), so A's row r takes point 4 (r % 4) + r / 4 and
 // the registers come out in the f32 point order.  With WD > 1 the dim-segment partials are
-// summed in a fixed order through LDS (red64: WD*WC*NPB*8*64 doubles).  The
-// result, (c_k - C) + sum, is rounded once to float32 into acc.
-template <class SH, int WC, int WD, int DPW>
-__device__ __forceinline__ void logits_f64(const float* __restrict__ xt, const double* __restrict__ w0,
+// summed in a fixed order through LDS (red64: WD*WC*8*64 doubles, one 16-row block at a time).  The
+// result, (c_k - C) + sum, is rounded once to float32 into acc.  xw is the
+// wave's dim segment of tile row 0, rows RSX floats apart.
+template <class SH, int WC, int WD, int DPW, int RSX = SH::RS>
+__device__ __forceinline__ void logits_f64(const float* __restrict__ xw, const double* __restrict__ w0,
                                            const double* __restrict__ w1, double c0, double c1,
                                            f4 (&acc)[SH::NPB][2], double* __restrict__ red64, int lane, int wc,
                                            int wd) {
   const int g = lane >> 4, r16 = lane & 15;
   const bool sq = (g & 1) == 0;
   const int prow = 4 * (r16 & 3) + (r16 >> 2);
-  const float* arow = xt + prow * SH::RS + wd * DPW + (g >> 1) * SH::HALF;
+  const float* arow = xw + prow * RSX + (g >> 1) * SH::HALF;
   constexpr int S4 = DPW / 8;
   d4 p[SH::NPB][2];
 #pragma unroll
@@ -698,7 +753,7 @@ __device__ __forceinline__ void logits_f64(const float* __restrict__ xt, const d
     const d4 b1 = *reinterpret_cast<const d4*>(w1 + (s4 * kWave + lane) * 4);
 #pragma unroll
     for (int pb = 0; pb < SH::NPB; ++pb) {
-      const f4 a = *reinterpret_cast<const f4*>(arow + pb * 16 * SH::RS + s4 * 4);
+      const f4 a = *reinterpret_cast<const f4*>(arow + pb * 16 * RSX + s4 * 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const double x = (double)a[i];
@@ -709,34 +764,39 @@ __device__ __forceinline__ void logits_f64(const float* __restrict__ xt, const d
     }
   }
   if constexpr (WD > 1) {
-    constexpr int PER = SH::NPB * 8;  // doubles per lane
+    // as reduce_partial_logits: wave wd sums values e = wd, wd + WD, ... over
+    // the WD partials in float64 (in wave order), rounds the sum once to
+    // float32 and posts it; every wave then reads the 8 sums it needs
+    constexpr int PER = 8;  // values per lane and 16-row block
     double* mine = red64 + ((wd * WC + wc) * PER) * kWave + lane;
+    float* sums = reinterpret_cast<float*>(red64 + WD * WC * PER * kWave);
+#pragma unroll
+    for (int pb = 0; pb < SH::NPB; ++pb) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) mine[(cb * 4 + v) * kWave] = p[pb][cb][v];
+      __syncthreads();
+      for (int e = wd; e < PER; e += WD) {
+        double t = 0.0;
+#pragma unroll
+        for (int k = 0; k < WD; ++k) t += red64[((k * WC + wc) * PER + e) * kWave + lane];
+        sums[((pb * WC + wc) * PER + e) * kWave + lane] = (float)t;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[pb][cb][v] = sums[((pb * WC + wc) * PER + cb * 4 + v) * kWave + lane];
+    }
+  } else {
 #pragma unroll
     for (int pb = 0; pb < SH::NPB; ++pb)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) mine[((pb * 2 + cb) * 4 + v) * kWave] = p[pb][cb][v];
-    __syncthreads();
-#pragma unroll
-    for (int pb = 0; pb < SH::NPB; ++pb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          double t = 0.0;
-#pragma unroll
-          for (int k = 0; k < WD; ++k) t += red64[((k * WC + wc) * PER + (pb * 2 + cb) * 4 + v) * kWave + lane];
-          p[pb][cb][v] = t;
-        }
-    __syncthreads();
+        for (int v = 0; v < 4; ++v) acc[pb][cb][v] = (float)p[pb][cb][v];
   }
-#pragma unroll
-  for (int pb = 0; pb < SH::NPB; ++pb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[pb][cb][v] = (float)p[pb][cb][v];
 }
 
 // ---------------------------------------------------------------------------

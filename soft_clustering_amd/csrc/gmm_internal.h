@@ -13,7 +13,10 @@ constexpr int kNumXCD = 8;         // MI355X: 8 accelerator complex dies
 
 // Rows per tile: 64 while a row's features fit one 128-dim wave segment set,
 // 16 for wide rows (their tiles would not fit LDS).
-constexpr int bn_for(int WD, int DPW) { return WD * DPW <= 128 ? 64 : 16; }
+// D > 128 (eight dim-segment waves): 32 rows up to D = 768, two 16-row MFMA
+// blocks per wave, so each W operand a wave loads serves 32 rows; wider rows
+// take 16-row tiles (a 32-row tile of 1024 dims would not fit LDS)
+constexpr int bn_for(int WD, int DPW) { return WD * DPW <= 128 ? 64 : WD * DPW <= 768 ? 32 : 16; }
 
 // Shape of the E-step kernels, chosen once per context from (K, D).
 //   WC comp groups x WD dim segments = waves per workgroup.

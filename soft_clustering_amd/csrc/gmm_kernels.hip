@@ -67,14 +67,17 @@ __device__ __forceinline__ void xgather(const EArgs& a, int rg, int j, int rd, f
   const int tid = threadIdx.x;
   const unsigned tag = (unsigned)(j + 1);
   const unsigned long long* xb = a.xbuf + ((size_t)((rg * 2 + rd) * 2 + (j & 1)) * a.P) * BN;
+  // The 32-row tiles of the eight-wave (D > 128) kernels have many peers per
+  // gathering lane: their words are loaded QB at a time, so the round trips
+  // overlap; the 64-row kernels (few peers per lane, no registers to spare)
+  // load one at a time.  Either way the words merge in ascending peer order.
+  constexpr int QB = (BN <= 32) ? 8 : 1;
   if (tid < QP * BN) {
     const int pt = tid % BN, qp = tid / BN;
     float M = kNegInf, S = 0.f;
-    for (int q = qp; q < a.P; q += QP) {
-      const unsigned long long* src = xb + (size_t)q * BN + pt;
-      unsigned long long word = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // Bounded wait: a peer that never publishes (impossible while all
-      // workgroups are co-resident) ends in flags[1] and a drained grid.
+    // Bounded wait: a peer that never publishes (impossible while all
+    // workgroups are co-resident) ends in flags[1] and a drained grid.
+    auto settle = [&](const unsigned long long* src, unsigned long long word) {
       for (int spins = 0; (unsigned)(word >> 32) != tag; ++spins) {
         if ((spins & 255) == 0 && __hip_atomic_load(&a.flags[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
           break;
@@ -90,6 +93,27 @@ __device__ __forceinline__ void xgather(const EArgs& a, int rg, int j, int rd, f
         lse_merge(M, S, val, 1.f);
       else
         M = fmaxf(M, val);
+    };
+    if constexpr (QB == 1) {
+      for (int q = qp; q < a.P; q += QP) {
+        const unsigned long long* src = xb + (size_t)q * BN + pt;
+        settle(src, __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      }
+    } else {
+      for (int q0 = qp; q0 < a.P; q0 += QB * QP) {
+        unsigned long long wv[QB];
+#pragma unroll
+        for (int i = 0; i < QB; ++i) {
+          const int q = q0 + i * QP;
+          wv[i] = (q < a.P) ? __hip_atomic_load(xb + (size_t)q * BN + pt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                            : 0ull;
+        }
+#pragma unroll
+        for (int i = 0; i < QB; ++i) {
+          const int q = q0 + i * QP;
+          if (q < a.P) settle(xb + (size_t)q * BN + pt, wv[i]);
+        }
+      }
     }
     exm[qp][pt] = M;
     exs[qp][pt] = S;
@@ -206,7 +230,15 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   // behind the statistics phase instead of behind the whole tile)
   static_assert(SPLIT < 2 || BN % 32 == 0, "split statistics: 32-row pairs");
   using SST = StatSplit<SH, DPW, ISO>;
-  constexpr int NB = (SPLIT == 2) ? 1 : SH::NBUF;
+  // SEG: the float64-logit fused kernel with dim-segment waves keeps the tile
+  // segment-major (wave wd's dims of all rows in a block of its own, rows SRS
+  // floats apart), since in that kernel a wave reads only its own dims: each
+  // wave stages its next block right after its own statistics, with no
+  // workgroup barrier between tiles
+  constexpr bool SEG = F64 && FUSED && WD > 1;
+  constexpr int SRS = SEG ? DPW + 4 : SH::RS;  // LDS floats between a wave's rows
+  constexpr int TILEX = SEG ? WD * BN * SRS : SH::TILE;
+  constexpr int NB = (SPLIT == 2 || SEG) ? 1 : SH::NBUF;
   constexpr int XSB = (SPLIT == 0) ? 8
                       : (SPLIT == 2 && SST::SIZE > BN * SPR::XSR) ? SST::SIZE : BN * SPR::XSR;
   static_assert(!SPLIT || SH::CPR <= kWave, "split rows follow the one-instruction-per-row DMA assignment");
@@ -215,14 +247,14 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   // row reductions on integer keys except in the soft isotropic kernel
   // (measured faster there with float maxima)
   constexpr bool IK = !ISO || HARD;
-  constexpr int FLUSH = (BN >= 64) ? 32 : 128;  // tiles between fp64 flushes (2048 rows)
+  constexpr int FLUSH = 2048 / BN;  // tiles between fp64 flushes (2048 rows)
   // row groups flush at staggered tiles, so the float64 atomics of the grid
   // do not all reach L2 at once; the members of a row group flush together
   // (a flush delays the member's next exchange word, so staggering within a
   // row group would hold the whole group up once per member)
   constexpr int QP = (SH::NT / BN) > 0 ? (SH::NT / BN) : 1;
 
-  __shared__ __attribute__((aligned(16))) float xt[NB][SH::TILE];
+  __shared__ __attribute__((aligned(16))) float xt[NB][TILEX];
   __shared__ __attribute__((aligned(16))) float red[F64 ? 1 : SH::RED];
   __shared__ double red64[F64 ? SH::RED : 1];
   __shared__ __attribute__((aligned(16))) float lzt[BN];
@@ -343,7 +375,10 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
   auto stage_now = [&](float* buf, int tile) {
     const int64_t r0 = (int64_t)tile * BN;
     const int rws = (int)min((int64_t)BN, a.nrows - r0);
-    if (a.dma) {
+    if constexpr (SEG) {
+      stage_seg<DPW, BN>(buf + wd * BN * SRS, a.X, a.ldx, a.row0 + r0, rws, a.D, wd, a.dma != 0);
+      if (a.dma) dma_wait();
+    } else if (a.dma) {
       stage_dma<SH>(buf, a.X, a.ldx, a.row0 + r0, rws);
       dma_wait();
     } else {
@@ -382,7 +417,8 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
     // ---- logits
     f4 acc[NPB][2];
     if constexpr (F64) {
-      logits_f64<SH, WC, WD, DPW>(xt[cur], w0d, w1d, c0d, c1d, acc, red64, lane, wc, wd);
+      logits_f64<SH, WC, WD, DPW, SRS>(xt[cur] + (SEG ? wd * BN * SRS : wd * DPW), w0d, w1d, c0d, c1d, acc, red64,
+                                       lane, wc, wd);
     } else {
       // diagonal kernel with split statistics: the per-lane constants are
       // reloaded each tile (through an index the compiler cannot hoist), so
@@ -569,7 +605,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
     // 4g + v of each 16-point block: offsets from xs are compile-time except
     // for DPW = 16, whose 8-dim halves split a 16-lane block
     constexpr bool NARROW = !ISO && SH::HALF < 16;
-    const float* xs = xt[cur] + wd * DPW + (NARROW ? (r16 & 7) : r16) + 4 * g * SH::RS;
+    const float* xs = xt[cur] + (SEG ? wd * BN * SRS : wd * DPW) + (NARROW ? (r16 & 7) : r16) + 4 * g * SRS;
     auto fdim = [&](int fb) {  // dim offset of feature block fb (minus the lane part)
       if constexpr (ISO) return fb * 16;
       else if constexpr (NARROW) return fb * 8;
@@ -581,7 +617,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
       else return ((fb * 16 / SH::HALF) & 1) == 0;
     };
     auto bload = [&](int fb, int pt) {
-      const float x = xs[pt * SH::RS + fdim(fb)];
+      const float x = xs[pt * SRS + fdim(fb)];
       return fsq(fb) ? x * x : x;
     };
     // responsibilities in place (the logits are not needed afterwards), so
@@ -649,6 +685,19 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_stats
         split_rows<SH, DPW, ISO>(xt[0], xsb, w, NORMS_IN_SPLIT ? nrm : nullptr);
         __syncthreads();
       }
+      continue;
+    }
+    if constexpr (SEG) {
+      // the wave's own block is free once its own statistics are issued (their
+      // operand reads have returned); no other wave reads it.  Every LDS word
+      // other waves share is next written behind a barrier of the next tile
+      // that this wave only reaches after its statistics.
+      if (has_next) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block's reads have returned
+        __builtin_amdgcn_sched_barrier(0);
+        stage_now(xt[0], tn);
+      }
+      if ((j + 1 + fphase) % FLUSH == 0) flush();
       continue;
     }
     if (has_next) {
@@ -738,7 +787,7 @@ __global__ void __launch_bounds__(kWave* WC* WD, (WC * WD == 4) ? 2 : 1) k_logz(
       const int compbase = cg * 32;
       f4 acc[NPB][2];
       if constexpr (F64) {
-        logits_f64<SH, WC, WD, DPW>(xt, wop_block(a.wop64, compbase >> 4, WD, wd, DPW),
+        logits_f64<SH, WC, WD, DPW>(xt + wd * DPW, wop_block(a.wop64, compbase >> 4, WD, wd, DPW),
                                     wop_block(a.wop64, (compbase >> 4) + 1, WD, wd, DPW),
                                     wd == 0 ? a.cvec64[compbase + r16] : 0.0,
                                     wd == 0 ? a.cvec64[compbase + 16 + r16] : 0.0, acc, red64, lane, wc, wd);
@@ -1422,7 +1471,7 @@ static size_t lds_stats_bytes(int WC, int WD, int DPW) {
   const int BN = bn_for(WD, DPW);
   const int RS = WD * DPW + 4;  // mirrors Shape
   const int per_cu = (WC * WD == 4) ? 2 : 1;
-  const size_t red = WD > 1 ? (size_t)WD * WC * (BN / 16) * 8 * 64 * 4 : 4;
+  const size_t red = WD > 1 ? (size_t)(WD + BN / 16) * WC * 8 * 64 * 4 : 4;
   const int NBUF = ((size_t)BN * RS * 8 + red <= (size_t)(per_cu == 1 ? 140 : 68) * 1024) ? 2 : 1;
   const int QP = (64 * WC * WD) / BN;
   size_t b = (size_t)NBUF * BN * RS * 4 + red;
