@@ -24,6 +24,10 @@ CASES = {
     "k16384": ("ivf", 20_011, 128, 16_384, None),
     "d200_k100": ("mid", 2_005, 200, 100, None),
     "embed_d768": ("embed", 2_003, 768, 512, None),
+    # the other dim-segment widths of the eight-wave kernels: 64 dims per wave
+    # (32-row tiles, LDS DMA) and 128 (16-row tiles, register staging)
+    "d512_k40": ("mid", 1_201, 512, 40, None),
+    "d1000_k48": ("embed", 1_001, 1000, 48, None),
 }
 
 
