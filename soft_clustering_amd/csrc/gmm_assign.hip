@@ -445,7 +445,7 @@ __device__ __forceinline__ void refine_entries_ct(const unsigned short* __restri
                                                   int count, const float* __restrict__ xt, const EArgs& a, double C,
                                                   int compbase, int lane) {
   constexpr int DPT = DPW / 16;            // dims per lane (16 lanes per logit)
-  constexpr int DCH = DPT < 4 ? DPT : 4;   // dims with loads in flight together
+  constexpr int DCH = DPT;  // every load of a pass in flight together (one L2 round trip per pass)
   const int g = lane >> 4, r16 = lane & 15;
   for (int base = 0; base < count; base += 4) {
     const int e = base + g;
