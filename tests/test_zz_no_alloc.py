@@ -53,6 +53,7 @@ def zeros(K, D):
     ("mid", 60_013, 128, 1024, True),      # every statistics slot fits: bit-identical
     ("ivf", 30_011, 128, 16_384, False),   # fewer slots than the context: same sums, other order
     ("tiny", 5_003, 8, 16, True),
+    ("embed", 9_001, 768, 512, False),     # eight dim-segment waves, 32-row tiles
 ])
 def test_noalloc_matches_estep_stats(law, N, D, K, exact):
     lib = _lib()
