@@ -28,6 +28,9 @@ CASES = {
     # (32-row tiles, LDS DMA) and 128 (16-row tiles, register staging)
     "d512_k40": ("mid", 1_201, 512, 40, None),
     "d1000_k48": ("embed", 1_001, 1000, 48, None),
+    # 160 workgroups per row group: the fused kernels gather the exchange
+    # words of 128 peers, then of the remaining 32
+    "embed_k5120": ("embed", 6_007, 768, 5_120, None),
 }
 
 
