@@ -106,7 +106,27 @@ __device__ __forceinline__ void xgather(const EArgs& a, int rg, int j, int rd, f
         for (int i = 0; i < QB; ++i) {
           const int q = q0 + i * QP;
           wv[i] = (q < a.P) ? __hip_atomic_load(xb + (size_t)q * BN + pt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                            : 0ull;
+                            : ((unsigned long long)tag << 32);
+        }
+        // late words are polled again together (one round trip per poll for
+        // the whole batch), with the bounded wait of settle
+        for (int spins = 0;; ++spins) {
+          unsigned miss = 0;
+#pragma unroll
+          for (int i = 0; i < QB; ++i) miss |= ((unsigned)(wv[i] >> 32) != tag ? 1u : 0u) << i;
+          if (miss == 0) break;
+          if ((spins & 255) == 0 && __hip_atomic_load(&a.flags[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+            break;
+          if (spins > (1 << 20)) {
+            __hip_atomic_store(&a.flags[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+          for (int i = 0; i < QB; ++i)
+            if ((miss >> i) & 1u)
+              wv[i] = __hip_atomic_load(xb + (size_t)(q0 + i * QP) * BN + pt, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
         }
 #pragma unroll
         for (int i = 0; i < QB; ++i) {
